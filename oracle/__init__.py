@@ -1,0 +1,249 @@
+"""CPU oracle for MoE dispatch / combine -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product (``combine_moe_layout_amd``)
+never imports, loads or calls it, and it shares no code with the HIP library.
+
+This module is a thin numpy <-> ctypes wrapper around ``ep_oracle.c``: plain,
+single-threaded scalar loops written from the definitions on the pages (cited
+in that file's header, with the readings R1..R12 it takes where the pages are
+silent).  Every function here only marshals arrays; all arithmetic is in C.
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ep_oracle.c")
+_LIB = os.path.join(_HERE, "libep_oracle.so")
+
+# Plain IEEE arithmetic: no fast-math, no contraction of a*b+c into one fma.
+GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11"]
+
+
+def build(force: bool = False) -> str:
+    """Compile ep_oracle.c with gcc into libep_oracle.so (next to the source)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load(path: str) -> ctypes.CDLL:
+    L = ctypes.CDLL(path)
+    i64, i32, u32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p
+    L.ep_oracle_bf16_to_double.restype = ctypes.c_double
+    L.ep_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    L.ep_oracle_bf16_from_double.restype = ctypes.c_uint16
+    L.ep_oracle_bf16_from_double.argtypes = [ctypes.c_double]
+    L.ep_oracle_e4m3_decode.restype = ctypes.c_double
+    L.ep_oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    L.ep_oracle_e4m3_encode.restype = ctypes.c_uint8
+    L.ep_oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    L.ep_oracle_e4m3_encode_array.argtypes = [vp, i64, vp]
+    L.ep_oracle_e4m3_encode_bits.argtypes = [u32, i64, vp]
+    L.ep_oracle_num_recv_rows.restype = i64
+    L.ep_oracle_num_recv_rows.argtypes = [i64, i32, i32, i32]
+    L.ep_oracle_layout.restype = ctypes.c_int
+    L.ep_oracle_layout.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    L.ep_oracle_dispatch_bf16.argtypes = [vp, i64, i32, i32, vp, vp]
+    L.ep_oracle_quantize_token_fp8.argtypes = [vp, i32, vp, vp]
+    L.ep_oracle_dispatch_fp8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    L.ep_oracle_dequant_fp8.argtypes = [vp, vp, i64, i32, vp]
+    L.ep_oracle_combine.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+    L.ep_oracle_combine_tokens.argtypes = [vp, vp, vp, i32, i32, vp, i64, vp]
+    return L
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        build()
+        _lib = _load(_LIB)
+    return _lib
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Temporarily route every wrapper through another build of the oracle
+    (used by the test that checks the pins catch planted mistakes)."""
+    global _lib
+    saved = lib()
+    _lib = _load(path)
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def _p(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ----------------------------------------------------------------------------- scalars
+def bf16_to_float(bits) -> float:
+    return lib().ep_oracle_bf16_to_double(int(bits) & 0xFFFF)
+
+
+def bf16_from_double(v: float) -> int:
+    return int(lib().ep_oracle_bf16_from_double(float(v)))
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().ep_oracle_e4m3_decode(int(code) & 0xFF)
+
+
+def e4m3_encode(v: float) -> int:
+    return int(lib().ep_oracle_e4m3_encode(float(v)))
+
+
+def e4m3_encode_array(v: np.ndarray) -> np.ndarray:
+    v = _c(v, np.float32).reshape(-1)
+    out = np.empty(v.size, np.uint8)
+    lib().ep_oracle_e4m3_encode_array(_p(v), v.size, _p(out))
+    return out
+
+
+def e4m3_encode_bits(first: int, n: int, out: np.ndarray | None = None) -> np.ndarray:
+    if out is None:
+        out = np.empty(n, np.uint8)
+    lib().ep_oracle_e4m3_encode_bits(ctypes.c_uint32(first), n, _p(out))
+    return out
+
+
+# ----------------------------------------------------------------------------- layout
+def num_recv_rows(T: int, k: int, E: int, cap: int) -> int:
+    return int(lib().ep_oracle_num_recv_rows(T, k, E, cap))
+
+
+def layout(topk_idx: np.ndarray, E: int, G: int = 1, cap: int = 0, want_recv_src: bool = True):
+    """Returns a dict: num_tokens_per_expert [E], expert_offsets [E+1],
+    num_tokens_per_group [G], slot_idx [T,k], recv_src [R] (or None), error_flags."""
+    topk_idx = _c(topk_idx, np.int64)
+    T, k = topk_idx.shape
+    R = num_recv_rows(T, k, E, cap)
+    cnt = np.zeros(E, np.int32)
+    off = np.zeros(E + 1, np.int32)
+    grp = np.zeros(G, np.int32)
+    slot = np.empty((T, k), np.int32)
+    src = np.full(R, -1, np.int32) if want_recv_src else None
+    flags = np.zeros(1, np.int32)
+    rc = lib().ep_oracle_layout(_p(topk_idx) if T else None, T, k, E, G, cap, _p(cnt), _p(off),
+                                _p(grp), _p(slot) if T else None,
+                                _p(src) if src is not None and R > 0 else None, _p(flags))
+    if rc != 0:
+        raise ValueError("oracle layout rejected its arguments (status %d)" % rc)
+    return dict(num_tokens_per_expert=cnt, expert_offsets=off, num_tokens_per_group=grp,
+                slot_idx=slot, recv_src=src, error_flags=int(flags[0]), num_recv_rows=R)
+
+
+# ----------------------------------------------------------------------------- dispatch
+def dispatch_bf16(x_bits: np.ndarray, slot_idx: np.ndarray, R: int) -> np.ndarray:
+    """x_bits: uint16 [T,H] bf16 bit patterns.  Rows no slot addresses stay 0."""
+    x_bits = _c(x_bits, np.uint16)
+    slot_idx = _c(slot_idx, np.int32)
+    T, H = x_bits.shape
+    k = slot_idx.shape[1]
+    recv = np.zeros((R, H), np.uint16)
+    lib().ep_oracle_dispatch_bf16(_p(x_bits), T, k, H, _p(slot_idx), _p(recv))
+    return recv
+
+
+def quantize_token_fp8(x_row_bits: np.ndarray):
+    x_row_bits = _c(x_row_bits, np.uint16).reshape(-1)
+    H = x_row_bits.size
+    q = np.empty(H, np.uint8)
+    s = np.empty(H // 128, np.float32)
+    lib().ep_oracle_quantize_token_fp8(_p(x_row_bits), H, _p(q), _p(s))
+    return q, s
+
+
+def dispatch_fp8(x_bits: np.ndarray, slot_idx: np.ndarray, R: int):
+    """Returns (recv_q uint8 [R,H], recv_scales float32 [R,H/128]); rows no slot
+    addresses stay 0."""
+    x_bits = _c(x_bits, np.uint16)
+    slot_idx = _c(slot_idx, np.int32)
+    T, H = x_bits.shape
+    k = slot_idx.shape[1]
+    q = np.zeros((R, H), np.uint8)
+    s = np.zeros((R, H // 128), np.float32)
+    lib().ep_oracle_dispatch_fp8(_p(x_bits), T, k, H, _p(slot_idx), _p(q), _p(s))
+    return q, s
+
+
+def dequant_fp8(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    q = _c(q, np.uint8)
+    scales = _c(scales, np.float32)
+    R, H = q.shape
+    y = np.empty((R, H), np.uint16)
+    lib().ep_oracle_dequant_fp8(_p(q), _p(scales), R, H, _p(y))
+    return y
+
+
+# ----------------------------------------------------------------------------- combine
+def combine(y_bits: np.ndarray, w: np.ndarray, slot_idx: np.ndarray) -> np.ndarray:
+    y_bits = _c(y_bits, np.uint16)
+    w = _c(w, np.float32)
+    slot_idx = _c(slot_idx, np.int32)
+    T, k = slot_idx.shape
+    H = y_bits.shape[1]
+    out = np.empty((T, H), np.uint16)
+    lib().ep_oracle_combine(_p(y_bits), _p(w), _p(slot_idx), T, k, H, _p(out))
+    return out
+
+
+def combine_tokens(y_bits: np.ndarray, w: np.ndarray, slot_idx: np.ndarray, tokens) -> np.ndarray:
+    y_bits = _c(y_bits, np.uint16)
+    w = _c(w, np.float32)
+    slot_idx = _c(slot_idx, np.int32)
+    tokens = _c(tokens, np.int64).reshape(-1)
+    k = slot_idx.shape[1]
+    H = y_bits.shape[1]
+    out = np.empty((tokens.size, H), np.uint16)
+    lib().ep_oracle_combine_tokens(_p(y_bits), _p(w), _p(slot_idx), k, H, _p(tokens),
+                                   tokens.size, _p(out))
+    return out
+
+
+def chain_fp8_tokens(x_bits: np.ndarray, w: np.ndarray, slot_idx: np.ndarray, tokens) -> np.ndarray:
+    """Full path for single tokens with identity experts and FP8 dispatch:
+    every valid receive row of token t holds t's codes and scales, so the
+    expert output at each of t's slots is dequant(quantize(x_t)); combine sums
+    those with t's weights.  Built only from the oracle's own functions."""
+    tokens = np.asarray(tokens, np.int64).reshape(-1)
+    H = x_bits.shape[1]
+    k = slot_idx.shape[1]
+    out = np.empty((tokens.size, H), np.uint16)
+    for i, t in enumerate(tokens):
+        q, s = quantize_token_fp8(x_bits[t])
+        yrow = dequant_fp8(q.reshape(1, H), s.reshape(1, -1))
+        local_slot = np.where(np.asarray(slot_idx[t]) >= 0, 0, -1).astype(np.int32).reshape(1, k)
+        out[i] = combine(yrow, np.asarray(w[t], np.float32).reshape(1, k), local_slot)[0]
+    return out
+
+
+def chain_bf16_tokens(x_bits: np.ndarray, w: np.ndarray, slot_idx: np.ndarray, tokens) -> np.ndarray:
+    """Full path for single tokens with identity experts and bf16 dispatch."""
+    tokens = np.asarray(tokens, np.int64).reshape(-1)
+    H = x_bits.shape[1]
+    k = slot_idx.shape[1]
+    out = np.empty((tokens.size, H), np.uint16)
+    for i, t in enumerate(tokens):
+        yrow = np.ascontiguousarray(x_bits[t], np.uint16).reshape(1, H)
+        local_slot = np.where(np.asarray(slot_idx[t]) >= 0, 0, -1).astype(np.int32).reshape(1, k)
+        out[i] = combine(yrow, np.asarray(w[t], np.float32).reshape(1, k), local_slot)[0]
+    return out

@@ -1,0 +1,349 @@
+/*
+ * ep_oracle.c -- plain, slow, scalar CPU oracle for MoE token dispatch / combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file.  Its only users are the tests under tests/, the smoke check in
+ * __graft_entry__.py and the cpu_baseline leg of bench.py.  It shares no code,
+ * header, table or constant generator with the HIP library.
+ *
+ * What it computes, and where that is defined
+ * -------------------------------------------
+ * The method: tokens pick top-k experts; dispatch sends each token's hidden
+ * state to its experts, arranged by expert; combine brings the expert outputs
+ * back to the original token order and reduces them with the routing weights.
+ * Sources (web pages, cited by title and section):
+ *   [yololab] "DeepEP是什麼？MoE Dispatch、Combine、All-to-all與V2架構",
+ *             section "MoE為什麼需要All-to-all？" (stage table: dispatch takes
+ *             tokens, top-k index and weights and yields hidden states arranged
+ *             by expert; combine takes expert outputs and routing weights and
+ *             yields results in the original token order), section
+ *             "FP8與低精度通訊" (low-precision dispatch with scales; check the
+ *             scale granularity and format), section "ElasticBuffer" (capacity
+ *             headroom; overflow needs a drop policy), section "Load Imbalance"
+ *             (per-expert token counts, per-rank send/receive volume).
+ *   [backyes] "DeepEP 编址服务深度对抗分析", section 五.2 "MoE EP AllToAll 的
+ *             特殊性" (dispatch and combine each move batch x top_k x hidden x
+ *             sizeof(dtype): one receive row per (token, k) pair, no dedup).
+ *   [donniechu] DeepEP v2 release notes, section "Số liệu kỹ thuật" (benchmark
+ *             configuration: 8K tokens, hidden 7168, FP8 dispatch, BF16 combine).
+ * Where the pages leave a step open, this file takes one plain reading; every
+ * reading is named at the function that applies it (R1..R12 below).
+ *
+ * Readings
+ *   R1  Order inside an expert's segment: stable in the flattened pair index
+ *       p = t*k + j (a counting sort).  The pages fix no order.
+ *   R2  topk_idx == -1 marks an unrouted pair: no slot, contributes nothing, no
+ *       error.  Any other id outside [0, E) is treated the same way and sets
+ *       error bit 0.
+ *   R3  Experts map to G logical groups in contiguous blocks of E/G.
+ *   R4  No per-group dedup: one receive row per valid (token, k) pair.
+ *   R5  Padded mode (capacity > 0): expert e owns rows [e*cap, (e+1)*cap); a
+ *       pair whose rank inside its expert is >= cap is dropped (slot -1) and
+ *       sets error bit 1.  Counts stay unclamped (they report the demand).
+ *   R6  FP8 is OCP E4M3 ("e4m3fn"): bias 7, largest finite 448, subnormals
+ *       down to 2^-9, no infinities, 0x7F/0xFF are NaN.
+ *   R7  One fp32 scale per (receive row, block of 128 channels):
+ *       a = max(amax, 1e-4f); scale = a / 448 and inv = 448 / a, both single
+ *       correctly rounded fp32 divisions.
+ *   R8  Quantised code: v = x * inv (one fp32 multiply), clamped to
+ *       [-448, 448], rounded to the nearest E4M3 value, ties to even; the
+ *       sign is kept, so a negative value that rounds to zero encodes 0x80.
+ *   R9  Scales are laid out row-major [R, H/128], one scale row per receive row.
+ *   R10 Combine: out[t] = bf16(sum_j w[t,j] * y[slot[t,j]]), skipping dropped
+ *       or unrouted pairs; no renormalisation.  The oracle sums in fp64 (each
+ *       product of an fp32 weight and a bf16 value is exact there), then
+ *       rounds once to bf16, nearest-even.  A token with no valid pair gives +0.
+ *   R11 Identity expert stand-in (harness only, not part of the method): with
+ *       FP8 dispatch the expert output is the dequantised receive row,
+ *       bf16(decode(q) * scale), rounded once from the exact product.
+ *   R12 Integer types: topk_idx int64; counts, offsets and slots int32.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define EXPORT __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------------- */
+/* Status codes (the oracle's own; they mirror the meaning, not the source,   */
+/* of the library's codes).                                                    */
+/* ------------------------------------------------------------------------- */
+#define ORACLE_OK 0
+#define ORACLE_ERR_NULL (-1)
+#define ORACLE_ERR_SHAPE (-2)
+
+/* ------------------------------------------------------------------------- */
+/* bf16 <-> real numbers                                                       */
+/* ------------------------------------------------------------------------- */
+
+/* A bf16 value is the upper half of an fp32 bit pattern. */
+EXPORT double ep_oracle_bf16_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* The bf16 value nearest to v, ties to the even significand (IEEE 754
+ * round-to-nearest-even applied to an 8-bit significand with the fp32
+ * exponent range).  Written from the definition: find the quantum of v's
+ * binade, round v/quantum to an integer with ties to even, scale back. */
+EXPORT uint16_t ep_oracle_bf16_from_double(double v) {
+    if (isnan(v)) return (uint16_t)(signbit(v) ? 0xFFC0u : 0x7FC0u);
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+    if (a == 0.0) return sign;
+    const double min_normal = ldexp(1.0, -126);
+    double quantum;
+    if (a < min_normal) {
+        quantum = ldexp(1.0, -133);          /* subnormal spacing: 2^-126 / 2^7 */
+    } else {
+        int ex;
+        frexp(a, &ex);                       /* a in [2^(ex-1), 2^ex) */
+        quantum = ldexp(1.0, ex - 1 - 7);    /* 7 stored mantissa bits */
+    }
+    double n = a / quantum;                  /* exact: power-of-two scaling */
+    double r = nearbyint(n);                 /* default mode: ties to even */
+    double val = r * quantum;
+    const double max_finite = ldexp(255.0, 127 - 7); /* (2 - 2^-7) * 2^127 */
+    if (val > max_finite) return (uint16_t)(sign | 0x7F80u);
+    float f = (float)val;                    /* exact: val is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (uint16_t)((u >> 16) & 0x7FFFu));
+}
+
+static float bf16_to_float(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* ------------------------------------------------------------------------- */
+/* OCP FP8 E4M3 (reading R6)                                                   */
+/* ------------------------------------------------------------------------- */
+
+/* Value of an E4M3 code from the format's definition. */
+EXPORT double ep_oracle_e4m3_decode(uint8_t code) {
+    int s = (code >> 7) & 1;
+    int e = (code >> 3) & 0xF;
+    int m = code & 7;
+    if (e == 0xF && m == 7) return NAN;               /* the only NaN codes */
+    double mag = (e == 0) ? ldexp((double)m, -9)       /* m/8 * 2^(1-7) */
+                          : ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* Magnitudes of the 127 non-negative finite codes 0x00..0x7E, ascending. */
+static double g_e4m3_mag[127];
+static int g_e4m3_ready = 0;
+
+static void e4m3_table_init(void) {
+    if (g_e4m3_ready) return;
+    for (int c = 0; c < 127; ++c) g_e4m3_mag[c] = ep_oracle_e4m3_decode((uint8_t)c);
+    g_e4m3_ready = 1;
+}
+
+/* Nearest E4M3 value to v, ties to the even code (the even significand);
+ * magnitudes above 448 saturate to 448 (callers clamp first, reading R8);
+ * the sign bit of v is kept; NaN encodes 0x7F. */
+EXPORT uint8_t ep_oracle_e4m3_encode(float v) {
+    e4m3_table_init();
+    if (isnan(v)) return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= g_e4m3_mag[126]) return (uint8_t)(sign | 126);
+    /* largest code lo with mag[lo] <= a (binary search over the ascending table) */
+    int lo = 0, hi = 126;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (g_e4m3_mag[mid] <= a) lo = mid; else hi = mid;
+    }
+    /* now mag[lo] <= a < mag[lo+1] */
+    double d_lo = a - g_e4m3_mag[lo];
+    double d_hi = g_e4m3_mag[lo + 1] - a;
+    int code;
+    if (d_lo < d_hi) code = lo;
+    else if (d_hi < d_lo) code = lo + 1;
+    else code = (lo % 2 == 0) ? lo : lo + 1;          /* tie: even code */
+    return (uint8_t)(sign | code);
+}
+
+EXPORT void ep_oracle_e4m3_encode_array(const float* v, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = ep_oracle_e4m3_encode(v[i]);
+}
+
+/* Encode the n fp32 values whose bit patterns are first, first+1, ... */
+EXPORT void ep_oracle_e4m3_encode_bits(uint32_t first, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u = first + (uint32_t)i;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        out[i] = ep_oracle_e4m3_encode(f);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Layout: per-expert counts, offsets, per-group counts, slot of every pair    */
+/* ([yololab] stage table and "Load Imbalance"; readings R1-R5)                */
+/* ------------------------------------------------------------------------- */
+
+/* Number of receive rows: T*k in contiguous mode, E*cap in padded mode. */
+EXPORT int64_t ep_oracle_num_recv_rows(int64_t T, int32_t k, int32_t E, int32_t cap) {
+    return cap > 0 ? (int64_t)E * cap : T * (int64_t)k;
+}
+
+EXPORT int ep_oracle_layout(const int64_t* topk_idx, int64_t T, int32_t k, int32_t E,
+                            int32_t G, int32_t cap, int32_t* num_tokens_per_expert,
+                            int32_t* expert_offsets, int32_t* num_tokens_per_group,
+                            int32_t* slot_idx, int32_t* recv_src, int32_t* error_flags) {
+    if (T < 0 || k < 1 || E < 1 || G < 1 || cap < 0 || E % G != 0) return ORACLE_ERR_SHAPE;
+    if ((T > 0 && (!topk_idx || !slot_idx)) || !num_tokens_per_expert || !expert_offsets ||
+        !num_tokens_per_group || !error_flags)
+        return ORACLE_ERR_NULL;
+    int64_t P = T * (int64_t)k;
+    int32_t flags = 0;
+
+    /* 1. count the valid pairs of every expert */
+    for (int32_t e = 0; e < E; ++e) num_tokens_per_expert[e] = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t e = topk_idx[p];
+        if (e == -1) continue;                        /* R2: unrouted */
+        if (e < 0 || e >= E) { flags |= 1; continue; } /* R2: invalid id */
+        num_tokens_per_expert[e] += 1;
+    }
+
+    /* 2. expert offsets: exclusive prefix sum (contiguous) or e*cap (padded, R5) */
+    if (cap == 0) {
+        expert_offsets[0] = 0;
+        for (int32_t e = 0; e < E; ++e)
+            expert_offsets[e + 1] = expert_offsets[e] + num_tokens_per_expert[e];
+    } else {
+        for (int32_t e = 0; e <= E; ++e) expert_offsets[e] = e * cap;
+    }
+
+    /* 3. per-group totals over contiguous expert blocks (R3) */
+    int32_t per_group = E / G;
+    for (int32_t g = 0; g < G; ++g) {
+        int32_t s = 0;
+        for (int32_t e = g * per_group; e < (g + 1) * per_group; ++e) s += num_tokens_per_expert[e];
+        num_tokens_per_group[g] = s;
+    }
+
+    /* 4. slots: walk the pairs in p order with one running cursor per expert (R1) */
+    int32_t* cursor = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    if (!cursor) return ORACLE_ERR_NULL;
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t e = topk_idx[p];
+        if (e < 0 || e >= E) { slot_idx[p] = -1; continue; }
+        int32_t r = cursor[e]++;
+        if (cap > 0 && r >= cap) { slot_idx[p] = -1; flags |= 2; continue; } /* R5: drop */
+        slot_idx[p] = expert_offsets[e] + r;
+        if (recv_src) recv_src[slot_idx[p]] = (int32_t)p;
+    }
+    free(cursor);
+    *error_flags = flags;
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Dispatch ([yololab] stage table; [backyes] 五.2: one row per pair, R4)      */
+/* ------------------------------------------------------------------------- */
+
+/* bf16 dispatch: receive row slot[p] is a bit copy of token p/k's row. */
+EXPORT void ep_oracle_dispatch_bf16(const uint16_t* x, int64_t T, int32_t k, int32_t H,
+                                    const int32_t* slot_idx, uint16_t* recv_x) {
+    for (int64_t p = 0; p < T * (int64_t)k; ++p) {
+        int32_t s = slot_idx[p];
+        if (s < 0) continue;
+        int64_t t = p / k;
+        for (int32_t c = 0; c < H; ++c) recv_x[(int64_t)s * H + c] = x[t * H + c];
+    }
+}
+
+/* FP8 quantisation of one token row ([yololab] "FP8與低精度通訊"; R6-R8):
+ * per block of 128 channels, scale from the block's largest magnitude, then
+ * every channel to the nearest E4M3 code of x * inv. */
+EXPORT void ep_oracle_quantize_token_fp8(const uint16_t* x_row, int32_t H, uint8_t* q_row,
+                                         float* scales_row) {
+    const int32_t B = 128;
+    for (int32_t b = 0; b < H / B; ++b) {
+        float amax = 0.0f;
+        for (int32_t c = b * B; c < (b + 1) * B; ++c) {
+            float m = fabsf(bf16_to_float(x_row[c]));
+            if (m > amax) amax = m;
+        }
+        float a = amax > 1e-4f ? amax : 1e-4f;
+        float scale = a / 448.0f;
+        float inv = 448.0f / a;
+        scales_row[b] = scale;
+        for (int32_t c = b * B; c < (b + 1) * B; ++c) {
+            float v = bf16_to_float(x_row[c]) * inv;
+            if (v > 448.0f) v = 448.0f;
+            if (v < -448.0f) v = -448.0f;
+            q_row[c] = ep_oracle_e4m3_encode(v);
+        }
+    }
+}
+
+/* FP8 dispatch: every valid slot of token t receives t's codes and scales. */
+EXPORT void ep_oracle_dispatch_fp8(const uint16_t* x, int64_t T, int32_t k, int32_t H,
+                                   const int32_t* slot_idx, uint8_t* recv_q, float* recv_scales) {
+    int32_t nb = H / 128;
+    uint8_t* q = (uint8_t*)malloc((size_t)H);
+    float* sc = (float*)malloc((size_t)nb * sizeof(float));
+    if (!q || !sc) { free(q); free(sc); return; }
+    for (int64_t t = 0; t < T; ++t) {
+        ep_oracle_quantize_token_fp8(x + t * H, H, q, sc);
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t s = slot_idx[t * k + j];
+            if (s < 0) continue;
+            memcpy(recv_q + (int64_t)s * H, q, (size_t)H);
+            memcpy(recv_scales + (int64_t)s * nb, sc, (size_t)nb * sizeof(float));
+        }
+    }
+    free(q);
+    free(sc);
+}
+
+/* Identity expert stand-in for FP8 dispatch (harness only, R11). */
+EXPORT void ep_oracle_dequant_fp8(const uint8_t* q, const float* scales, int64_t R, int32_t H,
+                                  uint16_t* y) {
+    int32_t nb = H / 128;
+    for (int64_t r = 0; r < R; ++r)
+        for (int32_t c = 0; c < H; ++c)
+            y[r * H + c] = ep_oracle_bf16_from_double(ep_oracle_e4m3_decode(q[r * H + c]) *
+                                                      (double)scales[r * nb + c / 128]);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Combine ([yololab] stage table, combine row; R10)                           */
+/* ------------------------------------------------------------------------- */
+
+static void combine_one(const uint16_t* y, const float* w, const int32_t* slot_idx, int64_t t,
+                        int32_t k, int32_t H, uint16_t* out_row) {
+    for (int32_t c = 0; c < H; ++c) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t s = slot_idx[t * k + j];
+            if (s < 0) continue;
+            acc += (double)w[t * k + j] * ep_oracle_bf16_to_double(y[(int64_t)s * H + c]);
+        }
+        out_row[c] = ep_oracle_bf16_from_double(acc);
+    }
+}
+
+EXPORT void ep_oracle_combine(const uint16_t* y, const float* w, const int32_t* slot_idx,
+                              int64_t T, int32_t k, int32_t H, uint16_t* out) {
+    for (int64_t t = 0; t < T; ++t) combine_one(y, w, slot_idx, t, k, H, out + t * H);
+}
+
+/* Combine for a list of tokens only (for sampled checks at full size). */
+EXPORT void ep_oracle_combine_tokens(const uint16_t* y, const float* w, const int32_t* slot_idx,
+                                     int32_t k, int32_t H, const int64_t* tokens, int64_t n,
+                                     uint16_t* out_rows) {
+    for (int64_t i = 0; i < n; ++i) combine_one(y, w, slot_idx, tokens[i], k, H, out_rows + i * H);
+}

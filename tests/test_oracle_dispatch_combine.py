@@ -1,0 +1,214 @@
+"""Pins for the oracle's dispatch (bf16 and FP8) and combine (CPU only).
+
+Checked against hand-worked fixtures, numpy gathers, the closed-form error
+bound of round-to-nearest E4M3 with a per-block scale, special cases that
+reduce combine to a gather or to the identity, and an independent float64
+weighted sum.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from combine_moe_layout_amd import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+bf = workloads.float32_to_bf16_bits
+unbf = workloads.bf16_bits_to_float32
+
+
+def _ev(expr):
+    return float(eval(expr, {"__builtins__": {}}, {}))
+
+
+def _decode_all(q):
+    table = np.array([oracle.e4m3_decode(c) for c in range(256)])
+    return table[q]
+
+
+# --------------------------------------------------------------------------- FP8 dispatch
+def test_fp8_block_golden():
+    with open(os.path.join(GOLDEN, "fp8_block.json")) as f:
+        blocks = json.load(f)["blocks"]
+    b0, b1 = blocks
+    x = np.zeros(256, np.float32)
+    codes = np.zeros(256, np.uint8)
+    for i, (expr, code, _) in enumerate(b0["x"]):
+        x[i] = _ev(expr)
+        codes[i] = int(code, 16)
+    x[128:] = _ev(b1["fill"])
+    codes[128:] = int(b1["code"], 16)
+    xb = bf(x)
+    assert (unbf(xb) == x).all(), "fixture values must be exact in bf16"
+    q, s = oracle.quantize_token_fp8(xb)
+    assert (q[:128] == codes[:128]).all(), [(i, hex(a), hex(b)) for i, (a, b) in
+                                           enumerate(zip(q, codes)) if a != b][:5]
+    assert s[:1].view(np.uint32)[0] == int(b0["scale_bits"], 16)
+    assert (q[128:] == codes[128:]).all()
+    # the floor block: a = float32(1e-4); scale and inv are single fp32 divisions
+    a = np.float32(1e-4)
+    assert s[1] == np.float32(a / np.float32(448.0))
+    assert np.float32(np.float32(448.0) / a) == np.float32(_ev(b1["inv"]))
+
+
+def _fp8_error_bound_holds(xb, q, s):
+    """|decode(q)*scale - x| <= 2**-4 |x| + 2**-10 scale per element: half an
+    E4M3 ulp relative in the normal range, half the smallest subnormal spacing
+    (2**-10 in code units) below it."""
+    H = xb.shape[-1]
+    x = unbf(xb).astype(np.float64).reshape(-1, H)
+    deq = _decode_all(q.reshape(-1, H)) * np.repeat(s.reshape(-1, H // 128).astype(np.float64), 128, 1)
+    scale = np.repeat(s.reshape(-1, H // 128).astype(np.float64), 128, 1)
+    err = np.abs(deq - x)
+    bound = 2.0 ** -4 * np.abs(x) + 2.0 ** -10 * scale
+    # the scale itself carries one fp32 rounding: allow its relative 2**-23 on top
+    return bool((err <= bound * (1 + 2.0 ** -20) + np.abs(x) * 2.0 ** -21).all())
+
+
+@pytest.mark.parametrize("name,T", [("dsv3", 48), ("large", 64), ("lowlat", 16)])
+def test_fp8_quantisation_properties(name, T):
+    wl = workloads.make(name, T=T)
+    H = wl.H
+    for t in range(T):
+        q, s = oracle.quantize_token_fp8(wl.x_bits[t])
+        assert _fp8_error_bound_holds(wl.x_bits[t:t + 1], q, s)
+        x = unbf(wl.x_bits[t]).reshape(H // 128, 128)
+        amax = np.abs(x).max(1)
+        a = np.maximum(amax, np.float32(1e-4)).astype(np.float32)
+        assert (s == (a / np.float32(448.0)).astype(np.float32)).all()
+        # the largest magnitude of each block maps to the top code 448 (0x7e/0xfe)
+        top = np.abs(x).argmax(1)
+        assert ((q.reshape(H // 128, 128)[np.arange(H // 128), top] & 0x7F) == 0x7E).all()
+        # signs agree wherever the code is non-zero
+        nz = (q & 0x7F) != 0
+        assert ((q[nz] >= 0x80) == (unbf(wl.x_bits[t])[nz] < 0)).all()
+
+
+def test_fp8_dispatch_copies_and_rows():
+    wl = workloads.make("dsv3", T=40, H=1024)
+    lay = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
+    q, s = oracle.dispatch_fp8(wl.x_bits, lay["slot_idx"], wl.R)
+    for t in range(wl.T):
+        q1, s1 = oracle.quantize_token_fp8(wl.x_bits[t])
+        for j in range(wl.k):
+            r = lay["slot_idx"][t, j]
+            assert (q[r] == q1).all() and (s[r] == s1).all()
+
+
+def test_fp8_zero_and_signed_zero_blocks():
+    x = np.zeros(256, np.float32)
+    x[128:] = -0.0
+    q, s = oracle.quantize_token_fp8(bf(x))
+    assert (q[:128] == 0).all() and (q[128:] == 0x80).all()
+    assert (s == np.float32(np.float32(1e-4) / np.float32(448.0))).all()
+
+
+# --------------------------------------------------------------------------- bf16 dispatch
+def test_bf16_dispatch_is_the_gather():
+    wl = workloads.make("skewed", T=64, H=512)
+    lay = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
+    recv = oracle.dispatch_bf16(wl.x_bits, lay["slot_idx"], wl.R)
+    src = lay["recv_src"]
+    assert (recv == wl.x_bits[src // wl.k]).all()
+
+
+def test_bf16_dispatch_padded_skips_dropped():
+    idx = np.array([[0, 1], [0, 1], [0, 2]], np.int64)
+    x = bf(np.arange(3 * 8, dtype=np.float32).reshape(3, 8))
+    lay = oracle.layout(idx, 3, 1, cap=2)
+    recv = oracle.dispatch_bf16(x, lay["slot_idx"], 6)
+    assert lay["slot_idx"][2, 0] == -1 and lay["error_flags"] == 2
+    assert (recv[0] == x[0]).all() and (recv[1] == x[1]).all()
+    assert (recv[2] == x[0]).all() and (recv[3] == x[1]).all() and (recv[4] == x[2]).all()
+    assert (recv[5] == 0).all()
+
+
+# --------------------------------------------------------------------------- combine
+def test_combine_golden():
+    with open(os.path.join(GOLDEN, "combine_tiny.json")) as f:
+        c = json.load(f)
+    y = bf(np.array([[_ev(v) for v in row] for row in c["y"]], np.float32))
+    w = np.array([[_ev(v) for v in row] for row in c["topk_weights"]], np.float32)
+    slot = np.array(c["slot_idx"], np.int32)
+    out = oracle.combine(y, w, slot)
+    want = np.array([[int(b, 16) for b in row] for row in c["out_bits"]], np.uint16)
+    assert (out == want).all(), (out, want)
+
+
+@pytest.mark.parametrize("name", ["tiny", "skewed", "dsv3"])
+def test_combine_identity_round_trip(name):
+    """bf16 dispatch, identity experts, weights summing to 1: combine returns x
+    bit for bit (up to the sign of zero), since the sum's error is far below
+    half a bf16 ulp."""
+    wl = workloads.make(name, T=min(96, workloads.CONFIGS[name][0]), H=512 if name != "tiny" else None)
+    lay = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
+    recv = oracle.dispatch_bf16(wl.x_bits, lay["slot_idx"], wl.R)
+    out = oracle.combine(recv, wl.topk_weights, lay["slot_idx"])
+    assert ((out == wl.x_bits) | ((out & 0x7FFF) == 0) & ((wl.x_bits & 0x7FFF) == 0)).all()
+
+
+def test_combine_one_hot_is_a_gather():
+    g = np.random.default_rng(5)
+    T, k, H, R = 50, 4, 256, 200
+    y = workloads.random_expert_outputs(R, H, seed=1)
+    slot = g.permutation(R)[: T * k].reshape(T, k).astype(np.int32)
+    w = np.zeros((T, k), np.float32)
+    pick = g.integers(0, k, T)
+    w[np.arange(T), pick] = 1.0
+    out = oracle.combine(y, w, slot)
+    want = y[slot[np.arange(T), pick]]
+    assert ((out == want) | ((out & 0x7FFF) == 0) & ((want & 0x7FFF) == 0)).all()
+
+
+def test_combine_vs_float64_sum_and_order():
+    g = np.random.default_rng(9)
+    T, k, H, R = 64, 8, 384, 700
+    y = workloads.random_expert_outputs(R, H, seed=4)
+    slot = g.integers(-1, R, size=(T, k)).astype(np.int32)  # includes skipped pairs
+    w = g.random((T, k)).astype(np.float32)
+    out = unbf(oracle.combine(y, w, slot)).astype(np.float64)
+    yv = unbf(y).astype(np.float64)
+    ref = np.zeros((T, H))
+    for j in range(k):
+        m = slot[:, j] >= 0
+        ref[m] += w[m, j:j + 1].astype(np.float64) * yv[slot[m, j]]
+    # a correctly rounded bf16 result is within half a bf16 ulp of the exact sum
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    assert (np.abs(out - ref) <= 0.5 * ulp * (1 + 1e-9)).all()
+    # permuting the k pairs of every token changes nothing
+    perm = g.permutation(k)
+    out2 = unbf(oracle.combine(y, w[:, perm], slot[:, perm])).astype(np.float64)
+    assert (out2 == out).all()
+
+
+def test_combine_all_skipped_gives_positive_zero():
+    y = workloads.random_expert_outputs(4, 128, seed=2)
+    out = oracle.combine(y, np.ones((3, 2), np.float32), np.full((3, 2), -1, np.int32))
+    assert (out == 0).all()
+
+
+def test_chain_helpers_match_full_path():
+    wl = workloads.make("dsv3", T=24, H=512)
+    lay = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
+    q, s = oracle.dispatch_fp8(wl.x_bits, lay["slot_idx"], wl.R)
+    y = oracle.dequant_fp8(q, s)
+    full = oracle.combine(y, wl.topk_weights, lay["slot_idx"])
+    toks = [0, 5, 23]
+    assert (oracle.chain_fp8_tokens(wl.x_bits, wl.topk_weights, lay["slot_idx"], toks) == full[toks]).all()
+    recv = oracle.dispatch_bf16(wl.x_bits, lay["slot_idx"], wl.R)
+    full_b = oracle.combine(recv, wl.topk_weights, lay["slot_idx"])
+    assert (oracle.chain_bf16_tokens(wl.x_bits, wl.topk_weights, lay["slot_idx"], toks) == full_b[toks]).all()
+
+
+def test_fp8_round_trip_error_bound_through_combine():
+    """FP8 dispatch, identity experts, weights summing to 1: every output is
+    within the E4M3 bound of x (plus bf16 roundings)."""
+    wl = workloads.make("dsv3", T=32, H=1024)
+    lay = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
+    q, s = oracle.dispatch_fp8(wl.x_bits, lay["slot_idx"], wl.R)
+    out = unbf(oracle.combine(oracle.dequant_fp8(q, s), wl.topk_weights, lay["slot_idx"]))
+    x = unbf(wl.x_bits).astype(np.float64)
+    smax = s.max()
+    assert (np.abs(out - x) <= (2.0 ** -4 + 2.0 ** -7) * np.abs(x) + 2.0 ** -9 * smax).all()

@@ -1,0 +1,142 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case below plants one mistake in a copy of oracle/ep_oracle.c (a dropped
+term, a wrong sign, index or bound, a wrong rounding rule), builds it with the
+oracle's own gcc flags into a temporary library, and runs the pin battery
+against it through ``oracle.use_library`` in a child process (a mistake that
+sends a slot out of range can corrupt memory; the child keeps that away from
+the test run).  Every planted mistake must make at least one pin fail, or make
+the child die.  The mutants live only in a temporary directory.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+if os.path.dirname(HERE) not in sys.path:
+    sys.path.insert(0, os.path.dirname(HERE))
+
+import oracle
+import test_oracle_dispatch_combine as pins_dc
+import test_oracle_formats as pins_fmt
+import test_oracle_layout as pins_lay
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ep_oracle.c")
+
+MUTANTS = [
+    ("E4M3 ties go up", "else code = (lo % 2 == 0) ? lo : lo + 1;", "else code = lo + 1;"),
+    ("E4M3 loses the sign of zero", "uint8_t sign = signbit(v) ? 0x80 : 0x00;",
+     "uint8_t sign = (v < 0) ? 0x80 : 0x00;"),
+    ("E4M3 subnormal spacing", "ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    ("E4M3 exponent bias", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    ("bf16 ties away from zero", "double r = nearbyint(n);", "double r = floor(n + 0.5);"),
+    ("bf16 rounds through fp32 first", "double n = a / quantum;",
+     "double n = (double)(float)a / quantum;"),
+    ("bf16 subnormal quantum", "quantum = ldexp(1.0, -133);", "quantum = ldexp(1.0, -134);"),
+    ("slot uses the next expert's offset", "slot_idx[p] = expert_offsets[e] + r;",
+     "slot_idx[p] = expert_offsets[e + 1] + r;"),
+    ("slot rank starts at 1", "int32_t r = cursor[e]++;", "int32_t r = ++cursor[e];"),
+    ("capacity bound off by one", "if (cap > 0 && r >= cap)", "if (cap > 0 && r > cap)"),
+    ("unrouted -1 counted as an error", "if (e == -1) continue;                        /* R2: unrouted */",
+     ""),
+    ("group ranges overlap", "e < (g + 1) * per_group; ++e) s +=",
+     "e <= (g + 1) * per_group && e < E; ++e) s +="),
+    ("slots filled in reverse pair order",
+     "for (int64_t p = 0; p < P; ++p) {\n        int64_t e = topk_idx[p];\n        if (e < 0 || e >= E) { slot_idx[p] = -1;",
+     "for (int64_t p = P - 1; p >= 0; --p) {\n        int64_t e = topk_idx[p];\n        if (e < 0 || e >= E) { slot_idx[p] = -1;"),
+    ("offsets as an inclusive scan", "expert_offsets[0] = 0;\n", "expert_offsets[0] = num_tokens_per_expert[0];\n"),
+    ("dispatch reads the wrong token", "int64_t t = p / k;", "int64_t t = p % k;"),
+    ("no floor under tiny blocks", "float a = amax > 1e-4f ? amax : 1e-4f;", "float a = amax;"),
+    ("scale inverted", "float scale = a / 448.0f;", "float scale = 448.0f / a;"),
+    ("amax of signed values", "float m = fabsf(bf16_to_float(x_row[c]));", "float m = bf16_to_float(x_row[c]);"),
+    ("FP8 copies take the wrong scale row", "memcpy(recv_scales + (int64_t)s * nb, sc,",
+     "memcpy(recv_scales + (int64_t)(s / 2) * nb, sc,"),
+    ("combine uses the first weight only", "acc += (double)w[t * k + j] *", "acc += (double)w[t * k] *"),
+    ("combine sums in fp32", "double acc = 0.0;", "float acc = 0.0f;"),
+    ("combine drops the last pair", "for (int32_t j = 0; j < k; ++j) {\n            int32_t s = slot_idx[t * k + j];\n            if (s < 0) continue;\n            acc",
+     "for (int32_t j = 0; j < k - 1; ++j) {\n            int32_t s = slot_idx[t * k + j];\n            if (s < 0) continue;\n            acc"),
+    ("dequant reads the wrong block scale", "(double)scales[r * nb + c / 128]", "(double)scales[r * nb + c % nb]"),
+]
+
+
+def _battery():
+    """Fast pins (the exhaustive FP8 sweep is left out; the fixtures and the
+    torch comparison on structured values cover the same rules)."""
+    checks = [
+        pins_fmt.test_e4m3_golden_values,
+        pins_fmt.test_e4m3_decode_table_is_the_format,
+        pins_fmt.test_e4m3_matches_torch_decode,
+        pins_fmt.test_bf16_golden_values,
+        pins_fmt.test_bf16_rounding_from_binary64_exact,
+        pins_lay.test_layout_golden,
+        pins_lay.test_layout_random_with_masks_and_overflow,
+        pins_lay.test_layout_empty_and_degenerate,
+        pins_dc.test_fp8_block_golden,
+        pins_dc.test_fp8_dispatch_copies_and_rows,
+        pins_dc.test_fp8_zero_and_signed_zero_blocks,
+        pins_dc.test_bf16_dispatch_is_the_gather,
+        pins_dc.test_bf16_dispatch_padded_skips_dropped,
+        pins_dc.test_combine_golden,
+        pins_dc.test_combine_one_hot_is_a_gather,
+        pins_dc.test_combine_vs_float64_sum_and_order,
+        pins_dc.test_combine_all_skipped_gives_positive_zero,
+        pins_dc.test_fp8_round_trip_error_bound_through_combine,
+    ]
+    checks += [lambda s=s: pins_lay.test_layout_brute_force_tiny(s) for s in range(12)]
+    checks += [lambda: pins_dc.test_fp8_quantisation_properties("dsv3", 8)]
+    checks += [lambda: pins_dc.test_combine_identity_round_trip("tiny")]
+    return checks
+
+
+def test_unmutated_oracle_passes_the_battery():
+    for check in _battery():
+        check()
+
+
+def _run_battery_on(lib_path: str) -> int:
+    """Number of pins that fail against the library at lib_path."""
+    failures = 0
+    with oracle.use_library(lib_path):
+        for check in _battery():
+            try:
+                check()
+            except Exception:  # an assertion, or a shape / status error
+                failures += 1
+    return failures
+
+
+def _build_and_run(tmp_dir, i, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site must be unique: %r" % old
+    mutated = os.path.join(tmp_dir, "mutant%d.c" % i)
+    with open(mutated, "w") as f:
+        f.write(src.replace(old, new))
+    lib = os.path.join(tmp_dir, "libmutant%d.so" % i)
+    subprocess.run(["gcc", *oracle.GCC_FLAGS, mutated, "-o", lib, "-lm"], check=True)
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), lib], capture_output=True,
+                       text=True, timeout=300)
+    return r.returncode, r.stdout[-400:] + r.stderr[-400:]
+
+
+def test_planted_mistakes_are_caught(tmp_path):
+    # the child itself must pass on the real oracle, or every mutant would look caught
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), oracle.build()],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout[-400:] + r.stderr[-400:]
+    with ThreadPoolExecutor(4) as ex:
+        results = list(ex.map(lambda im: _build_and_run(str(tmp_path), im[0], im[1][1], im[1][2]),
+                              enumerate(MUTANTS)))
+    survivors = [MUTANTS[i][0] for i, (rc, _) in enumerate(results) if rc == 0]
+    assert not survivors, "planted mistakes that passed every pin: %s" % survivors
+
+
+if __name__ == "__main__":
+    # child process: exit status 0 means every pin passed against this library
+    n = _run_battery_on(sys.argv[1])
+    print("failing pins:", n)
+    sys.exit(1 if n else 0)
