@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE layout -> dispatch -> combine on one MI355X.
+
+One step is one pass of the whole path over one batch of the DeepSeek-V3-style
+prefill workload: T=8192 tokens, hidden 7168, 256 experts in 8 groups, top-8,
+FP8 E4M3 dispatch with one fp32 scale per 128 channels, bf16 combine.  Inputs
+are seeded synthetic data, resident in HBM before timing starts.  The expert
+stage is an identity stand-in computed once before timing (dispatch is
+deterministic, so its output is the same every step); it is not part of the
+path and not timed.
+
+Prints one JSON line.  `value` is the step's ideal (algorithmic) HBM bytes
+divided by the step's wall time; the per-kernel times come from HIP events
+recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["ep_combine.hip", "ep_dispatch.hip", "ep_layout.hip", "ep_device.h"]
+
+
+def ideal_bytes(T: int, H: int, E: int, G: int, k: int, R_used: int, fp8: bool) -> dict:
+    """Algorithmic HBM bytes of one pass (each byte the path must move, once).
+
+    layout:   read topk_idx (8 B per pair), write slot_idx (4 B per pair),
+              write counts / offsets / group totals (4 B each).
+    dispatch: read x once (2H B per token); per used receive row write H B of
+              codes and 4*H/128 B of scales (FP8) or 2H B (bf16); read the
+              token's k slots (4 B per pair).
+    combine:  per pair read one expert-output row (2H B), its weight and slot
+              (8 B); per token write one bf16 row (2H B).
+    """
+    P = T * k
+    layout = 8 * P + 4 * P + 4 * (E + (E + 1) + G)
+    row = H + 4 * (H // 128) if fp8 else 2 * H
+    dispatch = 2 * H * T + row * R_used + 4 * P
+    combine = 2 * H * R_used + 8 * P + 2 * H * T
+    return dict(layout=layout, dispatch=dispatch, combine=combine)
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "combine_moe_layout_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, "%s_%s_traffic.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"traffic_json:\s*(\{.*\})", open(path).read())
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    return rec if rec.get("sources_digest") == digest else None
+
+
+def cpu_baseline(wl) -> dict:
+    """The oracle, as it is, single-threaded on this host, over the whole
+    workload: layout + FP8 dispatch + combine (the identity expert between
+    them is the oracle's own dequantisation, untimed, like on the GPU)."""
+    import oracle
+    import numpy as np
+    oracle.lib()
+    t0 = time.perf_counter()
+    lay = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap, want_recv_src=False)
+    q, s = oracle.dispatch_fp8(wl.x_bits, lay["slot_idx"], wl.R)
+    t1 = time.perf_counter()
+    y = oracle.dequant_fp8(q, s)
+    del q, s
+    t2 = time.perf_counter()
+    out = oracle.combine(y, wl.topk_weights, lay["slot_idx"])
+    t3 = time.perf_counter()
+    secs = (t1 - t0) + (t3 - t2)
+    used = int((lay["slot_idx"] >= 0).sum())
+    b = ideal_bytes(wl.T, wl.H, wl.E, wl.G, wl.k, used, True)
+    del y, out
+    return {"value": round(sum(b.values()) / secs / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "the whole workload (T=%d, H=%d, E=%d, top-%d, FP8 dispatch, bf16 "
+                      "combine), layout+dispatch+combine timed once, %.2f s" % (
+                          wl.T, wl.H, wl.E, wl.k, secs),
+            "seconds": round(secs, 3), "cpu": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the path runs on a single MI355X and has no "
+              "multi-GPU mode (asked for --gpus %d)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from combine_moe_layout_amd import binding as B
+    from combine_moe_layout_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    name = "dsv3"
+    wl = W.make(name, seed=args.seed)
+    T, H, E, G, k = wl.T, wl.H, wl.E, wl.G, wl.k
+    x = torch.from_numpy(wl.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    topk_idx = torch.from_numpy(wl.topk_idx).to(dev)
+    topk_w = torch.from_numpy(wl.topk_weights).to(dev)
+    lay = B.EpLayout(T, k, E, G, wl.cap, device=dev)
+    R = lay.num_recv_rows
+    recv_q = torch.empty((R, H), dtype=torch.uint8, device=dev)
+    recv_s = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    # identity expert, once, untimed
+    B.ep_get_layout(topk_idx, lay)
+    B.ep_dispatch(x, lay, B.EP_FP8_E4M3, recv_q, recv_s)
+    B.ep_dequant_fp8(recv_q, recv_s, y)
+    torch.cuda.synchronize()
+    used = int((lay.slot_idx >= 0).sum().item())
+    nbytes = ideal_bytes(T, H, E, G, k, used, True)
+    step_bytes = sum(nbytes.values())
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.ep_get_layout(topk_idx, lay, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        B.ep_dispatch(x, lay, B.EP_FP8_E4M3, recv_q, recv_s, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        B.ep_combine(y, topk_w, lay, out, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronised on both sides
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per = {"layout": [], "dispatch": [], "combine": []}
+    for ev in events:
+        per["layout"].append(ev[0].elapsed_time(ev[1]))
+        per["dispatch"].append(ev[1].elapsed_time(ev[2]))
+        per["combine"].append(ev[2].elapsed_time(ev[3]))
+    us = {kname: float(np.mean(v)) * 1e3 for kname, v in per.items()}
+    p50 = {kname: float(np.percentile(v, 50)) * 1e3 for kname, v in per.items()}
+    p95 = {kname: float(np.percentile(v, 95)) * 1e3 for kname, v in per.items()}
+
+    # plain copy of the same size as combine's traffic: the practical ceiling
+    copy_bytes = 1 << 30
+    src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        B.ep_copy(src, dst, stream)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    reps = 10
+    for _ in range(reps):
+        B.ep_copy(src, dst, stream)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * copy_bytes * reps / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dc_gbps = (nbytes["dispatch"] + nbytes["combine"]) / ((us["dispatch"] + us["combine"]) * 1e-6) / 1e9
+    combine_gbps = nbytes["combine"] / (us["combine"] * 1e-6) / 1e9
+    dispatch_gbps = nbytes["dispatch"] / (us["dispatch"] * 1e-6) / 1e9
+    digest = sources_digest()
+    traffic = committed_traffic("combine", name, digest)
+
+    result = {
+        "metric": "dispatch+combine effective HBM GB/s (% peak) at 8K tok×7168, top-8/256",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic (seeded: x ~ N(0,1) bf16, uniform-random top-8 of 256)",
+        "config": {"workload": W.DESCRIPTIONS[name], "T": T, "hidden": H, "experts": E,
+                   "groups": G, "topk": k, "dispatch_dtype": "fp8_e4m3+fp32 scale/128ch",
+                   "combine_dtype": "bf16", "step": "layout+dispatch+combine"},
+        "pct_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "ideal_bytes": nbytes,
+        "kernel_us_mean": {kk: round(v, 2) for kk, v in us.items()},
+        "kernel_us_p50": {kk: round(v, 2) for kk, v in p50.items()},
+        "kernel_us_p95": {kk: round(v, 2) for kk, v in p95.items()},
+        "dispatch_plus_combine_gbps": round(dc_gbps, 1),
+        "dispatch_plus_combine_pct_peak": round(100 * dc_gbps / HBM_PEAK_GBPS, 2),
+        "dispatch_gbps": round(dispatch_gbps, 1),
+        "copy_kernel_gbps": round(copy_gbps, 1),
+        "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(combine_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(combine_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                     "algorithmic_bytes": nbytes["combine"]},
+        "sources_digest": digest,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

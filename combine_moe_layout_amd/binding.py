@@ -1,0 +1,230 @@
+"""ctypes binding of libep.so: the same entry points as include/ep.h.
+
+Argument marshalling only: tensors become device pointers, torch's current
+stream becomes the HIP stream, and a non-zero status becomes an exception.
+Every step of the path runs in the HIP kernels; there is no fallback -- if the
+library is missing or the tensors are not on the GPU, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libep.so")
+
+EP_OK = 0
+EP_BF16 = 0
+EP_FP8_E4M3 = 1
+EP_FLAG_BAD_EXPERT = 1
+EP_FLAG_OVERFLOW = 2
+EP_MAX_EXPERTS = 1024
+EP_MAX_TOPK = 64
+EP_MAX_HIDDEN = 65536
+
+
+class EpError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__("%s failed with status %d: %s" % (fn, status, text))
+        self.status = status
+
+
+class ep_layout_t(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int64),
+        ("num_recv_rows", ctypes.c_int64),
+        ("num_topk", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("num_groups", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("num_tokens_per_expert", ctypes.c_void_p),
+        ("expert_offsets", ctypes.c_void_p),
+        ("num_tokens_per_group", ctypes.c_void_p),
+        ("slot_idx", ctypes.c_void_p),
+        ("recv_src", ctypes.c_void_p),
+        ("error_flags", ctypes.c_void_p),
+    ]
+
+
+# name -> (restype, argtypes), mirroring include/ep.h
+_i64, _i32, _u32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_size_t
+_LP = ctypes.POINTER(ep_layout_t)
+SIGNATURES = {
+    "ep_layout_init": (ctypes.c_int, [_LP, _i64, _i32, _i32, _i32, _i32]),
+    "ep_num_recv_rows": (_i64, [_i64, _i32, _i32, _i32]),
+    "ep_layout_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "ep_get_layout": (ctypes.c_int, [_vp, _LP, _vp, _sz, _vp]),
+    "ep_dispatch": (ctypes.c_int, [_vp, _LP, _i32, _i32, _vp, _vp, _vp]),
+    "ep_combine": (ctypes.c_int, [_vp, _vp, _LP, _i32, _vp, _vp]),
+    "ep_dequant_fp8": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp]),
+    "ep_cast_e4m3_bits": (ctypes.c_int, [_u32, _i64, _i32, _vp, _vp]),
+    "ep_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
+    "ep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "ep_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libep.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libep.so is not built (%s); run `python -m "
+                               "combine_moe_layout_amd.build`" % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != EP_OK:
+        raise EpError(fn, status, lib().ep_status_string(status).decode())
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor | None, name: str, dtype=None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+class EpLayout:
+    """Device arrays of one routing layout plus the ep_layout_t that points at
+    them (the handle passed from ep_get_layout to ep_dispatch / ep_combine)."""
+
+    def __init__(self, num_tokens: int, num_topk: int, num_experts: int, num_groups: int = 1,
+                 capacity: int = 0, with_recv_src: bool = False, device=None):
+        self.struct = ep_layout_t()
+        _check("ep_layout_init", lib().ep_layout_init(ctypes.byref(self.struct), num_tokens,
+                                                      num_topk, num_experts, num_groups, capacity))
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.num_tokens_per_expert = torch.empty(num_experts, **i32)
+        self.expert_offsets = torch.empty(num_experts + 1, **i32)
+        self.num_tokens_per_group = torch.empty(num_groups, **i32)
+        self.slot_idx = torch.empty((num_tokens, num_topk), **i32)
+        self.recv_src = torch.empty(self.struct.num_recv_rows, **i32) if with_recv_src else None
+        self.error_flags = torch.empty(1, **i32)
+        s = self.struct
+        s.num_tokens_per_expert = self.num_tokens_per_expert.data_ptr()
+        s.expert_offsets = self.expert_offsets.data_ptr()
+        s.num_tokens_per_group = self.num_tokens_per_group.data_ptr()
+        s.slot_idx = self.slot_idx.data_ptr() if num_tokens > 0 else None
+        s.recv_src = self.recv_src.data_ptr() if with_recv_src and self.recv_src.numel() else None
+        s.error_flags = self.error_flags.data_ptr()
+        nbytes = lib().ep_layout_workspace_bytes(num_tokens, num_topk, num_experts)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    @property
+    def num_tokens(self) -> int:
+        return self.struct.num_tokens
+
+    @property
+    def num_topk(self) -> int:
+        return self.struct.num_topk
+
+    @property
+    def num_experts(self) -> int:
+        return self.struct.num_experts
+
+    @property
+    def num_recv_rows(self) -> int:
+        return self.struct.num_recv_rows
+
+
+# ----------------------------------------------------------------------------- entry points
+def ep_num_recv_rows(num_tokens: int, num_topk: int, num_experts: int, capacity: int = 0) -> int:
+    return int(lib().ep_num_recv_rows(num_tokens, num_topk, num_experts, capacity))
+
+
+def ep_layout_workspace_bytes(num_tokens: int, num_topk: int, num_experts: int) -> int:
+    return int(lib().ep_layout_workspace_bytes(num_tokens, num_topk, num_experts))
+
+
+def ep_get_layout(topk_idx: torch.Tensor, layout: EpLayout, stream=None) -> EpLayout:
+    """topk_idx: int64 [T, k] on the GPU.  Fills layout's arrays."""
+    if tuple(topk_idx.shape) != (layout.num_tokens, layout.num_topk):
+        raise ValueError("topk_idx shape %s does not match the layout" % (tuple(topk_idx.shape),))
+    _check("ep_get_layout", lib().ep_get_layout(
+        _ptr(topk_idx, "topk_idx", torch.int64) if topk_idx.numel() else None,
+        ctypes.byref(layout.struct), layout.workspace.data_ptr(), layout.workspace.numel(),
+        _stream(stream)))
+    return layout
+
+
+def ep_dispatch(x: torch.Tensor, layout: EpLayout, recv_dtype: int, recv_x: torch.Tensor,
+                recv_scales: torch.Tensor | None = None, stream=None) -> None:
+    """x bf16 [T, H] -> recv_x (bf16 [R, H], or uint8 [R, H] FP8 codes with
+    recv_scales fp32 [R, H/128])."""
+    T, H = layout.num_tokens, x.shape[-1]
+    if tuple(x.shape) != (T, H) or recv_x.shape[0] != layout.num_recv_rows or recv_x.shape[-1] != H:
+        raise ValueError("dispatch buffers do not match the layout")
+    want = torch.uint8 if recv_dtype == EP_FP8_E4M3 else torch.bfloat16
+    _check("ep_dispatch", lib().ep_dispatch(
+        _ptr(x, "x", torch.bfloat16), ctypes.byref(layout.struct), H, recv_dtype,
+        _ptr(recv_x, "recv_x", want), _ptr(recv_scales, "recv_scales", torch.float32),
+        _stream(stream)))
+
+
+def ep_combine(expert_out: torch.Tensor, topk_weights: torch.Tensor, layout: EpLayout,
+               out: torch.Tensor, stream=None) -> None:
+    """expert_out bf16 [R, H], topk_weights fp32 [T, k] -> out bf16 [T, H]."""
+    H = expert_out.shape[-1]
+    if (expert_out.shape[0] != layout.num_recv_rows
+            or tuple(topk_weights.shape) != (layout.num_tokens, layout.num_topk)
+            or tuple(out.shape) != (layout.num_tokens, H)):
+        raise ValueError("combine buffers do not match the layout")
+    _check("ep_combine", lib().ep_combine(
+        _ptr(expert_out, "expert_out", torch.bfloat16), _ptr(topk_weights, "topk_weights", torch.float32),
+        ctypes.byref(layout.struct), H, _ptr(out, "out", torch.bfloat16), _stream(stream)))
+
+
+def ep_dequant_fp8(q: torch.Tensor, scales: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    rows, H = q.shape
+    if tuple(y.shape) != (rows, H) or tuple(scales.shape) != (rows, H // 128):
+        raise ValueError("dequant buffers disagree")
+    _check("ep_dequant_fp8", lib().ep_dequant_fp8(
+        _ptr(q, "q", torch.uint8), _ptr(scales, "scales", torch.float32), rows, H,
+        _ptr(y, "y", torch.bfloat16), _stream(stream)))
+
+
+def ep_cast_e4m3_bits(first: int, n: int, method: int, out: torch.Tensor, stream=None) -> None:
+    if out.numel() < n:
+        raise ValueError("out too small")
+    _check("ep_cast_e4m3_bits", lib().ep_cast_e4m3_bits(
+        first & 0xFFFFFFFF, n, method, _ptr(out, "out", torch.uint8), _stream(stream)))
+
+
+def ep_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check("ep_copy", lib().ep_copy(_ptr(src, "src"), _ptr(dst, "dst"), nbytes, _stream(stream)))
+
+
+def ep_version() -> str:
+    return lib().ep_version().decode()

@@ -1,0 +1,160 @@
+// ep_api.hip -- the extern "C" entry points of libep.so (declared in ep.h):
+// host-side argument checks, then one enqueue of the HIP kernels on the
+// caller's stream.  Nothing here allocates or synchronises.
+#include <stdint.h>
+
+#include "ep_internal.h"
+
+namespace {
+
+constexpr int64_t kInt32Limit = INT32_MAX;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Sizes of a layout are valid on their own.
+int check_sizes(int64_t T, int32_t k, int32_t E, int32_t G, int32_t cap) {
+  if (T < 0 || k < 1 || k > EP_MAX_TOPK || E < 1 || E > EP_MAX_EXPERTS || G < 1 || E % G != 0 ||
+      cap < 0)
+    return EP_ERR_SHAPE;
+  if (T > kInt32Limit / k) return EP_ERR_SHAPE;                      // pairs index int32 slots
+  if (cap > 0 && (int64_t)E * cap > kInt32Limit) return EP_ERR_SHAPE;  // rows fit int32
+  // the packed layout intermediate holds a rank below the chunk size
+  return EP_OK;
+}
+
+int check_layout(const ep_layout_t* L) {
+  if (L == nullptr) return EP_ERR_NULL;
+  int rc = check_sizes(L->num_tokens, L->num_topk, L->num_experts, L->num_groups, L->capacity);
+  if (rc != EP_OK) return rc;
+  const int64_t R = L->capacity > 0 ? (int64_t)L->num_experts * L->capacity
+                                    : L->num_tokens * L->num_topk;
+  if (L->num_recv_rows != R) return EP_ERR_SHAPE;
+  if (L->num_tokens > 0 && L->slot_idx == nullptr) return EP_ERR_NULL;
+  return EP_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int ep_layout_init(ep_layout_t* layout, int64_t num_tokens, int32_t num_topk,
+                   int32_t num_experts, int32_t num_groups, int32_t capacity) {
+  if (layout == nullptr) return EP_ERR_NULL;
+  const int rc = check_sizes(num_tokens, num_topk, num_experts, num_groups, capacity);
+  if (rc != EP_OK) return rc;
+  *layout = ep_layout_t{};
+  layout->num_tokens = num_tokens;
+  layout->num_topk = num_topk;
+  layout->num_experts = num_experts;
+  layout->num_groups = num_groups;
+  layout->capacity = capacity;
+  layout->num_recv_rows =
+      capacity > 0 ? (int64_t)num_experts * capacity : num_tokens * (int64_t)num_topk;
+  return EP_OK;
+}
+
+int64_t ep_num_recv_rows(int64_t num_tokens, int32_t num_topk, int32_t num_experts,
+                         int32_t capacity) {
+  if (check_sizes(num_tokens, num_topk, num_experts, 1, capacity) != EP_OK) return -1;
+  return capacity > 0 ? (int64_t)num_experts * capacity : num_tokens * (int64_t)num_topk;
+}
+
+size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_experts) {
+  if (check_sizes(num_tokens, num_topk, num_experts, 1, 0) != EP_OK) return 0;
+  return ep::layout_workspace_bytes(num_tokens * (int64_t)num_topk, num_experts);
+}
+
+int ep_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int rc = check_layout(layout);
+  if (rc != EP_OK) return rc;
+  const ep_layout_t& L = *layout;
+  if ((L.num_tokens > 0 && topk_idx == nullptr) || L.num_tokens_per_expert == nullptr ||
+      L.expert_offsets == nullptr || L.num_tokens_per_group == nullptr ||
+      L.error_flags == nullptr || workspace == nullptr)
+    return EP_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return EP_ERR_ALIGN;
+  if (workspace_bytes <
+      ep::layout_workspace_bytes(L.num_tokens * (int64_t)L.num_topk, L.num_experts))
+    return EP_ERR_WORKSPACE;
+  return launch_status(
+      ep::launch_layout(topk_idx, L, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,
+                void* recv_x, float* recv_scales, void* stream) {
+  int rc = check_layout(layout);
+  if (rc != EP_OK) return rc;
+  if (recv_dtype != EP_BF16 && recv_dtype != EP_FP8_E4M3) return EP_ERR_DTYPE;
+  const bool fp8 = recv_dtype == EP_FP8_E4M3;
+  if (hidden < 8 || hidden > EP_MAX_HIDDEN || hidden % 8 != 0 || (fp8 && hidden % 128 != 0))
+    return EP_ERR_SHAPE;
+  if (layout->num_tokens == 0) return EP_OK;
+  if (x == nullptr || recv_x == nullptr || (fp8 && recv_scales == nullptr)) return EP_ERR_NULL;
+  if (!aligned16(x) || !aligned16(recv_x) ||
+      (fp8 && (reinterpret_cast<uintptr_t>(recv_scales) & 3u) != 0))
+    return EP_ERR_ALIGN;
+  return launch_status(ep::launch_dispatch(x, *layout, hidden, fp8, recv_x, recv_scales,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine(const void* expert_out, const float* topk_weights, const ep_layout_t* layout,
+               int32_t hidden, void* out, void* stream) {
+  int rc = check_layout(layout);
+  if (rc != EP_OK) return rc;
+  if (hidden < 8 || hidden > EP_MAX_HIDDEN || hidden % 8 != 0) return EP_ERR_SHAPE;
+  if (layout->num_tokens == 0) return EP_OK;
+  if (expert_out == nullptr || topk_weights == nullptr || out == nullptr) return EP_ERR_NULL;
+  if (!aligned16(expert_out) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(topk_weights) & 3u) != 0)
+    return EP_ERR_ALIGN;
+  return launch_status(ep::launch_combine(expert_out, topk_weights, *layout, hidden, out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int ep_dequant_fp8(const uint8_t* q, const float* scales, int64_t rows, int32_t hidden, void* y,
+                   void* stream) {
+  if (rows < 0 || hidden < 128 || hidden > EP_MAX_HIDDEN || hidden % 128 != 0)
+    return EP_ERR_SHAPE;
+  if (rows == 0) return EP_OK;
+  if (q == nullptr || scales == nullptr || y == nullptr) return EP_ERR_NULL;
+  if (!aligned16(q) || !aligned16(y) || (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+    return EP_ERR_ALIGN;
+  return launch_status(
+      ep::launch_dequant_fp8(q, scales, rows, hidden, y, static_cast<hipStream_t>(stream)));
+}
+
+int ep_cast_e4m3_bits(uint32_t first, int64_t n, int32_t method, uint8_t* out, void* stream) {
+  if (n < 0 || method < 0 || method > 2) return EP_ERR_SHAPE;
+  if (n == 0) return EP_OK;
+  if (out == nullptr) return EP_ERR_NULL;
+  return launch_status(
+      ep::launch_cast_e4m3_bits(first, n, method, out, static_cast<hipStream_t>(stream)));
+}
+
+int ep_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes % 16 != 0) return EP_ERR_SHAPE;
+  if (bytes == 0) return EP_OK;
+  if (src == nullptr || dst == nullptr) return EP_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return EP_ERR_ALIGN;
+  return launch_status(ep::launch_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
+const char* ep_status_string(int status) {
+  switch (status) {
+    case EP_OK: return "ok";
+    case EP_ERR_NULL: return "a required pointer is NULL";
+    case EP_ERR_SHAPE: return "a size is out of range or sizes disagree";
+    case EP_ERR_ALIGN: return "a buffer is not aligned as required";
+    case EP_ERR_WORKSPACE: return "workspace smaller than ep_layout_workspace_bytes()";
+    case EP_ERR_LAUNCH: return "the HIP runtime reported a launch error";
+    case EP_ERR_DTYPE: return "unknown receive dtype";
+    default: return "unknown status";
+  }
+}
+
+const char* ep_version(void) { return "combine_moe_layout_amd 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// ep_device.h -- device helpers shared by the gfx950 kernels of libep.so:
+// wave64 lane masks, bf16 and OCP FP8 E4M3 conversions, 16-byte vector types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kFp8Block = 128;     // channels per FP8 scale
+constexpr float kFp8Max = 448.0f;  // largest finite E4M3 value
+constexpr float kScaleFloor = 1e-4f;
+
+struct alignas(16) u32x4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+
+// fp32 -> bf16 bit pattern, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// Rounds the exact value p + err to bf16 (nearest, ties to even), where p is an
+// fp32 value and err the exact remainder of the product that produced it
+// (|err| <= half an fp32 ulp of p).  Only a p that sits exactly on a bf16
+// midpoint needs err: then err's sign decides the direction.
+__device__ __forceinline__ uint32_t bf16_round_exact(float p, float err) {
+  uint32_t u = __float_as_uint(p);
+  if ((u & 0xFFFFu) == 0x8000u && err != 0.0f) {
+    bool away = (err > 0.0f) == (p > 0.0f);  // exact value lies beyond the midpoint
+    return away ? (u >> 16) + 1u : (u >> 16);
+  }
+  return bf16_rne(p);
+}
+
+// ---------------------------------------------------------------------------
+// OCP FP8 E4M3 (bias 7, 3 mantissa bits, subnormals, largest finite 448).
+// ---------------------------------------------------------------------------
+
+// Software encoder of v already clamped to [-448, 448]: nearest code, ties to
+// even, sign kept (a negative value that rounds to zero gives 0x80).
+__device__ __forceinline__ uint32_t e4m3_encode_sw(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t mag = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (mag >= 0x3C800000u) {  // |v| >= 2^-6: normal E4M3 range
+    uint32_t e8 = (mag >> 23) - 120u;  // unbiased exponent + 7
+    uint32_t m = mag & 0x7FFFFFu;
+    code = (e8 << 3) | (m >> 20);
+    uint32_t rem = m & 0xFFFFFu;
+    code += (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u;
+    code = code > 0x7Eu ? 0x7Eu : code;  // only |v| == 448 rounding up could exceed
+  } else {
+    // subnormal codes are multiples of 2^-9: round |v| * 2^9 to an integer, ties to even
+    code = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
+  }
+  return sign | code;
+}
+
+// Hardware conversion of two clamped values to two E4M3 bytes (low 16 bits).
+__device__ __forceinline__ uint32_t e4m3_encode2_hw(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Encode four clamped values into one 32-bit word, byte i = value i.
+template <bool kHw>
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+  if constexpr (kHw) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+  } else {
+    return e4m3_encode_sw(a) | (e4m3_encode_sw(b) << 8) | (e4m3_encode_sw(c) << 16) |
+           (e4m3_encode_sw(d) << 24);
+  }
+}
+
+__device__ __forceinline__ float clamp_fp8(float v) { return fminf(fmaxf(v, -kFp8Max), kFp8Max); }
+
+// E4M3 code -> fp32 (exact).  0x7F / 0xFF decode to NaN.
+__device__ __forceinline__ float e4m3_decode(uint32_t code) {
+  uint32_t s = (code & 0x80u) << 24;
+  uint32_t e = (code >> 3) & 0xFu;
+  uint32_t m = code & 7u;
+  float mag;
+  if (e == 0u) {
+    mag = (float)m * 0.001953125f;  // m * 2^-9
+  } else if (e == 15u && m == 7u) {
+    mag = __uint_as_float(0x7FC00000u);
+  } else {
+    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  }
+  return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+}  // namespace ep

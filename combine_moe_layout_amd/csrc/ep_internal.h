@@ -1,0 +1,47 @@
+// ep_internal.h -- launchers shared between the kernel sources and the C ABI
+// (ep_api.hip).  Arguments are validated by the caller before these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ep.h"
+
+namespace ep {
+
+// Layout: chunks of kChunkPairs (t, k) pairs; each chunk is one workgroup of
+// the counting kernel.  The packed intermediate in slot_idx keeps the expert
+// id in the low kExpertBits bits and the rank inside the chunk above them.
+constexpr int kLayoutThreads = 256;
+constexpr int kLayoutWaves = kLayoutThreads / 64;
+constexpr int kLayoutItems = 8;
+constexpr int kWavePairs = kLayoutItems * 64;
+constexpr int kChunkPairs = kWavePairs * kLayoutWaves;
+constexpr int kExpertBits = 11;
+static_assert((1 << kExpertBits) >= EP_MAX_EXPERTS, "expert id must fit the packed field");
+
+inline int64_t layout_num_chunks(int64_t pairs) { return (pairs + kChunkPairs - 1) / kChunkPairs; }
+
+size_t layout_workspace_bytes(int64_t pairs, int32_t num_experts);
+
+hipError_t launch_layout(const int64_t* topk_idx, const ep_layout_t& L, void* workspace,
+                         hipStream_t stream);
+
+hipError_t launch_dispatch(const void* x, const ep_layout_t& L, int32_t hidden, bool fp8,
+                           void* recv_x, float* recv_scales, hipStream_t stream);
+
+hipError_t launch_combine(const void* y, const float* w, const ep_layout_t& L, int32_t hidden,
+                          void* out, hipStream_t stream);
+
+hipError_t launch_dequant_fp8(const uint8_t* q, const float* scales, int64_t rows, int32_t hidden,
+                              void* y, hipStream_t stream);
+
+hipError_t launch_cast_e4m3_bits(uint32_t first, int64_t n, int32_t method, uint8_t* out,
+                                 hipStream_t stream);
+
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+// The encoder ep_dispatch uses: true = the gfx950 conversion instruction.
+extern const bool kDispatchUsesHwCast;
+
+}  // namespace ep

@@ -1,0 +1,204 @@
+/*
+ * ep.h -- C ABI of libep.so: MoE token dispatch and combine on one MI355X
+ * (gfx950), as hand-written HIP kernels.
+ *
+ * The method (sources are web pages, cited by title and section):
+ *   - "DeepEP是什麼？MoE Dispatch、Combine、All-to-all與V2架構" (yololab.net),
+ *     section "MoE為什麼需要All-to-all？", stage table: dispatch takes the
+ *     tokens, their top-k expert index and weights and produces hidden states
+ *     arranged by expert; combine takes the expert outputs and the routing
+ *     weights and produces results in the original token order, with a
+ *     reduction.  Section "Load Imbalance": per-expert token counts and per-rank
+ *     send/receive volume are the quantities to track.  Section "ElasticBuffer":
+ *     buffers are sized from max tokens, top-k, hidden and EP degree, and an
+ *     overflow needs a drop policy.  Section "FP8與低精度通訊": FP8 dispatch
+ *     carries scales whose granularity and format must be checked.
+ *   - "DeepEP 编址服务深度对抗分析" (backyes.github.io), section 五.2: each of
+ *     dispatch and combine moves batch x top_k x hidden x sizeof(dtype), i.e.
+ *     one receive row per (token, k) pair.
+ *   - DeepEP v2 release notes (donniechu.com), section "Số liệu kỹ thuật": the
+ *     DeepSeek-V3-style test case uses FP8 dispatch and BF16 combine; section
+ *     "Có gì mới trong v2": an EPHandle carries orchestration state between
+ *     calls (ep_layout_t plays that role here).
+ *
+ * One GPU holds every expert.  The G logical groups are the expert blocks a
+ * real EP rank would own (experts [g*E/G, (g+1)*E/G)), laid out as partitions
+ * of one receive buffer.
+ *
+ * Conventions for every call:
+ *   - Ownership: the caller allocates and frees all device memory (inputs,
+ *     outputs, layout arrays, workspace).  The library allocates nothing and
+ *     keeps no mutable global state; calls on different buffers may run
+ *     concurrently.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *     stream).  Calls only enqueue work and never synchronise; outputs and
+ *     error flags are valid once the stream has been synchronised.
+ *   - Layout: every array is dense row-major.  Token rows have stride
+ *     `hidden` elements; pointers to row data must be 16-byte aligned.
+ *   - Errors checked on the host return a negative status before anything is
+ *     enqueued.  Errors found on the device are reported in
+ *     layout->error_flags (EP_FLAG_*); the offending pairs are skipped and no
+ *     memory outside the caller's buffers is touched.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum ep_status {
+    EP_OK = 0,
+    EP_ERR_NULL = -1,      /* a required pointer is NULL */
+    EP_ERR_SHAPE = -2,     /* a size is out of range or sizes disagree */
+    EP_ERR_ALIGN = -3,     /* a row buffer is not 16-byte aligned */
+    EP_ERR_WORKSPACE = -4, /* workspace smaller than ep_layout_workspace_bytes() */
+    EP_ERR_LAUNCH = -5,    /* the HIP runtime reported an error when launching */
+    EP_ERR_DTYPE = -6      /* unknown receive dtype */
+};
+
+/* Receive-buffer element types for ep_dispatch. */
+enum ep_dtype {
+    EP_BF16 = 0,    /* bf16 rows, a bit copy of x */
+    EP_FP8_E4M3 = 1 /* OCP FP8 E4M3 codes + one fp32 scale per 128 channels */
+};
+
+/* Bits of layout->error_flags, written by ep_get_layout. */
+enum ep_flag {
+    EP_FLAG_BAD_EXPERT = 1, /* some topk_idx entry is outside [-1, num_experts) */
+    EP_FLAG_OVERFLOW = 2    /* padded mode: some expert received more than capacity pairs */
+};
+
+/* Limits checked by the host-side validation. */
+#define EP_MAX_EXPERTS 1024
+#define EP_MAX_TOPK 64
+#define EP_MAX_HIDDEN 65536
+
+/*
+ * The routing layout: the handle that ep_get_layout fills and ep_dispatch /
+ * ep_combine consume.  Size fields are set by ep_layout_init; the caller then
+ * points the array fields at device memory it owns:
+ *   num_tokens_per_expert [E]   pairs routed to each expert (unclamped demand)
+ *   expert_offsets        [E+1] first receive row of each expert; [E] = rows used
+ *                               (contiguous) or E*capacity (padded)
+ *   num_tokens_per_group  [G]   pairs routed to each group of E/G experts
+ *   slot_idx              [T*k] receive row of pair p = t*k + j, or -1 if the
+ *                               pair is unrouted, names a bad expert, or was
+ *                               dropped for capacity
+ *   recv_src              [R]   optional (NULL to skip): pair index p stored in
+ *                               each used receive row; unused rows untouched
+ *   error_flags           [1]   EP_FLAG_* bits of the latest ep_get_layout call
+ * Receive rows: R = T*k (contiguous, capacity == 0) or E*capacity (padded).
+ */
+typedef struct ep_layout {
+    int64_t num_tokens;    /* T */
+    int64_t num_recv_rows; /* R */
+    int32_t num_topk;      /* k */
+    int32_t num_experts;   /* E */
+    int32_t num_groups;    /* G, divides E */
+    int32_t capacity;      /* 0: contiguous; > 0: rows per expert (padded) */
+    int32_t* num_tokens_per_expert;
+    int32_t* expert_offsets;
+    int32_t* num_tokens_per_group;
+    int32_t* slot_idx;
+    int32_t* recv_src;
+    int32_t* error_flags;
+} ep_layout_t;
+
+/*
+ * Fill the size fields of *layout (and set every array pointer to NULL).
+ * Requires 0 <= num_tokens, 1 <= num_topk <= EP_MAX_TOPK,
+ * 1 <= num_experts <= EP_MAX_EXPERTS, 1 <= num_groups, num_experts %
+ * num_groups == 0, 0 <= capacity, num_tokens*num_topk and R below 2^31.
+ * Returns EP_OK, EP_ERR_NULL or EP_ERR_SHAPE.  Host only.
+ */
+int ep_layout_init(ep_layout_t* layout, int64_t num_tokens, int32_t num_topk,
+                   int32_t num_experts, int32_t num_groups, int32_t capacity);
+
+/* R for these sizes (T*k, or E*capacity when capacity > 0); -1 if invalid.  Host only. */
+int64_t ep_num_recv_rows(int64_t num_tokens, int32_t num_topk, int32_t num_experts,
+                         int32_t capacity);
+
+/* Bytes of device workspace ep_get_layout needs for these sizes.  Host only. */
+size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_experts);
+
+/*
+ * Routing layout ([yololab] stage table, dispatch row: the sort by expert;
+ * section "Load Imbalance": per-expert and per-rank counts).
+ * topk_idx: device int64 [T, k], the router's top-k expert ids; -1 = unrouted.
+ * Writes every array of *layout.  Order inside an expert's segment is stable
+ * in p = t*k + j, so the result is deterministic.  Padded mode keeps the
+ * first `capacity` pairs of each expert (in p order) and drops the rest.
+ * workspace: device memory of at least ep_layout_workspace_bytes(T, k, E)
+ * bytes, 256-byte aligned; contents need no initialisation and are scratch.
+ * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_WORKSPACE or EP_ERR_LAUNCH.
+ */
+int ep_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * Dispatch ([yololab] stage table, dispatch row; [backyes] 五.2: one row
+ * per pair).  x: device bf16 [T, hidden].  For every pair p with
+ * slot_idx[p] >= 0, receive row slot_idx[p] gets token p/k:
+ *   EP_BF16:     recv_x bf16 [R, hidden], a bit copy; recv_scales unused (may be NULL).
+ *   EP_FP8_E4M3: recv_x uint8 [R, hidden] E4M3 codes and recv_scales fp32
+ *                [R, hidden/128] ([yololab] "FP8與低精度通訊"): per block of
+ *                128 channels a = max(max|x|, 1e-4), scale = a/448,
+ *                code = nearest E4M3 (ties to even, sign kept) of
+ *                clamp(x * (448/a), -448, 448); requires hidden % 128 == 0.
+ * Rows that no slot names are left untouched.  hidden % 8 == 0.
+ * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN, EP_ERR_DTYPE or EP_ERR_LAUNCH.
+ */
+int ep_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,
+                void* recv_x, float* recv_scales, void* stream);
+
+/*
+ * Combine ([yololab] stage table, combine row: back to token order with a
+ * weighted reduction).  expert_out: device bf16 [R, hidden]; topk_weights:
+ * device fp32 [T, k].  out[t] = bf16(sum over j with slot_idx[t*k+j] >= 0 of
+ * topk_weights[t,k] * expert_out[slot]), accumulated in fp32, rounded to
+ * nearest-even; a token with no valid pair gets +0.  No renormalisation.
+ * out: device bf16 [T, hidden], must not alias the inputs.  hidden % 8 == 0.
+ * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN or EP_ERR_LAUNCH.
+ */
+int ep_combine(const void* expert_out, const float* topk_weights, const ep_layout_t* layout,
+               int32_t hidden, void* out, void* stream);
+
+/*
+ * Identity-expert stand-in for FP8 receive buffers (not part of the path;
+ * used to feed combine in checks and benchmarks): y[r, c] = the bf16 nearest
+ * (ties to even) to decode(q[r, c]) * scales[r, c/128], rounded once from the
+ * exact product.  q uint8 [rows, hidden], scales fp32 [rows, hidden/128],
+ * y bf16 [rows, hidden]; hidden % 128 == 0.
+ */
+int ep_dequant_fp8(const uint8_t* q, const float* scales, int64_t rows, int32_t hidden, void* y,
+                   void* stream);
+
+/*
+ * The FP8 encoder that ep_dispatch applies to x * inv, exposed for
+ * verification: out[i] = E4M3 code of clamp(f, -448, 448) for the n fp32
+ * values f whose bit patterns are first, first+1, ... (the sequence wraps
+ * modulo 2^32).  method 0 = the encoder ep_dispatch uses; 1 = the software
+ * encoder; 2 = the hardware conversion instruction.  out: device uint8 [n].
+ */
+int ep_cast_e4m3_bits(uint32_t first, int64_t n, int32_t method, uint8_t* out, void* stream);
+
+/* Plain device copy of `bytes` bytes (both 16-byte aligned, bytes % 16 == 0);
+ * the bandwidth reference that measurements are compared against. */
+int ep_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* ep_status_string(int status);
+
+/* Library version string (static storage). */
+const char* ep_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

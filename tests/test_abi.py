@@ -1,0 +1,150 @@
+"""The C ABI boundary on the host (CPU only, no kernel launches).
+
+libep.so loads, exports every function include/ep.h declares, the Python
+binding mirrors exactly that list, and the host-side checks reject bad
+arguments before anything is enqueued (fake device pointers below are never
+dereferenced: every call here fails validation first).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from combine_moe_layout_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep.h")
+PKG = os.path.join(ROOT, "combine_moe_layout_amd")
+
+
+def header_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.library_path()):
+        from combine_moe_layout_amd.build import build_library
+        build_library()
+    return binding.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    declared = header_functions()
+    assert len(declared) >= 10
+    nm = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()], capture_output=True,
+                        text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in nm.splitlines() if " T " in ln}
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    for f in declared:
+        getattr(L, f)
+
+
+def test_binding_mirrors_the_header():
+    assert sorted(binding.SIGNATURES) == header_functions()
+
+
+def test_library_has_no_oracle_code(L):
+    nm = subprocess.run(["nm", "-D", binding.library_path()], capture_output=True, text=True,
+                        check=True).stdout
+    assert "oracle" not in nm
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", src, re.M), f
+                assert "ep_oracle" not in src, f
+
+
+def test_missing_library_is_an_error(monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "_LIB_PATH", "/nonexistent/libep.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.lib()
+
+
+def test_layout_init_validation(L):
+    s = binding.ep_layout_t()
+    ok = L.ep_layout_init(ctypes.byref(s), 8192, 8, 256, 8, 0)
+    assert ok == 0 and s.num_recv_rows == 65536 and s.slot_idx is None
+    assert L.ep_layout_init(ctypes.byref(s), 128, 8, 256, 8, 128) == 0 and s.num_recv_rows == 32768
+    assert L.ep_layout_init(ctypes.byref(s), 0, 1, 1, 1, 0) == 0 and s.num_recv_rows == 0
+    bad = [(-1, 8, 256, 8, 0), (10, 0, 256, 8, 0), (10, 65, 256, 8, 0), (10, 8, 0, 1, 0),
+           (10, 8, 1025, 1, 0), (10, 8, 256, 7, 0), (10, 8, 256, 0, 0), (10, 8, 256, 8, -1),
+           (2 ** 31, 8, 256, 8, 0), (10, 8, 1024, 8, 2 ** 22)]
+    for args in bad:
+        assert L.ep_layout_init(ctypes.byref(s), *args) == -2, args
+    assert L.ep_layout_init(None, 1, 1, 1, 1, 0) == -1
+
+
+def test_size_queries(L):
+    assert binding.ep_num_recv_rows(8192, 8, 256, 0) == 65536
+    assert binding.ep_num_recv_rows(128, 8, 256, 128) == 32768
+    assert binding.ep_num_recv_rows(-5, 8, 256, 0) == -1
+    prev = 0
+    for pairs in (0, 1, 2047, 2048, 2049, 65536, 393216):
+        b = binding.ep_layout_workspace_bytes(pairs, 1, 256)
+        chunks = -(-pairs // 2048)
+        assert b >= 4 * (chunks * 256 + chunks) and b % 256 == 0 and b >= prev
+        prev = b
+    assert binding.ep_layout_workspace_bytes(10, 0, 256) == 0
+
+
+def _layout(T=64, k=4, E=16, G=4, cap=0):
+    s = binding.ep_layout_t()
+    assert binding.lib().ep_layout_init(ctypes.byref(s), T, k, E, G, cap) == 0
+    fake = 1 << 20  # never dereferenced: each call below fails validation first
+    s.num_tokens_per_expert = s.expert_offsets = s.num_tokens_per_group = fake
+    s.slot_idx = s.error_flags = fake
+    return s
+
+
+def test_entry_points_reject_bad_arguments(L):
+    s = _layout()
+    ws_need = L.ep_layout_workspace_bytes(64, 4, 16)
+    fake = 1 << 20
+    by = ctypes.byref
+    assert L.ep_get_layout(fake, None, fake, ws_need, None) == -1
+    assert L.ep_get_layout(None, by(s), fake, ws_need, None) == -1          # no topk_idx
+    assert L.ep_get_layout(fake, by(s), None, ws_need, None) == -1          # no workspace
+    assert L.ep_get_layout(fake, by(s), fake + 16, ws_need, None) == -3     # workspace alignment
+    assert L.ep_get_layout(fake, by(s), fake, ws_need - 1, None) == -4      # workspace too small
+    s2 = _layout()
+    s2.num_recv_rows = 7                                                    # inconsistent sizes
+    assert L.ep_get_layout(fake, by(s2), fake, ws_need, None) == -2
+    s3 = _layout()
+    s3.error_flags = None
+    assert L.ep_get_layout(fake, by(s3), fake, ws_need, None) == -1
+    # dispatch
+    assert L.ep_dispatch(fake, by(s), 256, 7, fake, fake, None) == -6       # dtype
+    assert L.ep_dispatch(fake, by(s), 200, 1, fake, fake, None) == -2       # fp8 needs H % 128
+    assert L.ep_dispatch(fake, by(s), 260, 0, fake, None, None) == -2       # H % 8
+    assert L.ep_dispatch(fake, by(s), 256, 1, fake, None, None) == -1       # fp8 needs scales
+    assert L.ep_dispatch(fake + 8, by(s), 256, 0, fake, None, None) == -3   # x alignment
+    assert L.ep_dispatch(fake, by(s), 256, 1, fake, fake + 2, None) == -3   # scales alignment
+    assert L.ep_dispatch(fake, None, 256, 0, fake, None, None) == -1
+    # combine
+    assert L.ep_combine(None, fake, by(s), 256, fake, None) == -1
+    assert L.ep_combine(fake, fake, by(s), 256, fake + 4, None) == -3
+    assert L.ep_combine(fake, fake, by(s), 0, fake, None) == -2
+    assert L.ep_combine(fake, fake, by(s), 65536 + 8, fake, None) == -2
+    # auxiliaries
+    assert L.ep_dequant_fp8(fake, fake, 4, 100, fake, None) == -2
+    assert L.ep_cast_e4m3_bits(0, 16, 3, fake, None) == -2
+    assert L.ep_copy(fake, fake, 17, None) == -2
+    assert L.ep_copy(fake + 1, fake, 16, None) == -3
+    # empty inputs are valid no-ops that enqueue nothing
+    e = _layout(T=0)
+    assert L.ep_dispatch(None, by(e), 256, 0, None, None, None) == 0
+    assert L.ep_combine(None, None, by(e), 256, None, None) == 0
+    assert L.ep_copy(None, None, 0, None) == 0
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert L.ep_status_string(code).decode() not in ("", "unknown status")
+    assert L.ep_status_string(42).decode() == "unknown status"

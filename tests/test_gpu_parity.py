@@ -1,0 +1,393 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Both sides are fed from the same seeded generators and never see each
+other's outputs.  The bar: layout, slots, bf16 dispatch, FP8 codes and scales
+and the identity-expert dequantisation are bit-exact; combine is within
+|gpu - ref| <= 8e-3 * max(|ref|, 1e-3) element-wise (the oracle sums in fp64,
+the kernel in fp32; both round once to bf16).  At the workloads' full sizes
+(the launch shapes the benchmark times) outputs are checked on sampled tokens
+the oracle computes one by one.
+"""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_moe_layout_amd import binding as B
+from combine_moe_layout_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 8e-3
+ABS_FLOOR = 1e-3
+
+
+def note(msg):
+    print("[gpu-parity] " + msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the GPU tests need an MI355X"
+    B.lib()
+    note("library: %s" % B.ep_version())
+
+
+# --------------------------------------------------------------------------- helpers
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def gpu_layout(idx: np.ndarray, E: int, G: int, cap: int, with_src: bool = True) -> B.EpLayout:
+    T, k = idx.shape
+    lay = B.EpLayout(T, k, E, G, cap, with_recv_src=with_src)
+    if with_src and lay.recv_src is not None:
+        lay.recv_src.fill_(-1)
+    B.ep_get_layout(torch.from_numpy(np.ascontiguousarray(idx, np.int64)).cuda(), lay)
+    return lay
+
+
+def layout_to_host(lay: B.EpLayout) -> dict:
+    torch.cuda.synchronize()
+    return dict(num_tokens_per_expert=lay.num_tokens_per_expert.cpu().numpy(),
+                expert_offsets=lay.expert_offsets.cpu().numpy(),
+                num_tokens_per_group=lay.num_tokens_per_group.cpu().numpy(),
+                slot_idx=lay.slot_idx.cpu().numpy(),
+                recv_src=None if lay.recv_src is None else lay.recv_src.cpu().numpy(),
+                error_flags=int(lay.error_flags.cpu()[0]))
+
+
+def assert_layout_equal(g: dict, o: dict, what: str):
+    for key in ("num_tokens_per_expert", "expert_offsets", "num_tokens_per_group", "slot_idx"):
+        a, b = g[key], o[key]
+        assert a.shape == b.shape and (a == b).all(), "%s: %s differs (first at %s)" % (
+            what, key, np.argwhere(a != b)[:3].tolist())
+    if g["recv_src"] is not None:
+        assert (g["recv_src"] == o["recv_src"]).all(), "%s: recv_src differs" % what
+    assert g["error_flags"] == o["error_flags"], "%s: flags %d vs %d" % (
+        what, g["error_flags"], o["error_flags"])
+
+
+def assert_close_bf16(gpu_bits: np.ndarray, ref_bits: np.ndarray, what: str) -> float:
+    g = W.bf16_bits_to_float32(gpu_bits).astype(np.float64)
+    r = W.bf16_bits_to_float32(ref_bits).astype(np.float64)
+    assert np.isfinite(g).all(), "%s: non-finite output" % what
+    err = np.abs(g - r)
+    lim = REL_TOL * np.maximum(np.abs(r), ABS_FLOOR)
+    bad = np.argwhere(err > lim)
+    assert bad.size == 0, "%s: %d elements beyond tolerance, first %s (gpu %r ref %r)" % (
+        what, len(bad), bad[0].tolist(), g[tuple(bad[0])], r[tuple(bad[0])])
+    rel = float((err / np.maximum(np.abs(r), ABS_FLOOR)).max()) if err.size else 0.0
+    note("%s: max rel err %.3e (tol %.0e)" % (what, rel, REL_TOL))
+    return rel
+
+
+def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
+    g = np.random.default_rng(1234 + seed)
+    picks = set(g.choice(T, size=min(n, T), replace=False).tolist())
+    picks.update([0, T - 1])
+    return np.array(sorted(picks), np.int64)
+
+
+# --------------------------------------------------------------------------- FP8 encoder
+def test_fp8_encoder_exhaustive():
+    """Every fp32 bit pattern of magnitude <= 448, both signs: the kernel's
+    encoders (dispatch's, the software one, the conversion instruction) give
+    the oracle's code."""
+    top = 0x43E00000
+    chunk = 1 << 26
+    out = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+    oracle.lib()
+    pool = ThreadPoolExecutor(16)
+    bad = {0: 0, 1: 0, 2: 0}
+    for sign in (0, 1):
+        base = 0x80000000 if sign else 0
+        note("fp8 encoder sweep, sign %d" % sign)
+        for start in range(0, top + 1, chunk):
+            n = min(chunk, top + 1 - start)
+            parts = [(base + start + i, min(1 << 22, n - i)) for i in range(0, n, 1 << 22)]
+            ref = np.concatenate(list(pool.map(lambda a: oracle.e4m3_encode_bits(*a), parts)))
+            for method in (0, 1, 2):
+                B.ep_cast_e4m3_bits(base + start, n, method, out)
+                got = out[:n].cpu().numpy()
+                bad[method] += int((got != ref).sum())
+    pool.shutdown()
+    assert bad == {0: 0, 1: 0, 2: 0}, bad
+
+
+# --------------------------------------------------------------------------- layout
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_layout_named_workloads(name):
+    T, H, E, G, k, cap, fp8, kind = W.CONFIGS[name]
+    idx, _ = W.route(kind, T, E, k, G, seed=0)
+    note("layout %s T=%d k=%d E=%d cap=%d" % (name, T, k, E, cap))
+    g = layout_to_host(gpu_layout(idx, E, G, cap))
+    assert_layout_equal(g, oracle.layout(idx, E, G, cap), name)
+
+
+def _edge_layouts():
+    g = np.random.default_rng(77)
+    cases = [
+        ("empty", np.zeros((0, 4), np.int64), 8, 2, 0),
+        ("one pair", np.array([[0]], np.int64), 1, 1, 0),
+        ("ragged 2049 pairs", g.integers(0, 16, (2049, 1)), 16, 4, 0),
+        ("ragged 4097 pairs k=17", g.integers(0, 64, (241, 17)), 64, 8, 0),
+        ("all to one expert", np.full((3000, 8), 5, np.int64), 256, 8, 0),
+        ("masked and bad ids", g.integers(-3, 40, (1500, 6)), 32, 4, 0),
+        ("all unrouted", np.full((100, 4), -1, np.int64), 16, 4, 0),
+        ("E=1024", g.integers(0, 1024, (8192, 8)), 1024, 8, 0),
+        ("E=3 G=3", g.integers(0, 3, (999, 2)), 3, 3, 0),
+        ("k=64", g.integers(0, 128, (300, 64)), 128, 2, 0),
+        ("padded overflow cap=1", g.integers(0, 8, (500, 4)), 8, 2, 1),
+        ("padded overflow cap=37", g.integers(-1, 16, (2500, 3)), 16, 4, 37),
+        ("padded hot expert", np.concatenate([np.zeros((700, 1)), g.integers(1, 64, (700, 5))], 1), 64, 8, 128),
+        ("many chunks, few experts", g.integers(0, 4, (200000, 2)), 4, 2, 0),
+    ]
+    return cases
+
+
+@pytest.mark.parametrize("case", range(len(_edge_layouts())))
+def test_layout_edge_cases(case):
+    name, idx, E, G, cap = _edge_layouts()[case]
+    idx = np.ascontiguousarray(idx, np.int64)
+    note("layout edge case: %s %s" % (name, idx.shape))
+    g = layout_to_host(gpu_layout(idx, E, G, cap))
+    assert_layout_equal(g, oracle.layout(idx, E, G, cap), name)
+
+
+def test_layout_is_deterministic():
+    T, H, E, G, k, cap, fp8, kind = W.CONFIGS["skewed"]
+    idx, _ = W.route(kind, T, E, k, G, seed=3)
+    note("layout determinism (skewed, 5 runs)")
+    first = layout_to_host(gpu_layout(idx, E, G, cap))
+    for _ in range(4):
+        assert_layout_equal(layout_to_host(gpu_layout(idx, E, G, cap)), first, "rerun")
+
+
+# --------------------------------------------------------------------------- dispatch
+def _dispatch_gpu(wl, lay, fill=None):
+    R = lay.num_recv_rows
+    x = dev_bf16(wl.x_bits)
+    if wl.fp8:
+        recv = torch.zeros((R, wl.H), dtype=torch.uint8, device="cuda")
+        sc = torch.zeros((R, wl.H // 128), dtype=torch.float32, device="cuda")
+        if fill is not None:
+            recv.fill_(fill)
+            sc.fill_(float(fill))
+        B.ep_dispatch(x, lay, B.EP_FP8_E4M3, recv, sc)
+        torch.cuda.synchronize()
+        return recv.cpu().numpy(), sc.cpu().numpy()
+    recv = torch.zeros((R, wl.H), dtype=torch.bfloat16, device="cuda")
+    if fill is not None:
+        recv.view(torch.int16).fill_(fill)
+    B.ep_dispatch(x, lay, B.EP_BF16, recv)
+    torch.cuda.synchronize()
+    return host_bits(recv), None
+
+
+DISPATCH_CASES = [
+    # name, T, H (None = the workload's), override fp8
+    ("tiny", None, None, None),
+    ("skewed", 384, None, None),
+    ("dsv3", 256, None, None),
+    ("lowlat", None, None, None),
+    ("large", 512, None, None),
+    ("dsv3", 37, 128, None),      # 8 lanes per token, several tokens per workgroup
+    ("dsv3", 50, 384, None),      # 24 lanes rounded to 32
+    ("dsv3", 9, 16512, None),     # more vectors than one workgroup: the row loops
+    ("skewed", 70, 24, None),     # bf16, 3 vectors per row
+    ("skewed", 33, 16392, None),  # bf16, row loops
+    ("large", 300, 4096, False),  # bf16 at the large shape
+]
+
+
+@pytest.mark.parametrize("case", range(len(DISPATCH_CASES)))
+def test_dispatch_full_compare(case):
+    name, T, H, fp8 = DISPATCH_CASES[case]
+    wl = W.make(name, T=T, H=H)
+    if fp8 is not None:
+        wl.fp8 = fp8
+    note("dispatch %s T=%d H=%d fp8=%s cap=%d" % (name, wl.T, wl.H, wl.fp8, wl.cap))
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap)
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, wl.cap)
+    fill = 0x5A if wl.fp8 else 0x1234  # rows no slot names must keep it
+    q, s = _dispatch_gpu(wl, lay, fill=fill)
+    used = np.zeros(ol["num_recv_rows"], bool)
+    used[ol["slot_idx"][ol["slot_idx"] >= 0]] = True
+    if wl.fp8:
+        oq, os_ = oracle.dispatch_fp8(wl.x_bits, ol["slot_idx"], ol["num_recv_rows"])
+        assert (q[used] == oq[used]).all(), "FP8 codes differ"
+        assert (s[used].view(np.uint32) == os_[used].view(np.uint32)).all(), "FP8 scales differ"
+        assert (q[~used] == fill).all() and (s[~used] == float(fill)).all()
+    else:
+        orecv = oracle.dispatch_bf16(wl.x_bits, ol["slot_idx"], ol["num_recv_rows"])
+        assert (q[used] == orecv[used]).all(), "bf16 rows differ"
+        assert (q[~used] == fill).all()
+
+
+@pytest.mark.parametrize("name", ["dsv3", "large", "skewed"])
+def test_dispatch_full_size_sampled(name):
+    wl = W.make(name)
+    note("dispatch full size %s T=%d H=%d" % (name, wl.T, wl.H))
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap)
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, wl.cap, with_src=False)
+    q, s = _dispatch_gpu(wl, lay)
+    g_slots = layout_to_host(lay)["slot_idx"]
+    assert (g_slots == ol["slot_idx"]).all()
+    for t in sample_tokens(wl.T, 48):
+        rows = ol["slot_idx"][t]
+        if wl.fp8:
+            oq, os_ = oracle.quantize_token_fp8(wl.x_bits[t])
+            assert (q[rows] == oq).all(), "token %d codes" % t
+            assert (s[rows].view(np.uint32) == os_.view(np.uint32)).all(), "token %d scales" % t
+        else:
+            assert (q[rows] == wl.x_bits[t]).all(), "token %d rows" % t
+
+
+def test_dequant_matches_oracle():
+    wl = W.make("dsv3", T=128)
+    note("dequant (identity expert) T=128")
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
+    oq, os_ = oracle.dispatch_fp8(wl.x_bits, ol["slot_idx"], wl.R)
+    oy = oracle.dequant_fp8(oq, os_)
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, 0, with_src=False)
+    x = dev_bf16(wl.x_bits)
+    q = torch.empty((wl.R, wl.H), dtype=torch.uint8, device="cuda")
+    s = torch.empty((wl.R, wl.H // 128), dtype=torch.float32, device="cuda")
+    B.ep_dispatch(x, lay, B.EP_FP8_E4M3, q, s)
+    y = torch.empty((wl.R, wl.H), dtype=torch.bfloat16, device="cuda")
+    B.ep_dequant_fp8(q, s, y)
+    assert (host_bits(y) == oy).all()
+
+
+# --------------------------------------------------------------------------- combine
+COMBINE_CASES = [
+    # name, T, H, k override
+    ("tiny", None, None),
+    ("skewed", 300, None),
+    ("dsv3", 200, None),
+    ("large", 400, None),
+    ("lowlat", None, None),
+    ("dsv3", 33, 24),      # H % 16 != 0: 8-channel lanes
+    ("dsv3", 21, 16400),   # row loops
+    ("dsv3", 64, 128),     # several tokens per workgroup
+]
+
+
+def _combine_gpu(y_bits, w, lay, H):
+    y = dev_bf16(y_bits)
+    wt = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+    out = torch.empty((lay.num_tokens, H), dtype=torch.bfloat16, device="cuda")
+    B.ep_combine(y, wt, lay, out)
+    torch.cuda.synchronize()
+    return host_bits(out)
+
+
+@pytest.mark.parametrize("case", range(len(COMBINE_CASES)))
+def test_combine_random_expert_outputs(case):
+    name, T, H = COMBINE_CASES[case]
+    wl = W.make(name, T=T, H=H)
+    note("combine %s T=%d H=%d k=%d" % (name, wl.T, wl.H, wl.k))
+    y = W.random_expert_outputs(wl.R, wl.H, seed=5)
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap)
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, wl.cap, with_src=False)
+    got = _combine_gpu(y, wl.topk_weights, lay, wl.H)
+    ref = oracle.combine(y, wl.topk_weights, ol["slot_idx"])
+    assert_close_bf16(got, ref, "combine %s" % name)
+
+
+@pytest.mark.parametrize("k", [1, 3, 9, 13])
+def test_combine_other_topk(k):
+    """k outside the compile-time set runs the general loop."""
+    wl = W.custom(T=150, H=512, E=32, k=k, G=4, seed=k)
+    note("combine k=%d" % k)
+    y = W.random_expert_outputs(wl.R, wl.H, seed=k)
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, 0, with_src=False)
+    assert_close_bf16(_combine_gpu(y, wl.topk_weights, lay, wl.H),
+                      oracle.combine(y, wl.topk_weights, ol["slot_idx"]), "combine k=%d" % k)
+
+
+def test_combine_skips_dropped_and_unrouted_pairs():
+    """Padded layout with drops, unrouted pairs and NaN in every row no slot
+    names: nothing from those rows reaches the output."""
+    g = np.random.default_rng(8)
+    T, k, E, cap, H = 400, 4, 8, 150, 256
+    idx = g.integers(-1, E, (T, k)).astype(np.int64)
+    w = g.random((T, k)).astype(np.float32)
+    note("combine with drops and NaN rows")
+    ol = oracle.layout(idx, E, 2, cap)
+    assert ol["error_flags"] & 2
+    y = W.random_expert_outputs(E * cap, H, seed=9)
+    used = np.zeros(E * cap, bool)
+    used[ol["slot_idx"][ol["slot_idx"] >= 0]] = True
+    y[~used] = 0x7FC0  # NaN
+    lay = gpu_layout(idx, E, 2, cap, with_src=False)
+    got = _combine_gpu(y, w, lay, H)
+    assert_close_bf16(got, oracle.combine(y, w, ol["slot_idx"]), "combine drops")
+
+
+def test_combine_full_size_sampled():
+    wl = W.make("dsv3")
+    note("combine full size dsv3 with random expert outputs")
+    y = W.random_expert_outputs(wl.R, wl.H, seed=6)
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, 0, with_src=False)
+    got = _combine_gpu(y, wl.topk_weights, lay, wl.H)
+    toks = sample_tokens(wl.T, 48)
+    ref = oracle.combine_tokens(y, wl.topk_weights, ol["slot_idx"], toks)
+    assert_close_bf16(got[toks], ref, "combine dsv3 full size")
+
+
+# --------------------------------------------------------------------------- whole path
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_whole_path_identity_experts(name):
+    """layout -> dispatch -> identity expert -> combine at the full size, on
+    the GPU; sampled tokens through the oracle's own chain."""
+    wl = W.make(name)
+    note("whole path %s T=%d H=%d E=%d k=%d fp8=%s cap=%d" % (
+        name, wl.T, wl.H, wl.E, wl.k, wl.fp8, wl.cap))
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, wl.cap, with_src=False)
+    x = dev_bf16(wl.x_bits)
+    R, H = wl.R, wl.H
+    if wl.fp8:
+        q = torch.empty((R, H), dtype=torch.uint8, device="cuda")
+        s = torch.empty((R, H // 128), dtype=torch.float32, device="cuda")
+        B.ep_dispatch(x, lay, B.EP_FP8_E4M3, q, s)
+        y = torch.zeros((R, H), dtype=torch.bfloat16, device="cuda")
+        B.ep_dequant_fp8(q, s, y)
+        del q, s
+    else:
+        y = torch.zeros((R, H), dtype=torch.bfloat16, device="cuda")
+        B.ep_dispatch(x, lay, B.EP_BF16, y)
+    out = torch.empty((wl.T, H), dtype=torch.bfloat16, device="cuda")
+    B.ep_combine(y, torch.from_numpy(wl.topk_weights).cuda(), lay, out)
+    got = host_bits(out)
+    del y
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap)
+    toks = sample_tokens(wl.T, 64) if wl.T > 256 else np.arange(wl.T)
+    chain = oracle.chain_fp8_tokens if wl.fp8 else oracle.chain_bf16_tokens
+    ref = chain(wl.x_bits, wl.topk_weights, ol["slot_idx"], toks)
+    assert_close_bf16(got[toks], ref, "whole path %s" % name)
+    if not wl.fp8:
+        # bf16 dispatch, identity experts, weights summing to 1: x comes back
+        same = (got[toks] == wl.x_bits[toks]) | (((got[toks] | wl.x_bits[toks]) & 0x7FFF) == 0)
+        assert same.all()
+
+
+def test_error_flags_on_gpu():
+    idx = np.array([[0, 9], [1, -1], [0, 0]], np.int64)
+    note("error flags")
+    g = layout_to_host(gpu_layout(idx, 4, 1, 0))
+    assert g["error_flags"] == 1 and g["slot_idx"][0, 1] == -1 and g["slot_idx"][1, 1] == -1
+    g = layout_to_host(gpu_layout(np.zeros((5, 2), np.int64), 4, 1, 3))
+    assert g["error_flags"] == 2 and (g["slot_idx"].reshape(-1)[3:] == -1).all()
+    g = layout_to_host(gpu_layout(np.zeros((3, 1), np.int64), 4, 1, 0))
+    assert g["error_flags"] == 0
