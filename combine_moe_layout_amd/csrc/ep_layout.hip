@@ -21,9 +21,10 @@
 //      slot_idx.
 //   2. finish: one workgroup per chunk again.  Each sums the chunk totals of
 //      earlier chunks (its base inside each expert) and of all chunks (the
-//      expert totals), scans the totals into expert offsets, and turns the
-//      packed values of its chunk into receive rows.  Workgroup 0 also writes
-//      the counts, offsets, group totals and error flags.
+//      expert totals) -- staging the whole count matrix in LDS with every load
+//      in flight at once when it fits -- scans the totals into expert offsets,
+//      and turns the packed values of its chunk into receive rows.  Workgroup
+//      0 also writes the counts, offsets, group totals and error flags.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -103,6 +104,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
   }
 }
 
+// Per-chunk counts up to this many ints are staged whole in LDS by the finish
+// kernel (all loads in flight at once); larger matrices are summed from memory.
+constexpr int kStageInts = 12288;
+static_assert(kStageInts % (4 * kLayoutThreads) == 0, "staging is done in whole 16-byte batches");
+
 __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(
     int64_t num_pairs, int32_t num_experts, int32_t num_groups, int32_t capacity,
     int32_t num_chunks, const int32_t* __restrict__ chunk_count,
@@ -110,6 +116,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(
     int32_t* __restrict__ recv_src, int32_t* __restrict__ num_tokens_per_expert,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ num_tokens_per_group,
     int32_t* __restrict__ error_flags) {
+  __shared__ int32_t s_counts[kStageInts];
   __shared__ int32_t s_tot[EP_MAX_EXPERTS];
   __shared__ int32_t s_pre[EP_MAX_EXPERTS];
   __shared__ int32_t s_off[EP_MAX_EXPERTS];
@@ -119,21 +126,67 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
+  const int64_t chunk_base = (int64_t)c * kChunkPairs;
+
+  // This chunk's packed (rank, expert) values, fetched now so that their
+  // latency overlaps the count loads below.
+  int32_t packed[kLayoutItems];
+#pragma unroll
+  for (int i = 0; i < kLayoutItems; ++i) {
+    const int64_t p = chunk_base + i * kLayoutThreads + tid;
+    packed[i] = p < num_pairs ? slot_idx[p] : -1;
+  }
 
   // 1. expert totals over all chunks, and over the chunks before this one
   for (int e = tid; e < E; e += kLayoutThreads) {
     s_tot[e] = 0;
     s_pre[e] = 0;
   }
-  __syncthreads();
-  {
+  const int64_t matrix = (int64_t)num_chunks * E;
+  if (matrix <= kStageInts) {
+    // 16-byte loads, a fixed number per thread, all issued before the first
+    // is waited for (the workspace is 256-byte aligned)
+    constexpr int kBatch = kStageInts / 4 / kLayoutThreads;
+    const int n4 = (int)(matrix / 4);
+    const int4* src4 = reinterpret_cast<const int4*>(chunk_count);
+    int4* dst4 = reinterpret_cast<int4*>(s_counts);
+    if (n4 > 0) {
+      int4 r[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int i = tid + b * kLayoutThreads;
+        r[b] = src4[i < n4 ? i : n4 - 1];  // unconditional, so r stays in registers
+      }
+      // unconditional as well: entries past the matrix land in the unused
+      // tail of s_counts and are never read
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) dst4[tid + b * kLayoutThreads] = r[b];
+    }
+    for (int i = 4 * n4 + tid; i < matrix; i += kLayoutThreads) s_counts[i] = chunk_count[i];
+    __syncthreads();
     const int lanes_per_expert = E >= kLayoutThreads ? 1 : kLayoutThreads / E;
     const int span = E >= kLayoutThreads ? E : E * lanes_per_expert;
     for (int idx = tid; idx < span; idx += kLayoutThreads) {
       const int e = idx % E;
       const int sub = idx / E;
       int32_t tot = 0, pre = 0;
-#pragma unroll 8
+      for (int cc = sub; cc < num_chunks; cc += lanes_per_expert) {
+        const int32_t v = s_counts[cc * E + e];
+        tot += v;
+        pre += cc < c ? v : 0;
+      }
+      atomicAdd(&s_tot[e], tot);
+      atomicAdd(&s_pre[e], pre);
+    }
+  } else {
+    __syncthreads();
+    const int lanes_per_expert = E >= kLayoutThreads ? 1 : kLayoutThreads / E;
+    const int span = E >= kLayoutThreads ? E : E * lanes_per_expert;
+    for (int idx = tid; idx < span; idx += kLayoutThreads) {
+      const int e = idx % E;
+      const int sub = idx / E;
+      int32_t tot = 0, pre = 0;
+#pragma unroll 16
       for (int cc = sub; cc < num_chunks; cc += lanes_per_expert) {
         const int32_t v = chunk_count[(int64_t)cc * E + e];
         tot += v;
@@ -175,11 +228,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(
   __syncthreads();
 
   // 3. receive rows of this chunk's pairs
-  const int64_t chunk_base = (int64_t)c * kChunkPairs;
-  for (int i = tid; i < kChunkPairs; i += kLayoutThreads) {
-    const int64_t p = chunk_base + i;
+#pragma unroll
+  for (int i = 0; i < kLayoutItems; ++i) {
+    const int64_t p = chunk_base + i * kLayoutThreads + tid;
     if (p >= num_pairs) break;
-    const int32_t v = slot_idx[p];
+    const int32_t v = packed[i];
     int32_t s = -1;
     if (v >= 0) {
       const int e = v & ((1 << kExpertBits) - 1);
