@@ -149,6 +149,9 @@ def _edge_layouts():
         ("padded overflow cap=37", g.integers(-1, 16, (2500, 3)), 16, 4, 37),
         ("padded hot expert", np.concatenate([np.zeros((700, 1)), g.integers(1, 64, (700, 5))], 1), 64, 8, 128),
         ("many chunks, few experts", g.integers(0, 4, (200000, 2)), 4, 2, 0),
+        # more chunks than workgroups resident at once: the two-launch path
+        ("1.1M pairs, 547 chunks", g.integers(0, 64, (140000, 8)), 64, 8, 0),
+        ("1.1M pairs padded", g.integers(-1, 64, (140000, 8)), 64, 8, 20000),
     ]
     return cases
 
