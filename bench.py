@@ -11,7 +11,9 @@ path and not timed.
 
 Prints one JSON line.  `value` is the step's ideal (algorithmic) HBM bytes
 divided by the step's wall time; the per-kernel times come from HIP events
-recorded on the stream the kernels run on.
+recorded on the stream the kernels run on.  `--workload` times the other
+named workloads (tiny, skewed, lowlat, large) the same way; the default is the
+configuration the metric is quoted on.
 """
 from __future__ import annotations
 
@@ -118,6 +120,14 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", default="dsv3",
+                    help="dsv3 (default: the metric's configuration), tiny, skewed, lowlat or large")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays (launch-bound "
+                         "workloads); per-kernel times are then not reported")
+    ap.add_argument("--fused", action="store_true",
+                    help="layout and dispatch through ep_layout_dispatch (one launch for batches "
+                         "of at most 2048 pairs); the layout/dispatch split is then not reported")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -136,59 +146,98 @@ def main() -> int:
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
-    name = "dsv3"
+    name = args.workload
+    if name not in W.CONFIGS:
+        print("unknown workload %r; choose from %s" % (name, ", ".join(W.CONFIGS)), file=sys.stderr)
+        return 2
     wl = W.make(name, seed=args.seed)
-    T, H, E, G, k = wl.T, wl.H, wl.E, wl.G, wl.k
+    T, H, E, G, k, fp8 = wl.T, wl.H, wl.E, wl.G, wl.k, wl.fp8
+    dtype_enum = B.EP_FP8_E4M3 if fp8 else B.EP_BF16
     x = torch.from_numpy(wl.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     topk_idx = torch.from_numpy(wl.topk_idx).to(dev)
     topk_w = torch.from_numpy(wl.topk_weights).to(dev)
     lay = B.EpLayout(T, k, E, G, wl.cap, device=dev)
     R = lay.num_recv_rows
-    recv_q = torch.empty((R, H), dtype=torch.uint8, device=dev)
-    recv_s = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+    if fp8:
+        recv_q = torch.empty((R, H), dtype=torch.uint8, device=dev)
+        recv_s = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+    else:
+        recv_q = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+        recv_s = None
     y = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
-    # identity expert, once, untimed
+    # identity expert, once, untimed; y is its own buffer, as an expert's output would be
     B.ep_get_layout(topk_idx, lay)
-    B.ep_dispatch(x, lay, B.EP_FP8_E4M3, recv_q, recv_s)
-    B.ep_dequant_fp8(recv_q, recv_s, y)
+    B.ep_dispatch(x, lay, dtype_enum, recv_q, recv_s)
+    if fp8:
+        B.ep_dequant_fp8(recv_q, recv_s, y)
+    else:
+        B.ep_copy(recv_q, y)
     torch.cuda.synchronize()
     used = int((lay.slot_idx >= 0).sum().item())
-    nbytes = ideal_bytes(T, H, E, G, k, used, True)
+    nbytes = ideal_bytes(T, H, E, G, k, used, fp8)
     step_bytes = sum(nbytes.values())
 
-    def step(ev=None):
+    def step(ev=None, s=None):
+        # s: the stream to launch on (None = torch's current stream, which is
+        # the capture stream while a graph is being recorded)
         if ev is not None:
-            ev[0].record(stream)
-        B.ep_get_layout(topk_idx, lay, stream)
+            ev[0].record(s)
+        if args.fused:
+            B.ep_layout_dispatch(topk_idx, lay, x, dtype_enum, recv_q, recv_s, s)
+            if ev is not None:
+                ev[1].record(s)
+        else:
+            B.ep_get_layout(topk_idx, lay, s)
+            if ev is not None:
+                ev[1].record(s)
+            B.ep_dispatch(x, lay, dtype_enum, recv_q, recv_s, s)
         if ev is not None:
-            ev[1].record(stream)
-        B.ep_dispatch(x, lay, B.EP_FP8_E4M3, recv_q, recv_s, stream)
+            ev[2].record(s)
+        B.ep_combine(y, topk_w, lay, out, s)
         if ev is not None:
-            ev[2].record(stream)
-        B.ep_combine(y, topk_w, lay, out, stream)
-        if ev is not None:
-            ev[3].record(stream)
+            ev[3].record(s)
 
     for _ in range(args.warmup):
-        step()
+        step(s=stream)
     torch.cuda.synchronize()
 
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
     # timed region: exactly K steps, synchronised on both sides
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    if graph is not None:
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    else:
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        if graph is not None:
+            events[i][0].record(stream)
+            graph.replay()
+            events[i][1].record(stream)
+        else:
+            step(events[i], stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    per = {"layout": [], "dispatch": [], "combine": []}
-    for ev in events:
-        per["layout"].append(ev[0].elapsed_time(ev[1]))
-        per["dispatch"].append(ev[1].elapsed_time(ev[2]))
-        per["combine"].append(ev[2].elapsed_time(ev[3]))
+    if graph is not None:
+        per = {"graph_step": [ev[0].elapsed_time(ev[1]) for ev in events]}
+    elif args.fused:
+        per = {"layout_dispatch": [ev[0].elapsed_time(ev[2]) for ev in events]}
+    else:
+        per = {"layout": [ev[0].elapsed_time(ev[1]) for ev in events],
+               "dispatch": [ev[1].elapsed_time(ev[2]) for ev in events]}
+    if graph is None:
+        per["combine"] = [ev[2].elapsed_time(ev[3]) for ev in events]
     us = {kname: float(np.mean(v)) * 1e3 for kname, v in per.items()}
     p50 = {kname: float(np.percentile(v, 50)) * 1e3 for kname, v in per.items()}
     p95 = {kname: float(np.percentile(v, 95)) * 1e3 for kname, v in per.items()}
@@ -210,9 +259,14 @@ def main() -> int:
     del src, dst
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dc_gbps = (nbytes["dispatch"] + nbytes["combine"]) / ((us["dispatch"] + us["combine"]) * 1e-6) / 1e9
-    combine_gbps = nbytes["combine"] / (us["combine"] * 1e-6) / 1e9
-    dispatch_gbps = nbytes["dispatch"] / (us["dispatch"] * 1e-6) / 1e9
+    if graph is None:
+        t_dispatch = us["layout_dispatch"] if args.fused else us["dispatch"]
+        d_bytes = nbytes["dispatch"] + (nbytes["layout"] if args.fused else 0)
+        dc_gbps = (d_bytes + nbytes["combine"]) / ((t_dispatch + us["combine"]) * 1e-6) / 1e9
+        combine_gbps = nbytes["combine"] / (us["combine"] * 1e-6) / 1e9
+        dispatch_gbps = d_bytes / (t_dispatch * 1e-6) / 1e9
+    else:
+        dc_gbps = combine_gbps = dispatch_gbps = None
     digest = sources_digest()
     traffic = committed_traffic("combine", name, digest)
 
@@ -228,27 +282,33 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp32",
-        "data": "synthetic (seeded: x ~ N(0,1) bf16, uniform-random top-8 of 256)",
-        "config": {"workload": W.DESCRIPTIONS[name], "T": T, "hidden": H, "experts": E,
-                   "groups": G, "topk": k, "dispatch_dtype": "fp8_e4m3+fp32 scale/128ch",
-                   "combine_dtype": "bf16", "step": "layout+dispatch+combine"},
+        "data": "synthetic (seeded: x ~ N(0,1) bf16; routing %s)" % W.CONFIGS[name][7],
+        "config": {"workload": W.DESCRIPTIONS[name], "name": name, "T": T, "hidden": H,
+                   "experts": E, "groups": G, "topk": k, "capacity": wl.cap,
+                   "dispatch_dtype": "fp8_e4m3+fp32 scale/128ch" if fp8 else "bf16",
+                   "combine_dtype": "bf16",
+                   "step": "layout_dispatch (fused call)+combine" if args.fused
+                   else "layout+dispatch+combine"},
         "pct_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "ideal_bytes": nbytes,
         "kernel_us_mean": {kk: round(v, 2) for kk, v in us.items()},
         "kernel_us_p50": {kk: round(v, 2) for kk, v in p50.items()},
         "kernel_us_p95": {kk: round(v, 2) for kk, v in p95.items()},
-        "dispatch_plus_combine_gbps": round(dc_gbps, 1),
-        "dispatch_plus_combine_pct_peak": round(100 * dc_gbps / HBM_PEAK_GBPS, 2),
-        "dispatch_gbps": round(dispatch_gbps, 1),
         "copy_kernel_gbps": round(copy_gbps, 1),
-        "roofline": {"kernel": "combine", "bound": "hbm", "achieved": round(combine_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(combine_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                     "algorithmic_bytes": nbytes["combine"]},
         "sources_digest": digest,
     }
-    if not args.no_cpu_baseline:
+    if graph is None:
+        result["dispatch_plus_combine_gbps"] = round(dc_gbps, 1)
+        result["dispatch_plus_combine_pct_peak"] = round(100 * dc_gbps / HBM_PEAK_GBPS, 2)
+        result["dispatch_gbps"] = round(dispatch_gbps, 1)
+        result["roofline"] = {
+            "kernel": "combine", "bound": "hbm", "achieved": round(combine_gbps, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(combine_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None if traffic is None else traffic["bytes_per_launch"],
+            "algorithmic_bytes": nbytes["combine"]}
+    else:
+        result["config"]["step"] += " (HIP graph replay)"
+    if not args.no_cpu_baseline and name == "dsv3":
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)
     return 0

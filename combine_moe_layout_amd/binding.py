@@ -56,6 +56,7 @@ SIGNATURES = {
     "ep_layout_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "ep_get_layout": (ctypes.c_int, [_vp, _LP, _vp, _sz, _vp]),
     "ep_dispatch": (ctypes.c_int, [_vp, _LP, _i32, _i32, _vp, _vp, _vp]),
+    "ep_layout_dispatch": (ctypes.c_int, [_vp, _LP, _vp, _sz, _vp, _i32, _i32, _vp, _vp, _vp]),
     "ep_combine": (ctypes.c_int, [_vp, _vp, _LP, _i32, _vp, _vp]),
     "ep_dequant_fp8": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp]),
     "ep_cast_e4m3_bits": (ctypes.c_int, [_u32, _i64, _i32, _vp, _vp]),
@@ -188,6 +189,24 @@ def ep_dispatch(x: torch.Tensor, layout: EpLayout, recv_dtype: int, recv_x: torc
         _ptr(x, "x", torch.bfloat16), ctypes.byref(layout.struct), H, recv_dtype,
         _ptr(recv_x, "recv_x", want), _ptr(recv_scales, "recv_scales", torch.float32),
         _stream(stream)))
+
+
+def ep_layout_dispatch(topk_idx: torch.Tensor, layout: EpLayout, x: torch.Tensor, recv_dtype: int,
+                       recv_x: torch.Tensor, recv_scales: torch.Tensor | None = None,
+                       stream=None) -> EpLayout:
+    """ep_get_layout followed by ep_dispatch; one launch for decode-sized batches."""
+    T, H = layout.num_tokens, x.shape[-1]
+    if tuple(topk_idx.shape) != (T, layout.num_topk):
+        raise ValueError("topk_idx shape %s does not match the layout" % (tuple(topk_idx.shape),))
+    if tuple(x.shape) != (T, H) or recv_x.shape[0] != layout.num_recv_rows or recv_x.shape[-1] != H:
+        raise ValueError("dispatch buffers do not match the layout")
+    want = torch.uint8 if recv_dtype == EP_FP8_E4M3 else torch.bfloat16
+    _check("ep_layout_dispatch", lib().ep_layout_dispatch(
+        _ptr(topk_idx, "topk_idx", torch.int64) if topk_idx.numel() else None,
+        ctypes.byref(layout.struct), layout.workspace.data_ptr(), layout.workspace.numel(),
+        _ptr(x, "x", torch.bfloat16), H, recv_dtype, _ptr(recv_x, "recv_x", want),
+        _ptr(recv_scales, "recv_scales", torch.float32), _stream(stream)))
+    return layout
 
 
 def ep_combine(expert_out: torch.Tensor, topk_weights: torch.Tensor, layout: EpLayout,

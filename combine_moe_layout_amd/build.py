@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libep.so")
-SOURCES = ["ep_api.hip", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_aux.hip"]
+SOURCES = ["ep_api.hip", "ep_layout.hip", "ep_dispatch.hip", "ep_fused.hip", "ep_combine.hip",
+           "ep_aux.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

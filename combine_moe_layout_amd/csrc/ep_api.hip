@@ -35,6 +35,38 @@ int check_layout(const ep_layout_t* L) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_LAUNCH; }
 
+// Checks shared by ep_get_layout and ep_layout_dispatch.
+int check_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
+                     size_t workspace_bytes) {
+  int rc = check_layout(layout);
+  if (rc != EP_OK) return rc;
+  const ep_layout_t& L = *layout;
+  if ((L.num_tokens > 0 && topk_idx == nullptr) || L.num_tokens_per_expert == nullptr ||
+      L.expert_offsets == nullptr || L.num_tokens_per_group == nullptr ||
+      L.error_flags == nullptr || workspace == nullptr)
+    return EP_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return EP_ERR_ALIGN;
+  if (workspace_bytes <
+      ep::layout_workspace_bytes(L.num_tokens * (int64_t)L.num_topk, L.num_experts))
+    return EP_ERR_WORKSPACE;
+  return EP_OK;
+}
+
+// Checks shared by ep_dispatch and ep_layout_dispatch (after the layout's).
+int check_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,
+                   void* recv_x, float* recv_scales) {
+  if (recv_dtype != EP_BF16 && recv_dtype != EP_FP8_E4M3) return EP_ERR_DTYPE;
+  const bool fp8 = recv_dtype == EP_FP8_E4M3;
+  if (hidden < 8 || hidden > EP_MAX_HIDDEN || hidden % 8 != 0 || (fp8 && hidden % 128 != 0))
+    return EP_ERR_SHAPE;
+  if (layout->num_tokens == 0) return EP_OK;
+  if (x == nullptr || recv_x == nullptr || (fp8 && recv_scales == nullptr)) return EP_ERR_NULL;
+  if (!aligned16(x) || !aligned16(recv_x) ||
+      (fp8 && (reinterpret_cast<uintptr_t>(recv_scales) & 3u) != 0))
+    return EP_ERR_ALIGN;
+  return EP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -68,36 +100,37 @@ size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t n
 
 int ep_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  int rc = check_layout(layout);
+  const int rc = check_get_layout(topk_idx, layout, workspace, workspace_bytes);
   if (rc != EP_OK) return rc;
-  const ep_layout_t& L = *layout;
-  if ((L.num_tokens > 0 && topk_idx == nullptr) || L.num_tokens_per_expert == nullptr ||
-      L.expert_offsets == nullptr || L.num_tokens_per_group == nullptr ||
-      L.error_flags == nullptr || workspace == nullptr)
-    return EP_ERR_NULL;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return EP_ERR_ALIGN;
-  if (workspace_bytes <
-      ep::layout_workspace_bytes(L.num_tokens * (int64_t)L.num_topk, L.num_experts))
-    return EP_ERR_WORKSPACE;
   return launch_status(
-      ep::launch_layout(topk_idx, L, workspace, static_cast<hipStream_t>(stream)));
+      ep::launch_layout(topk_idx, *layout, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int ep_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,
                 void* recv_x, float* recv_scales, void* stream) {
   int rc = check_layout(layout);
   if (rc != EP_OK) return rc;
-  if (recv_dtype != EP_BF16 && recv_dtype != EP_FP8_E4M3) return EP_ERR_DTYPE;
+  rc = check_dispatch(x, layout, hidden, recv_dtype, recv_x, recv_scales);
+  if (rc != EP_OK || layout->num_tokens == 0) return rc;
+  return launch_status(ep::launch_dispatch(x, *layout, hidden, recv_dtype == EP_FP8_E4M3, recv_x,
+                                           recv_scales, static_cast<hipStream_t>(stream)));
+}
+
+int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
+                       size_t workspace_bytes, const void* x, int32_t hidden, int32_t recv_dtype,
+                       void* recv_x, float* recv_scales, void* stream) {
+  int rc = check_get_layout(topk_idx, layout, workspace, workspace_bytes);
+  if (rc != EP_OK) return rc;
+  rc = check_dispatch(x, layout, hidden, recv_dtype, recv_x, recv_scales);
+  if (rc != EP_OK) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fp8 = recv_dtype == EP_FP8_E4M3;
-  if (hidden < 8 || hidden > EP_MAX_HIDDEN || hidden % 8 != 0 || (fp8 && hidden % 128 != 0))
-    return EP_ERR_SHAPE;
-  if (layout->num_tokens == 0) return EP_OK;
-  if (x == nullptr || recv_x == nullptr || (fp8 && recv_scales == nullptr)) return EP_ERR_NULL;
-  if (!aligned16(x) || !aligned16(recv_x) ||
-      (fp8 && (reinterpret_cast<uintptr_t>(recv_scales) & 3u) != 0))
-    return EP_ERR_ALIGN;
-  return launch_status(ep::launch_dispatch(x, *layout, hidden, fp8, recv_x, recv_scales,
-                                           static_cast<hipStream_t>(stream)));
+  if (ep::fused_layout_dispatch_fits(*layout))
+    return launch_status(
+        ep::launch_layout_dispatch_small(topk_idx, *layout, x, hidden, fp8, recv_x, recv_scales, s));
+  rc = launch_status(ep::launch_layout(topk_idx, *layout, workspace, s));
+  if (rc != EP_OK || layout->num_tokens == 0) return rc;
+  return launch_status(ep::launch_dispatch(x, *layout, hidden, fp8, recv_x, recv_scales, s));
 }
 
 int ep_combine(const void* expert_out, const float* topk_weights, const ep_layout_t* layout,

@@ -1,0 +1,250 @@
+// ep_fused.hip -- layout and dispatch in one launch for decode-sized batches.
+//
+// The pages' low-latency mode serves decode and small batches, where launch
+// latency rather than bandwidth sets the time ("DeepEP是什麼？…" (yololab.net),
+// section "高吞吐與低延遲工作負載"; v1's low-latency kernels dispatch in
+// tens of microseconds: erai.pro DeepEP article, section "Chi tiết").  For a
+// batch of at most kFusedMaxPairs (token, k) pairs this kernel computes the
+// same layout as ep_get_layout and the same receive rows as ep_dispatch, with
+// one launch and no barrier between workgroups:
+//   - every workgroup loads the whole (small) top-k table into LDS;
+//   - workgroup t < T finds its own token's receive rows directly: for each of
+//     its k pairs, the number of valid pairs routed to a lower expert (the
+//     expert's offset, contiguous mode) plus the number of earlier pairs
+//     routed to the same expert (its rank; padded mode keeps rank < capacity),
+//     counted over the table by all lanes and summed across the workgroup --
+//     exactly the stable counting-sort position ep_get_layout assigns;
+//     it writes those slot_idx / recv_src entries and then dispatches the
+//     token like ep_dispatch;
+//   - workgroup T writes the per-expert counts, offsets, group totals and
+//     error flags from an LDS histogram of the table.
+#include "ep_device.h"
+#include "ep_dispatch_token.h"
+#include "ep_internal.h"
+
+namespace ep {
+
+struct FusedArgs {
+  const int64_t* topk_idx;
+  int64_t num_tokens;
+  int32_t k, num_experts, num_groups, capacity, hidden;
+  const u32x4* x;
+  u32x4* recv;
+  float* scales;
+  int32_t* slot_idx;
+  int32_t* recv_src;
+  int32_t* num_tokens_per_expert;
+  int32_t* expert_offsets;
+  int32_t* num_tokens_per_group;
+  int32_t* error_flags;
+};
+
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Exclusive scan of n <= EP_MAX_EXPERTS values in LDS (in place into out),
+// returning the total; every thread of the block calls it.
+__device__ int32_t block_exclusive_scan(const int32_t* in, int32_t* out, int n, int32_t* s_wave) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int waves = (blockDim.x + kWave - 1) / kWave;
+  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int first = tid * per;
+  int32_t mine = 0;
+  for (int i = 0; i < per; ++i)
+    if (first + i < n) mine += in[first + i];
+  int32_t incl = mine;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int32_t v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  if (lane == kWave - 1) s_wave[wave] = incl;
+  __syncthreads();
+  int32_t before = 0, total = 0;
+  for (int w = 0; w < waves; ++w) {
+    before += w < wave ? s_wave[w] : 0;
+    total += s_wave[w];
+  }
+  int32_t run = before + incl - mine;
+  for (int i = 0; i < per; ++i) {
+    if (first + i < n) {
+      const int32_t v = in[first + i];
+      out[first + i] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  return total;
+}
+
+template <bool kFp8, bool kHw>
+__global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a) {
+  __shared__ int32_t s_idx[kFusedMaxPairs];  // expert of every pair, -1 if none
+  __shared__ int32_t s_sum[2 * kFusedMaxTopk];
+  __shared__ int32_t s_slot[kFusedMaxTopk];
+  __shared__ int32_t s_hist[EP_MAX_EXPERTS];
+  __shared__ int32_t s_off[EP_MAX_EXPERTS];
+  __shared__ int32_t s_wave[1024 / kWave];
+  __shared__ float s_scale[kMaxScalesPerBlock];
+  const int tid = threadIdx.x;
+  const int E = a.num_experts, k = a.k;
+  const int32_t P = (int32_t)(a.num_tokens * k);
+
+  bool bad = false;
+  for (int32_t p = tid; p < P; p += blockDim.x) {
+    const int64_t v = a.topk_idx[p];
+    const bool ok = v >= 0 && v < E;
+    bad |= !ok && v != -1;
+    s_idx[p] = ok ? (int32_t)v : -1;
+  }
+  if (tid < 2 * kFusedMaxTopk) s_sum[tid] = 0;
+  __syncthreads();
+
+  if (blockIdx.x == a.num_tokens) {
+    // metadata: histogram, offsets, group totals, flags
+    for (int e = tid; e < E; e += blockDim.x) s_hist[e] = 0;
+    __syncthreads();
+    for (int32_t p = tid; p < P; p += blockDim.x)
+      if (s_idx[p] >= 0) atomicAdd(&s_hist[s_idx[p]], 1);
+    __syncthreads();
+    const int32_t total = block_exclusive_scan(s_hist, s_off, E, s_wave);
+    bool over = false;
+    for (int e = tid; e < E; e += blockDim.x) {
+      a.num_tokens_per_expert[e] = s_hist[e];
+      a.expert_offsets[e] = a.capacity > 0 ? e * a.capacity : s_off[e];
+      over |= a.capacity > 0 && s_hist[e] > a.capacity;
+    }
+    if (tid == 0) a.expert_offsets[E] = a.capacity > 0 ? E * a.capacity : total;
+    const int per_group = E / a.num_groups;
+    for (int g = tid; g < a.num_groups; g += blockDim.x) {
+      int32_t s = 0;
+      for (int e = g * per_group; e < (g + 1) * per_group; ++e) s += s_hist[e];
+      a.num_tokens_per_group[g] = s;
+    }
+    const int any_bad = __syncthreads_or(bad ? 1 : 0);
+    const int any_over = __syncthreads_or(over ? 1 : 0);
+    if (tid == 0)
+      a.error_flags[0] = (any_bad ? EP_FLAG_BAD_EXPERT : 0) | (any_over ? EP_FLAG_OVERFLOW : 0);
+    return;
+  }
+
+  // this token's receive rows
+  const int64_t t = blockIdx.x;
+  // When one pass of the lanes covers the row, each lane's slice of the token
+  // is loaded now, so that its latency overlaps the table scan below.
+  const int32_t vecs = kFp8 ? a.hidden / 16 : a.hidden / 8;
+  const bool one_pass = vecs <= (int32_t)blockDim.x;
+  const u32x4* src = a.x + t * (a.hidden / 8);
+  u32x4 pre_lo = {0u, 0u, 0u, 0u}, pre_hi = {0u, 0u, 0u, 0u};
+  if (one_pass && tid < vecs) {
+    if constexpr (kFp8) {
+      pre_lo = src[2 * tid];
+      pre_hi = src[2 * tid + 1];
+    } else {
+      pre_lo = src[tid];
+    }
+  }
+  const int32_t p0 = (int32_t)(t * k);
+  int32_t e[kFusedMaxTopk], lower[kFusedMaxTopk], earlier[kFusedMaxTopk];
+#pragma unroll
+  for (int j = 0; j < kFusedMaxTopk; ++j) {
+    e[j] = j < k ? s_idx[p0 + j] : -1;
+    lower[j] = 0;
+    earlier[j] = 0;
+  }
+  for (int32_t p = tid; p < P; p += blockDim.x) {
+    const int32_t ep = s_idx[p];
+    if (ep < 0) continue;
+#pragma unroll
+    for (int j = 0; j < kFusedMaxTopk; ++j) {
+      lower[j] += ep < e[j] ? 1 : 0;
+      earlier[j] += (ep == e[j] && p < p0 + j) ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kFusedMaxTopk; ++j) {
+    const int32_t l = wave_sum(lower[j]), r = wave_sum(earlier[j]);
+    if (tid % kWave == 0 && j < k) {
+      atomicAdd(&s_sum[j], l);
+      atomicAdd(&s_sum[kFusedMaxTopk + j], r);
+    }
+  }
+  __syncthreads();
+  if (tid < k) {
+    const int j = tid;
+    int32_t s = -1;
+    if (e[j] >= 0) {
+      const int32_t rank = s_sum[kFusedMaxTopk + j];
+      if (a.capacity == 0) s = s_sum[j] + rank;
+      else if (rank < a.capacity) s = e[j] * a.capacity + rank;
+    }
+    s_slot[j] = s;
+    a.slot_idx[p0 + j] = s;
+    if (a.recv_src != nullptr && s >= 0) a.recv_src[s] = p0 + j;
+  }
+  __syncthreads();
+
+  // dispatch the token (one token per workgroup, all lanes on its row)
+  if (one_pass) {
+    if (tid < vecs) {
+      if constexpr (kFp8)
+        fp8_vector_codes<kHw>(pre_lo, pre_hi, tid, s_slot, k, a.recv, vecs, s_scale);
+      else
+        for (int32_t j = 0; j < k; ++j)
+          if (s_slot[j] >= 0) store_nt(a.recv + (int64_t)s_slot[j] * vecs + tid, pre_lo);
+    }
+  } else if constexpr (kFp8) {
+    fp8_token_codes<kHw>(src, a.hidden, tid, blockDim.x, s_slot, k, a.recv, s_scale);
+  } else {
+    bf16_token_copy(src, a.hidden, tid, blockDim.x, s_slot, k, a.recv);
+  }
+  if constexpr (kFp8) {
+    __syncthreads();
+    fp8_token_scales(a.hidden, tid, blockDim.x, s_slot, k, s_scale, a.scales);
+  }
+}
+
+bool fused_layout_dispatch_fits(const ep_layout_t& L) {
+  return L.num_tokens > 0 && L.num_tokens * (int64_t)L.num_topk <= kFusedMaxPairs &&
+         L.num_topk <= kFusedMaxTopk;
+}
+
+hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout_t& L,
+                                        const void* x, int32_t hidden, bool fp8, void* recv_x,
+                                        float* recv_scales, hipStream_t stream) {
+  FusedArgs a;
+  a.topk_idx = topk_idx;
+  a.num_tokens = L.num_tokens;
+  a.k = L.num_topk;
+  a.num_experts = L.num_experts;
+  a.num_groups = L.num_groups;
+  a.capacity = L.capacity;
+  a.hidden = hidden;
+  a.x = static_cast<const u32x4*>(x);
+  a.recv = static_cast<u32x4*>(recv_x);
+  a.scales = recv_scales;
+  a.slot_idx = L.slot_idx;
+  a.recv_src = L.recv_src;
+  a.num_tokens_per_expert = L.num_tokens_per_expert;
+  a.expert_offsets = L.expert_offsets;
+  a.num_tokens_per_group = L.num_tokens_per_group;
+  a.error_flags = L.error_flags;
+  // one token per workgroup: one lane per 16-byte output vector, whole waves,
+  // at least 256 lanes for the table scan, at most 1024 (longer rows loop)
+  const int32_t vecs = fp8 ? hidden / 16 : hidden / 8;
+  int32_t lanes = ((vecs + 63) / 64) * 64;
+  lanes = lanes < 256 ? 256 : (lanes > 1024 ? 1024 : lanes);
+  const dim3 grid((unsigned)(L.num_tokens + 1));
+  if (fp8)
+    hipLaunchKernelGGL((layout_dispatch_small_kernel<true, kDispatchUsesHwCast>), grid,
+                       dim3(lanes), 0, stream, a);
+  else
+    hipLaunchKernelGGL((layout_dispatch_small_kernel<false, kDispatchUsesHwCast>), grid,
+                       dim3(lanes), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace ep

@@ -41,7 +41,20 @@ hipError_t launch_cast_e4m3_bits(uint32_t first, int64_t n, int32_t method, uint
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
-// The encoder ep_dispatch uses: true = the gfx950 conversion instruction.
-extern const bool kDispatchUsesHwCast;
+// The encoder ep_dispatch uses: the gfx950 conversion instruction (OCP E4M3,
+// round to nearest even), checked against the software encoder and the
+// oracle over every fp32 input of magnitude <= 448.
+constexpr bool kDispatchUsesHwCast = true;
+
+// Batches of at most this many (token, k) pairs, with top-k at most
+// kFusedMaxTopk, take the one-launch layout+dispatch path.
+constexpr int kFusedMaxPairs = kChunkPairs;
+constexpr int kFusedMaxTopk = 8;
+
+bool fused_layout_dispatch_fits(const ep_layout_t& L);
+
+hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout_t& L,
+                                        const void* x, int32_t hidden, bool fp8, void* recv_x,
+                                        float* recv_scales, hipStream_t stream);
 
 }  // namespace ep

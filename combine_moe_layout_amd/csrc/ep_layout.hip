@@ -24,9 +24,10 @@
 //      receive rows of its chunk.  Workgroup 0 also writes the counts,
 //      offsets, group totals and error flags.
 // Two launches run the phases; the ranks travel from one to the other through
-// slot_idx, packed as (rank in chunk) << kExpertBits | expert.  (A single
-// cooperative launch with a grid barrier was measured slower on MI355X: the
-// cooperative launch costs more than the second ordinary launch.)
+// slot_idx, packed as (rank in chunk) << kExpertBits | expert.  An input of
+// one chunk (up to kChunkPairs pairs: decode batches) runs both phases in a
+// single workgroup and launch.  (A single cooperative launch with a grid
+// barrier was measured slower on MI355X than the two ordinary launches.)
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -60,14 +61,15 @@ __device__ __forceinline__ int64_t pair_of(int64_t c, int i) {
 
 // Phase 1 for chunk c: eid[i] = expert of item i (-1 if none), local[i] = its
 // rank among the chunk's pairs of that expert.  Writes the chunk's totals and
-// its bad-id flag.  Ends with the histograms no longer needed.
-__device__ __forceinline__ void count_chunk(const int64_t* __restrict__ topk_idx,
-                                            int64_t num_pairs, int32_t E, int32_t expert_bits,
-                                            int64_t c, int32_t* hist,
-                                            int32_t* __restrict__ chunk_count,
-                                            int32_t* __restrict__ chunk_flags,
-                                            int32_t (&eid)[kLayoutItems],
-                                            int32_t (&local)[kLayoutItems]) {
+// its bad-id flag (and, if tot_out is not null, the totals to that LDS array
+// too); returns the flag.  Ends with the histograms no longer needed.
+__device__ __forceinline__ int count_chunk(const int64_t* __restrict__ topk_idx,
+                                           int64_t num_pairs, int32_t E, int32_t expert_bits,
+                                           int64_t c, int32_t* hist,
+                                           int32_t* __restrict__ chunk_count,
+                                           int32_t* __restrict__ chunk_flags, int32_t* tot_out,
+                                           int32_t (&eid)[kLayoutItems],
+                                           int32_t (&local)[kLayoutItems]) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   int32_t* my_hist = hist + wave * EP_MAX_EXPERTS;
@@ -115,6 +117,7 @@ __device__ __forceinline__ void count_chunk(const int64_t* __restrict__ topk_idx
       run += h;
     }
     chunk_count[c * E + e] = run;
+    if (tot_out != nullptr) tot_out[e] = run;
   }
   const int any_bad = __syncthreads_or(bad ? 1 : 0);
   if (threadIdx.x == 0) chunk_flags[c] = any_bad ? EP_FLAG_BAD_EXPERT : 0;
@@ -122,21 +125,15 @@ __device__ __forceinline__ void count_chunk(const int64_t* __restrict__ topk_idx
   for (int i = 0; i < kLayoutItems; ++i)
     if (eid[i] >= 0) local[i] += my_hist[eid[i]];
   __syncthreads();
+  return any_bad ? EP_FLAG_BAD_EXPERT : 0;
 }
 
-// Phase 2 for chunk c, given every chunk's totals in memory.
-__device__ __forceinline__ void finish_chunk(
-    int64_t num_pairs, int32_t E, int32_t num_groups, int32_t capacity, int32_t num_chunks,
-    int64_t c, const int32_t* __restrict__ chunk_count, const int32_t* __restrict__ chunk_flags,
-    LayoutShared& sh, const int32_t (&eid)[kLayoutItems], const int32_t (&local)[kLayoutItems],
-    int32_t* __restrict__ slot_idx, int32_t* __restrict__ recv_src,
-    int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ expert_offsets,
-    int32_t* __restrict__ num_tokens_per_group, int32_t* __restrict__ error_flags) {
+// Expert totals over all chunks (sh.tot) and over the chunks before chunk c
+// (sh.pre), from the per-chunk totals in memory.
+__device__ __forceinline__ void chunk_totals(int32_t E, int32_t num_chunks, int64_t c,
+                                             const int32_t* __restrict__ chunk_count,
+                                             LayoutShared& sh) {
   const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = tid / kWave;
-
-  // 1. expert totals over all chunks, and over the chunks before this one
   for (int e = tid; e < E; e += kLayoutThreads) {
     sh.tot[e] = 0;
     sh.pre[e] = 0;
@@ -194,6 +191,26 @@ __device__ __forceinline__ void finish_chunk(
     }
   }
   __syncthreads();
+}
+
+// Phase 2 for chunk c, given every chunk's totals in memory.  kSingleChunk:
+// there is only this chunk, sh.tot and sh.pre are already set by the caller
+// and known_bad is its bad-id flag.
+template <bool kSingleChunk>
+__device__ __forceinline__ void finish_chunk(
+    int64_t num_pairs, int32_t E, int32_t num_groups, int32_t capacity, int32_t num_chunks,
+    int64_t c, const int32_t* __restrict__ chunk_count, const int32_t* __restrict__ chunk_flags,
+    LayoutShared& sh, const int32_t (&eid)[kLayoutItems], const int32_t (&local)[kLayoutItems],
+    int32_t* __restrict__ slot_idx, int32_t* __restrict__ recv_src,
+    int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ num_tokens_per_group, int32_t* __restrict__ error_flags,
+    int32_t known_bad) {
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+
+  // 1. expert totals over all chunks, and over the chunks before this one
+  if constexpr (!kSingleChunk) chunk_totals(E, num_chunks, c, chunk_count, sh);
 
   // 2. exclusive scan of the totals (contiguous mode) -> expert offsets
   const int per = (E + kLayoutThreads - 1) / kLayoutThreads;
@@ -256,7 +273,11 @@ __device__ __forceinline__ void finish_chunk(
       num_tokens_per_group[g] = s;
     }
     int32_t bad = 0;
-    for (int cc = tid; cc < num_chunks; cc += kLayoutThreads) bad |= chunk_flags[cc];
+    if constexpr (kSingleChunk) {
+      bad = known_bad;
+    } else {
+      for (int cc = tid; cc < num_chunks; cc += kLayoutThreads) bad |= chunk_flags[cc];
+    }
     const int any_bad = __syncthreads_or(bad);
     const int any_over = __syncthreads_or(over ? 1 : 0);
     if (tid == 0)
@@ -283,7 +304,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(LayoutArgs
   __shared__ int32_t hist[kLayoutWaves * EP_MAX_EXPERTS];
   int32_t eid[kLayoutItems], local[kLayoutItems];
   count_chunk(a.topk_idx, a.num_pairs, a.num_experts, a.expert_bits, blockIdx.x, hist,
-              a.chunk_count, a.chunk_flags, eid, local);
+              a.chunk_count, a.chunk_flags, nullptr, eid, local);
 #pragma unroll
   for (int i = 0; i < kLayoutItems; ++i) {
     const int64_t p = pair_of(blockIdx.x, i);
@@ -302,9 +323,25 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(LayoutArg
     eid[i] = v >= 0 ? (v & ((1 << kExpertBits) - 1)) : -1;
     local[i] = v >= 0 ? (v >> kExpertBits) : 0;
   }
-  finish_chunk(a.num_pairs, a.num_experts, a.num_groups, a.capacity, a.num_chunks, blockIdx.x,
-               a.chunk_count, a.chunk_flags, sh, eid, local, a.slot_idx, a.recv_src,
-               a.num_tokens_per_expert, a.expert_offsets, a.num_tokens_per_group, a.error_flags);
+  finish_chunk<false>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, a.num_chunks,
+                      blockIdx.x, a.chunk_count, a.chunk_flags, sh, eid, local, a.slot_idx,
+                      a.recv_src, a.num_tokens_per_expert, a.expert_offsets,
+                      a.num_tokens_per_group, a.error_flags, 0);
+}
+
+// Inputs of at most one chunk (decode-sized batches): both phases in one
+// workgroup and one launch; the totals stay in LDS.
+__global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(LayoutArgs a) {
+  __shared__ LayoutShared sh;
+  int32_t eid[kLayoutItems], local[kLayoutItems];
+  const int bad = count_chunk(a.topk_idx, a.num_pairs, a.num_experts, a.expert_bits, 0,
+                              sh.counts, a.chunk_count, a.chunk_flags, sh.tot, eid, local);
+  for (int e = threadIdx.x; e < a.num_experts; e += kLayoutThreads) sh.pre[e] = 0;
+  __syncthreads();
+  finish_chunk<true>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, 1, 0, a.chunk_count,
+                     a.chunk_flags, sh, eid, local, a.slot_idx, a.recv_src,
+                     a.num_tokens_per_expert, a.expert_offsets, a.num_tokens_per_group,
+                     a.error_flags, bad);
 }
 
 hipError_t launch_layout(const int64_t* topk_idx, const ep_layout_t& L, void* workspace,
@@ -329,6 +366,10 @@ hipError_t launch_layout(const int64_t* topk_idx, const ep_layout_t& L, void* wo
   a.num_tokens_per_group = L.num_tokens_per_group;
   a.error_flags = L.error_flags;
 
+  if (chunks == 1) {
+    hipLaunchKernelGGL(layout_single_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   if (chunks > 0)
     hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)chunks), dim3(kLayoutThreads), 0,
                        stream, a);

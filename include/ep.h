@@ -157,6 +157,19 @@ int ep_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_
                 void* recv_x, float* recv_scales, void* stream);
 
 /*
+ * Layout and dispatch in one call: the same results as ep_get_layout followed
+ * by ep_dispatch with the same arguments.  For decode-sized batches -- at most
+ * 2048 (token, k) pairs and top-k at most 8 -- both run in a single launch
+ * (the pages' low-latency mode: "DeepEP是什麼？…" (yololab.net), section
+ * "高吞吐與低延遲工作負載"); larger batches run the two calls' kernels in turn.
+ * Arguments, layouts and status codes are those of ep_get_layout and
+ * ep_dispatch; the workspace is required in both cases.
+ */
+int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
+                       size_t workspace_bytes, const void* x, int32_t hidden, int32_t recv_dtype,
+                       void* recv_x, float* recv_scales, void* stream);
+
+/*
  * Combine ([yololab] stage table, combine row: back to token order with a
  * weighted reduction).  expert_out: device bf16 [R, hidden]; topk_weights:
  * device fp32 [T, k].  out[t] = bf16(sum over j with slot_idx[t*k+j] >= 0 of

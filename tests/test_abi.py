@@ -127,6 +127,12 @@ def test_entry_points_reject_bad_arguments(L):
     assert L.ep_dispatch(fake + 8, by(s), 256, 0, fake, None, None) == -3   # x alignment
     assert L.ep_dispatch(fake, by(s), 256, 1, fake, fake + 2, None) == -3   # scales alignment
     assert L.ep_dispatch(fake, None, 256, 0, fake, None, None) == -1
+    # fused layout + dispatch: the union of both calls' checks
+    assert L.ep_layout_dispatch(fake, by(s), fake, ws_need - 1, fake, 256, 1, fake, fake, None) == -4
+    assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake, 256, 9, fake, fake, None) == -6
+    assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake, 200, 1, fake, fake, None) == -2
+    assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake + 4, 256, 0, fake, None, None) == -3
+    assert L.ep_layout_dispatch(None, by(s), fake, ws_need, fake, 256, 0, fake, None, None) == -1
     # combine
     assert L.ep_combine(None, fake, by(s), 256, fake, None) == -1
     assert L.ep_combine(fake, fake, by(s), 256, fake + 4, None) == -3

@@ -394,3 +394,72 @@ def test_error_flags_on_gpu():
     assert g["error_flags"] == 2 and (g["slot_idx"].reshape(-1)[3:] == -1).all()
     g = layout_to_host(gpu_layout(np.zeros((3, 1), np.int64), 4, 1, 0))
     assert g["error_flags"] == 0
+
+
+# --------------------------------------------------------------------------- fused low-latency path
+def _fused_cases():
+    g = np.random.default_rng(31)
+    cases = []
+    wl = W.make("lowlat")
+    cases.append(("lowlat (padded, FP8)", wl.topk_idx, wl.x_bits, wl.E, wl.G, wl.cap, True))
+    wl = W.make("tiny")
+    cases.append(("tiny (bf16)", wl.topk_idx, wl.x_bits, wl.E, wl.G, wl.cap, False))
+    wl = W.make("dsv3", T=256)
+    cases.append(("2048 pairs, the largest fused batch", wl.topk_idx, wl.x_bits, wl.E, wl.G, 0, True))
+    cases.append(("one token, one expert", np.array([[0]], np.int64), W.draw_x(1, 256), 1, 1, 0, True))
+    idx = g.integers(-3, 24, (37, 3)).astype(np.int64)
+    idx[5] = [4, 4, 4]  # the same expert three times in one token
+    cases.append(("masked, bad ids, duplicates, bf16 H=200", idx, W.draw_x(37, 200), 20, 4, 0, False))
+    cases.append(("padded overflow cap=3", g.integers(0, 8, (60, 5)).astype(np.int64), W.draw_x(60, 384),
+                  8, 2, 3, True))
+    cases.append(("rows longer than a workgroup", g.integers(0, 64, (16, 8)).astype(np.int64),
+                  W.draw_x(16, 16512), 64, 8, 0, True))
+    return cases
+
+
+@pytest.mark.parametrize("case", range(len(_fused_cases())))
+def test_layout_dispatch_fused_small_batches(case):
+    name, idx, x_bits, E, G, cap, fp8 = _fused_cases()[case]
+    T, k = idx.shape
+    H = x_bits.shape[1]
+    note("fused layout+dispatch: %s T=%d k=%d E=%d H=%d cap=%d fp8=%s" % (name, T, k, E, H, cap, fp8))
+    lay = B.EpLayout(T, k, E, G, cap, with_recv_src=True)
+    lay.recv_src.fill_(-1)
+    R = lay.num_recv_rows
+    x = dev_bf16(x_bits)
+    if fp8:
+        q = torch.full((R, H), 0x5A, dtype=torch.uint8, device="cuda")
+        s = torch.full((R, H // 128), 7.0, dtype=torch.float32, device="cuda")
+        B.ep_layout_dispatch(torch.from_numpy(idx).cuda(), lay, x, B.EP_FP8_E4M3, q, s)
+    else:
+        q = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
+        q.view(torch.int16).fill_(0x1234)
+        s = None
+        B.ep_layout_dispatch(torch.from_numpy(idx).cuda(), lay, x, B.EP_BF16, q)
+    g_lay = layout_to_host(lay)
+    ol = oracle.layout(idx, E, G, cap)
+    assert_layout_equal(g_lay, ol, name)
+    used = np.zeros(R, bool)
+    used[ol["slot_idx"][ol["slot_idx"] >= 0]] = True
+    if fp8:
+        oq, os_ = oracle.dispatch_fp8(x_bits, ol["slot_idx"], R)
+        qh, sh = q.cpu().numpy(), s.cpu().numpy()
+        assert (qh[used] == oq[used]).all() and (sh[used].view(np.uint32) == os_[used].view(np.uint32)).all()
+        assert (qh[~used] == 0x5A).all() and (sh[~used] == 7.0).all()
+    else:
+        orecv = oracle.dispatch_bf16(x_bits, ol["slot_idx"], R)
+        qh = host_bits(q)
+        assert (qh[used] == orecv[used]).all() and (qh[~used] == 0x1234).all()
+
+
+def test_layout_dispatch_large_batch_takes_the_two_launch_path():
+    wl = W.make("dsv3", T=1024, H=1024)
+    note("ep_layout_dispatch on 8192 pairs")
+    lay = B.EpLayout(wl.T, wl.k, wl.E, wl.G, 0)
+    q = torch.empty((wl.R, wl.H), dtype=torch.uint8, device="cuda")
+    s = torch.empty((wl.R, wl.H // 128), dtype=torch.float32, device="cuda")
+    B.ep_layout_dispatch(torch.from_numpy(wl.topk_idx).cuda(), lay, dev_bf16(wl.x_bits), B.EP_FP8_E4M3, q, s)
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
+    assert (layout_to_host(lay)["slot_idx"] == ol["slot_idx"]).all()
+    oq, os_ = oracle.dispatch_fp8(wl.x_bits, ol["slot_idx"], wl.R)
+    assert (q.cpu().numpy() == oq).all() and (s.cpu().numpy().view(np.uint32) == os_.view(np.uint32)).all()
