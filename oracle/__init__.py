@@ -6,7 +6,7 @@ never imports, loads or calls it, and it shares no code with the HIP library.
 
 This module is a thin numpy <-> ctypes wrapper around ``ep_oracle.c``: plain,
 single-threaded scalar loops written from the definitions on the pages (cited
-in that file's header, with the readings R1..R12 it takes where the pages are
+in that file's header, with the readings R1..R14 it takes where the pages are
 silent).  Every function here only marshals arrays; all arithmetic is in C.
 """
 from __future__ import annotations
@@ -61,6 +61,10 @@ def _load(path: str) -> ctypes.CDLL:
     L.ep_oracle_dequant_fp8.argtypes = [vp, vp, i64, i32, vp]
     L.ep_oracle_combine.argtypes = [vp, vp, vp, i64, i32, i32, vp]
     L.ep_oracle_combine_tokens.argtypes = [vp, vp, vp, i32, i32, vp, i64, vp]
+    L.ep_oracle_quantize_token_fp8_pow2.argtypes = [vp, i32, vp, vp]
+    L.ep_oracle_dispatch_fp8_pow2.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    L.ep_oracle_combine_fp8.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp]
+    L.ep_oracle_combine_fp8_tokens.argtypes = [vp, vp, vp, vp, i32, i32, vp, i64, vp]
     return L
 
 
@@ -246,4 +250,53 @@ def chain_bf16_tokens(x_bits: np.ndarray, w: np.ndarray, slot_idx: np.ndarray, t
         yrow = np.ascontiguousarray(x_bits[t], np.uint16).reshape(1, H)
         local_slot = np.where(np.asarray(slot_idx[t]) >= 0, 0, -1).astype(np.int32).reshape(1, k)
         out[i] = combine(yrow, np.asarray(w[t], np.float32).reshape(1, k), local_slot)[0]
+    return out
+
+
+# ----------------------------------------------------------------------------- variants
+def quantize_token_fp8_pow2(x_row_bits: np.ndarray):
+    """Power-of-two scales (reading R13)."""
+    x_row_bits = _c(x_row_bits, np.uint16).reshape(-1)
+    H = x_row_bits.size
+    q = np.empty(H, np.uint8)
+    s = np.empty(H // 128, np.float32)
+    lib().ep_oracle_quantize_token_fp8_pow2(_p(x_row_bits), H, _p(q), _p(s))
+    return q, s
+
+
+def dispatch_fp8_pow2(x_bits: np.ndarray, slot_idx: np.ndarray, R: int):
+    x_bits = _c(x_bits, np.uint16)
+    slot_idx = _c(slot_idx, np.int32)
+    T, H = x_bits.shape
+    k = slot_idx.shape[1]
+    q = np.zeros((R, H), np.uint8)
+    s = np.zeros((R, H // 128), np.float32)
+    lib().ep_oracle_dispatch_fp8_pow2(_p(x_bits), T, k, H, _p(slot_idx), _p(q), _p(s))
+    return q, s
+
+
+def combine_fp8(q: np.ndarray, scales: np.ndarray, w: np.ndarray, slot_idx: np.ndarray) -> np.ndarray:
+    """Combine of FP8 expert outputs (reading R14)."""
+    q = _c(q, np.uint8)
+    scales = _c(scales, np.float32)
+    w = _c(w, np.float32)
+    slot_idx = _c(slot_idx, np.int32)
+    T, k = slot_idx.shape
+    H = q.shape[1]
+    out = np.empty((T, H), np.uint16)
+    lib().ep_oracle_combine_fp8(_p(q), _p(scales), _p(w), _p(slot_idx), T, k, H, _p(out))
+    return out
+
+
+def combine_fp8_tokens(q, scales, w, slot_idx, tokens) -> np.ndarray:
+    q = _c(q, np.uint8)
+    scales = _c(scales, np.float32)
+    w = _c(w, np.float32)
+    slot_idx = _c(slot_idx, np.int32)
+    tokens = _c(tokens, np.int64).reshape(-1)
+    k = slot_idx.shape[1]
+    H = q.shape[1]
+    out = np.empty((tokens.size, H), np.uint16)
+    lib().ep_oracle_combine_fp8_tokens(_p(q), _p(scales), _p(w), _p(slot_idx), k, H, _p(tokens),
+                                       tokens.size, _p(out))
     return out

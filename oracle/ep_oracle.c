@@ -27,7 +27,7 @@
  *   [donniechu] DeepEP v2 release notes, section "Số liệu kỹ thuật" (benchmark
  *             configuration: 8K tokens, hidden 7168, FP8 dispatch, BF16 combine).
  * Where the pages leave a step open, this file takes one plain reading; every
- * reading is named at the function that applies it (R1..R12 below).
+ * reading is named at the function that applies it (R1..R14 below).
  *
  * Readings
  *   R1  Order inside an expert's segment: stable in the flattened pair index
@@ -57,6 +57,10 @@
  *       FP8 dispatch the expert output is the dequantised receive row,
  *       bf16(decode(q) * scale), rounded once from the exact product.
  *   R12 Integer types: topk_idx int64; counts, offsets and slots int32.
+ *   R13 Power-of-two scale variant: the smallest power of two s with
+ *       448 * s >= a; codes from the exact rescale x / s.
+ *   R14 FP8 combine variant: expert outputs as E4M3 codes + per-block fp32
+ *       scales, decoded exactly inside the weighted sum.
  */
 #include <math.h>
 #include <stdint.h>
@@ -346,4 +350,91 @@ EXPORT void ep_oracle_combine_tokens(const uint16_t* y, const float* w, const in
                                      int32_t k, int32_t H, const int64_t* tokens, int64_t n,
                                      uint16_t* out_rows) {
     for (int64_t i = 0; i < n; ++i) combine_one(y, w, slot_idx, tokens[i], k, H, out_rows + i * H);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Variants: power-of-two scales, FP8 combine                                  */
+/* ([yololab] "FP8與低精度通訊": low precision cuts dispatch / combine volume;  */
+/* the scale format is the implementation's to fix)                            */
+/* ------------------------------------------------------------------------- */
+
+/* R13 Power-of-two scales: a block's scale is the smallest power of two s
+ * with 448 * s >= a, a = max(amax, 1e-4f); each code is the nearest E4M3
+ * value of clamp(x / s, -448, 448), ties to even (x / s is an exact
+ * power-of-two rescale). */
+EXPORT void ep_oracle_quantize_token_fp8_pow2(const uint16_t* x_row, int32_t H, uint8_t* q_row,
+                                              float* scales_row) {
+    const int32_t B = 128;
+    for (int32_t b = 0; b < H / B; ++b) {
+        float amax = 0.0f;
+        for (int32_t c = b * B; c < (b + 1) * B; ++c) {
+            float m = fabsf(bf16_to_float(x_row[c]));
+            if (m > amax) amax = m;
+        }
+        float a = amax > 1e-4f ? amax : 1e-4f;
+        int e;
+        frexp((double)a / 448.0, &e);                  /* a first guess */
+        while (ldexp(448.0, e - 1) >= (double)a) --e;  /* exact comparisons */
+        while (ldexp(448.0, e) < (double)a) ++e;
+        scales_row[b] = (float)ldexp(1.0, e);
+        for (int32_t c = b * B; c < (b + 1) * B; ++c) {
+            double v = ldexp((double)bf16_to_float(x_row[c]), -e);
+            if (v > 448.0) v = 448.0;
+            if (v < -448.0) v = -448.0;
+            q_row[c] = ep_oracle_e4m3_encode((float)v);
+        }
+    }
+}
+
+EXPORT void ep_oracle_dispatch_fp8_pow2(const uint16_t* x, int64_t T, int32_t k, int32_t H,
+                                        const int32_t* slot_idx, uint8_t* recv_q,
+                                        float* recv_scales) {
+    int32_t nb = H / 128;
+    uint8_t* q = (uint8_t*)malloc((size_t)H);
+    float* sc = (float*)malloc((size_t)nb * sizeof(float));
+    if (!q || !sc) { free(q); free(sc); return; }
+    for (int64_t t = 0; t < T; ++t) {
+        ep_oracle_quantize_token_fp8_pow2(x + t * H, H, q, sc);
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t s = slot_idx[t * k + j];
+            if (s < 0) continue;
+            memcpy(recv_q + (int64_t)s * H, q, (size_t)H);
+            memcpy(recv_scales + (int64_t)s * nb, sc, (size_t)nb * sizeof(float));
+        }
+    }
+    free(q);
+    free(sc);
+}
+
+/* R14 FP8 combine: the expert outputs arrive as E4M3 codes with one fp32
+ * scale per (row, 128-channel block); out[t] = bf16(sum_j w[t,j] * decode(q)
+ * * scale) over valid pairs, summed in fp64 (each product is exact there) and
+ * rounded once, nearest-even. */
+static void combine_fp8_one(const uint8_t* q, const float* scales, const float* w,
+                            const int32_t* slot_idx, int64_t t, int32_t k, int32_t H,
+                            uint16_t* out_row) {
+    int32_t nb = H / 128;
+    for (int32_t c = 0; c < H; ++c) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t s = slot_idx[t * k + j];
+            if (s < 0) continue;
+            acc += (double)w[t * k + j] * ep_oracle_e4m3_decode(q[(int64_t)s * H + c]) *
+                   (double)scales[(int64_t)s * nb + c / 128];
+        }
+        out_row[c] = ep_oracle_bf16_from_double(acc);
+    }
+}
+
+EXPORT void ep_oracle_combine_fp8(const uint8_t* q, const float* scales, const float* w,
+                                  const int32_t* slot_idx, int64_t T, int32_t k, int32_t H,
+                                  uint16_t* out) {
+    for (int64_t t = 0; t < T; ++t) combine_fp8_one(q, scales, w, slot_idx, t, k, H, out + t * H);
+}
+
+EXPORT void ep_oracle_combine_fp8_tokens(const uint8_t* q, const float* scales, const float* w,
+                                         const int32_t* slot_idx, int32_t k, int32_t H,
+                                         const int64_t* tokens, int64_t n, uint16_t* out_rows) {
+    for (int64_t i = 0; i < n; ++i)
+        combine_fp8_one(q, scales, w, slot_idx, tokens[i], k, H, out_rows + i * H);
 }

@@ -25,6 +25,7 @@ import oracle
 import test_oracle_dispatch_combine as pins_dc
 import test_oracle_formats as pins_fmt
 import test_oracle_layout as pins_lay
+import test_oracle_variants as pins_var
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ep_oracle.c")
 
@@ -61,6 +62,14 @@ MUTANTS = [
     ("combine drops the last pair", "for (int32_t j = 0; j < k; ++j) {\n            int32_t s = slot_idx[t * k + j];\n            if (s < 0) continue;\n            acc",
      "for (int32_t j = 0; j < k - 1; ++j) {\n            int32_t s = slot_idx[t * k + j];\n            if (s < 0) continue;\n            acc"),
     ("dequant reads the wrong block scale", "(double)scales[r * nb + c / 128]", "(double)scales[r * nb + c % nb]"),
+    ("power-of-two scale one step too large", "while (ldexp(448.0, e) < (double)a) ++e;",
+     "while (ldexp(448.0, e) <= (double)a) ++e;"),
+    ("power-of-two rescale multiplies", "double v = ldexp((double)bf16_to_float(x_row[c]), -e);",
+     "double v = ldexp((double)bf16_to_float(x_row[c]), e);"),
+    ("FP8 combine reads block 0's scale", "(double)scales[(int64_t)s * nb + c / 128];",
+     "(double)scales[(int64_t)s * nb];"),
+    ("FP8 combine forgets the weight", "acc += (double)w[t * k + j] * ep_oracle_e4m3_decode(",
+     "acc += ep_oracle_e4m3_decode("),
 ]
 
 
@@ -90,6 +99,10 @@ def _battery():
     checks += [lambda s=s: pins_lay.test_layout_brute_force_tiny(s) for s in range(12)]
     checks += [lambda: pins_dc.test_fp8_quantisation_properties("dsv3", 8)]
     checks += [lambda: pins_dc.test_combine_identity_round_trip("tiny")]
+    checks += [pins_var.test_pow2_golden_blocks, pins_var.test_combine_fp8_golden,
+               pins_var.test_combine_fp8_one_hot_is_the_dequantisation,
+               pins_var.test_combine_fp8_vs_float64_sum,
+               lambda: pins_var.test_pow2_scale_is_the_smallest_power_of_two("dsv3")]
     return checks
 
 
@@ -111,11 +124,13 @@ def _run_battery_on(lib_path: str) -> int:
 
 
 def _build_and_run(tmp_dir, i, old, new):
+    # the first occurrence is the site (a few lines recur in the variant
+    # functions further down, which have mutants of their own)
     src = open(SRC).read()
-    assert src.count(old) == 1, "mutation site must be unique: %r" % old
+    assert old in src, "mutation site not found: %r" % old
     mutated = os.path.join(tmp_dir, "mutant%d.c" % i)
     with open(mutated, "w") as f:
-        f.write(src.replace(old, new))
+        f.write(src.replace(old, new, 1))
     lib = os.path.join(tmp_dir, "libmutant%d.so" % i)
     subprocess.run(["gcc", *oracle.GCC_FLAGS, mutated, "-o", lib, "-lm"], check=True)
     r = subprocess.run([sys.executable, os.path.abspath(__file__), lib], capture_output=True,
