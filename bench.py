@@ -34,7 +34,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["ep_combine.hip", "ep_dispatch.hip", "ep_layout.hip", "ep_device.h"]
 
 
-def ideal_bytes(T: int, H: int, E: int, G: int, k: int, R_used: int, fp8: bool) -> dict:
+def ideal_bytes(T: int, H: int, E: int, G: int, k: int, R_used: int, fp8: bool,
+                fp8_combine: bool = False) -> dict:
     """Algorithmic HBM bytes of one pass (each byte the path must move, once).
 
     layout:   read topk_idx (8 B per pair), write slot_idx (4 B per pair),
@@ -42,14 +43,16 @@ def ideal_bytes(T: int, H: int, E: int, G: int, k: int, R_used: int, fp8: bool) 
     dispatch: read x once (2H B per token); per used receive row write H B of
               codes and 4*H/128 B of scales (FP8) or 2H B (bf16); read the
               token's k slots (4 B per pair).
-    combine:  per pair read one expert-output row (2H B), its weight and slot
-              (8 B); per token write one bf16 row (2H B).
+    combine:  per pair read one expert-output row (2H B; with FP8 expert
+              outputs H B of codes and 4*H/128 B of scales), its weight and
+              slot (8 B); per token write one bf16 row (2H B).
     """
     P = T * k
     layout = 8 * P + 4 * P + 4 * (E + (E + 1) + G)
     row = H + 4 * (H // 128) if fp8 else 2 * H
     dispatch = 2 * H * T + row * R_used + 4 * P
-    combine = 2 * H * R_used + 8 * P + 2 * H * T
+    in_row = H + 4 * (H // 128) if fp8_combine else 2 * H
+    combine = in_row * R_used + 8 * P + 2 * H * T
     return dict(layout=layout, dispatch=dispatch, combine=combine)
 
 
@@ -125,6 +128,11 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays (launch-bound "
                          "workloads); per-kernel times are then not reported")
+    ap.add_argument("--pow2", action="store_true",
+                    help="FP8 dispatch with power-of-two scales (EP_FP8_E4M3_POW2)")
+    ap.add_argument("--fp8-combine", action="store_true",
+                    help="expert outputs stay FP8 (the dispatched codes and scales) and combine "
+                         "reads them with ep_combine_fp8")
     ap.add_argument("--fused", action="store_true",
                     help="layout and dispatch through ep_layout_dispatch (one launch for batches "
                          "of at most 2048 pairs); the layout/dispatch split is then not reported")
@@ -152,7 +160,10 @@ def main() -> int:
         return 2
     wl = W.make(name, seed=args.seed)
     T, H, E, G, k, fp8 = wl.T, wl.H, wl.E, wl.G, wl.k, wl.fp8
-    dtype_enum = B.EP_FP8_E4M3 if fp8 else B.EP_BF16
+    if args.fp8_combine and not fp8:
+        print("--fp8-combine needs an FP8 workload", file=sys.stderr)
+        return 2
+    dtype_enum = (B.EP_FP8_E4M3_POW2 if args.pow2 else B.EP_FP8_E4M3) if fp8 else B.EP_BF16
     x = torch.from_numpy(wl.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     topk_idx = torch.from_numpy(wl.topk_idx).to(dev)
     topk_w = torch.from_numpy(wl.topk_weights).to(dev)
@@ -164,19 +175,21 @@ def main() -> int:
     else:
         recv_q = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
         recv_s = None
-    y = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    y = None if args.fp8_combine else torch.empty((R, H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
     # identity expert, once, untimed; y is its own buffer, as an expert's output would be
     B.ep_get_layout(topk_idx, lay)
     B.ep_dispatch(x, lay, dtype_enum, recv_q, recv_s)
-    if fp8:
+    if args.fp8_combine:
+        pass  # the FP8 receive buffer itself is the expert output
+    elif fp8:
         B.ep_dequant_fp8(recv_q, recv_s, y)
     else:
         B.ep_copy(recv_q, y)
     torch.cuda.synchronize()
     used = int((lay.slot_idx >= 0).sum().item())
-    nbytes = ideal_bytes(T, H, E, G, k, used, fp8)
+    nbytes = ideal_bytes(T, H, E, G, k, used, fp8, args.fp8_combine)
     step_bytes = sum(nbytes.values())
 
     def step(ev=None, s=None):
@@ -195,7 +208,10 @@ def main() -> int:
             B.ep_dispatch(x, lay, dtype_enum, recv_q, recv_s, s)
         if ev is not None:
             ev[2].record(s)
-        B.ep_combine(y, topk_w, lay, out, s)
+        if args.fp8_combine:
+            B.ep_combine_fp8(recv_q, recv_s, topk_w, lay, out, s)
+        else:
+            B.ep_combine(y, topk_w, lay, out, s)
         if ev is not None:
             ev[3].record(s)
 
@@ -268,7 +284,8 @@ def main() -> int:
     else:
         dc_gbps = combine_gbps = dispatch_gbps = None
     digest = sources_digest()
-    traffic = committed_traffic("combine", name, digest)
+    # the committed counters cover the bf16-input combine kernel only
+    traffic = None if args.fp8_combine else committed_traffic("combine", name, digest)
 
     result = {
         "metric": "dispatch+combine effective HBM GB/s (% peak) at 8K tok×7168, top-8/256",
@@ -285,8 +302,9 @@ def main() -> int:
         "data": "synthetic (seeded: x ~ N(0,1) bf16; routing %s)" % W.CONFIGS[name][7],
         "config": {"workload": W.DESCRIPTIONS[name], "name": name, "T": T, "hidden": H,
                    "experts": E, "groups": G, "topk": k, "capacity": wl.cap,
-                   "dispatch_dtype": "fp8_e4m3+fp32 scale/128ch" if fp8 else "bf16",
-                   "combine_dtype": "bf16",
+                   "dispatch_dtype": ("fp8_e4m3+pow2 scale/128ch" if args.pow2 else
+                                      "fp8_e4m3+fp32 scale/128ch") if fp8 else "bf16",
+                   "combine_dtype": "fp8_e4m3 in, bf16 out" if args.fp8_combine else "bf16",
                    "step": "layout_dispatch (fused call)+combine" if args.fused
                    else "layout+dispatch+combine"},
         "pct_peak": round(100 * value / HBM_PEAK_GBPS, 2),
@@ -302,7 +320,8 @@ def main() -> int:
         result["dispatch_plus_combine_pct_peak"] = round(100 * dc_gbps / HBM_PEAK_GBPS, 2)
         result["dispatch_gbps"] = round(dispatch_gbps, 1)
         result["roofline"] = {
-            "kernel": "combine", "bound": "hbm", "achieved": round(combine_gbps, 1),
+            "kernel": "combine_fp8" if args.fp8_combine else "combine", "bound": "hbm",
+            "achieved": round(combine_gbps, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(combine_gbps / HBM_PEAK_GBPS, 4),
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
             "algorithmic_bytes": nbytes["combine"]}

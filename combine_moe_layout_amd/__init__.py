@@ -6,8 +6,9 @@ tensors into it under the same names.  Importing this package loads nothing:
 the library is opened on first use and a missing library is an error, never a
 fallback.
 """
-from .binding import (EP_BF16, EP_FLAG_BAD_EXPERT, EP_FLAG_OVERFLOW, EP_FP8_E4M3, EpError,
-                      EpLayout, ep_cast_e4m3_bits, ep_combine, ep_copy, ep_dequant_fp8,
+from .binding import (EP_BF16, EP_FLAG_BAD_EXPERT, EP_FLAG_OVERFLOW, EP_FP8_E4M3, EP_FP8_E4M3_POW2,
+                      EpError, EpLayout, ep_cast_e4m3_bits, ep_combine, ep_combine_fp8, ep_copy,
+                      ep_dequant_fp8,
                       ep_dispatch, ep_get_layout, ep_layout_dispatch, ep_layout_workspace_bytes,
                       ep_num_recv_rows,
                       ep_version)

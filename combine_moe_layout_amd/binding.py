@@ -17,6 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libep.so")
 EP_OK = 0
 EP_BF16 = 0
 EP_FP8_E4M3 = 1
+EP_FP8_E4M3_POW2 = 2
 EP_FLAG_BAD_EXPERT = 1
 EP_FLAG_OVERFLOW = 2
 EP_MAX_EXPERTS = 1024
@@ -58,6 +59,7 @@ SIGNATURES = {
     "ep_dispatch": (ctypes.c_int, [_vp, _LP, _i32, _i32, _vp, _vp, _vp]),
     "ep_layout_dispatch": (ctypes.c_int, [_vp, _LP, _vp, _sz, _vp, _i32, _i32, _vp, _vp, _vp]),
     "ep_combine": (ctypes.c_int, [_vp, _vp, _LP, _i32, _vp, _vp]),
+    "ep_combine_fp8": (ctypes.c_int, [_vp, _vp, _vp, _LP, _i32, _vp, _vp]),
     "ep_dequant_fp8": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp]),
     "ep_cast_e4m3_bits": (ctypes.c_int, [_u32, _i64, _i32, _vp, _vp]),
     "ep_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
@@ -184,7 +186,7 @@ def ep_dispatch(x: torch.Tensor, layout: EpLayout, recv_dtype: int, recv_x: torc
     T, H = layout.num_tokens, x.shape[-1]
     if tuple(x.shape) != (T, H) or recv_x.shape[0] != layout.num_recv_rows or recv_x.shape[-1] != H:
         raise ValueError("dispatch buffers do not match the layout")
-    want = torch.uint8 if recv_dtype == EP_FP8_E4M3 else torch.bfloat16
+    want = torch.bfloat16 if recv_dtype == EP_BF16 else torch.uint8
     _check("ep_dispatch", lib().ep_dispatch(
         _ptr(x, "x", torch.bfloat16), ctypes.byref(layout.struct), H, recv_dtype,
         _ptr(recv_x, "recv_x", want), _ptr(recv_scales, "recv_scales", torch.float32),
@@ -200,7 +202,7 @@ def ep_layout_dispatch(topk_idx: torch.Tensor, layout: EpLayout, x: torch.Tensor
         raise ValueError("topk_idx shape %s does not match the layout" % (tuple(topk_idx.shape),))
     if tuple(x.shape) != (T, H) or recv_x.shape[0] != layout.num_recv_rows or recv_x.shape[-1] != H:
         raise ValueError("dispatch buffers do not match the layout")
-    want = torch.uint8 if recv_dtype == EP_FP8_E4M3 else torch.bfloat16
+    want = torch.bfloat16 if recv_dtype == EP_BF16 else torch.uint8
     _check("ep_layout_dispatch", lib().ep_layout_dispatch(
         _ptr(topk_idx, "topk_idx", torch.int64) if topk_idx.numel() else None,
         ctypes.byref(layout.struct), layout.workspace.data_ptr(), layout.workspace.numel(),
@@ -220,6 +222,22 @@ def ep_combine(expert_out: torch.Tensor, topk_weights: torch.Tensor, layout: EpL
     _check("ep_combine", lib().ep_combine(
         _ptr(expert_out, "expert_out", torch.bfloat16), _ptr(topk_weights, "topk_weights", torch.float32),
         ctypes.byref(layout.struct), H, _ptr(out, "out", torch.bfloat16), _stream(stream)))
+
+
+def ep_combine_fp8(expert_q: torch.Tensor, expert_scales: torch.Tensor, topk_weights: torch.Tensor,
+                   layout: EpLayout, out: torch.Tensor, stream=None) -> None:
+    """expert_q uint8 [R, H] E4M3 codes, expert_scales fp32 [R, H/128],
+    topk_weights fp32 [T, k] -> out bf16 [T, H]."""
+    H = expert_q.shape[-1]
+    if (expert_q.shape[0] != layout.num_recv_rows
+            or tuple(expert_scales.shape) != (layout.num_recv_rows, H // 128)
+            or tuple(topk_weights.shape) != (layout.num_tokens, layout.num_topk)
+            or tuple(out.shape) != (layout.num_tokens, H)):
+        raise ValueError("combine buffers do not match the layout")
+    _check("ep_combine_fp8", lib().ep_combine_fp8(
+        _ptr(expert_q, "expert_q", torch.uint8), _ptr(expert_scales, "expert_scales", torch.float32),
+        _ptr(topk_weights, "topk_weights", torch.float32), ctypes.byref(layout.struct), H,
+        _ptr(out, "out", torch.bfloat16), _stream(stream)))
 
 
 def ep_dequant_fp8(q: torch.Tensor, scales: torch.Tensor, y: torch.Tensor, stream=None) -> None:

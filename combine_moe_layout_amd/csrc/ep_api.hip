@@ -55,8 +55,9 @@ int check_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* w
 // Checks shared by ep_dispatch and ep_layout_dispatch (after the layout's).
 int check_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,
                    void* recv_x, float* recv_scales) {
-  if (recv_dtype != EP_BF16 && recv_dtype != EP_FP8_E4M3) return EP_ERR_DTYPE;
-  const bool fp8 = recv_dtype == EP_FP8_E4M3;
+  if (recv_dtype != EP_BF16 && recv_dtype != EP_FP8_E4M3 && recv_dtype != EP_FP8_E4M3_POW2)
+    return EP_ERR_DTYPE;
+  const bool fp8 = recv_dtype != EP_BF16;
   if (hidden < 8 || hidden > EP_MAX_HIDDEN || hidden % 8 != 0 || (fp8 && hidden % 128 != 0))
     return EP_ERR_SHAPE;
   if (layout->num_tokens == 0) return EP_OK;
@@ -112,8 +113,8 @@ int ep_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_
   if (rc != EP_OK) return rc;
   rc = check_dispatch(x, layout, hidden, recv_dtype, recv_x, recv_scales);
   if (rc != EP_OK || layout->num_tokens == 0) return rc;
-  return launch_status(ep::launch_dispatch(x, *layout, hidden, recv_dtype == EP_FP8_E4M3, recv_x,
-                                           recv_scales, static_cast<hipStream_t>(stream)));
+  return launch_status(ep::launch_dispatch(x, *layout, hidden, recv_dtype, recv_x, recv_scales,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
@@ -124,13 +125,12 @@ int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void*
   rc = check_dispatch(x, layout, hidden, recv_dtype, recv_x, recv_scales);
   if (rc != EP_OK) return rc;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool fp8 = recv_dtype == EP_FP8_E4M3;
   if (ep::fused_layout_dispatch_fits(*layout))
-    return launch_status(
-        ep::launch_layout_dispatch_small(topk_idx, *layout, x, hidden, fp8, recv_x, recv_scales, s));
+    return launch_status(ep::launch_layout_dispatch_small(topk_idx, *layout, x, hidden, recv_dtype,
+                                                          recv_x, recv_scales, s));
   rc = launch_status(ep::launch_layout(topk_idx, *layout, workspace, s));
   if (rc != EP_OK || layout->num_tokens == 0) return rc;
-  return launch_status(ep::launch_dispatch(x, *layout, hidden, fp8, recv_x, recv_scales, s));
+  return launch_status(ep::launch_dispatch(x, *layout, hidden, recv_dtype, recv_x, recv_scales, s));
 }
 
 int ep_combine(const void* expert_out, const float* topk_weights, const ep_layout_t* layout,
@@ -145,6 +145,23 @@ int ep_combine(const void* expert_out, const float* topk_weights, const ep_layou
     return EP_ERR_ALIGN;
   return launch_status(ep::launch_combine(expert_out, topk_weights, *layout, hidden, out,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine_fp8(const uint8_t* expert_q, const float* expert_scales,
+                   const float* topk_weights, const ep_layout_t* layout, int32_t hidden, void* out,
+                   void* stream) {
+  int rc = check_layout(layout);
+  if (rc != EP_OK) return rc;
+  if (hidden < 128 || hidden > EP_MAX_HIDDEN || hidden % 128 != 0) return EP_ERR_SHAPE;
+  if (layout->num_tokens == 0) return EP_OK;
+  if (expert_q == nullptr || expert_scales == nullptr || topk_weights == nullptr || out == nullptr)
+    return EP_ERR_NULL;
+  if (!aligned16(expert_q) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(expert_scales) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(topk_weights) & 3u) != 0)
+    return EP_ERR_ALIGN;
+  return launch_status(ep::launch_combine_fp8(expert_q, expert_scales, topk_weights, *layout,
+                                              hidden, out, static_cast<hipStream_t>(stream)));
 }
 
 int ep_dequant_fp8(const uint8_t* q, const float* scales, int64_t rows, int32_t hidden, void* y,

@@ -138,4 +138,119 @@ hipError_t launch_combine(const void* y, const float* w, const ep_layout_t& L, i
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Combine of FP8 expert outputs: every lane owns 8 channels of the token, reads
+// their 8 code bytes from each row (one non-temporal 8-byte load; a wave
+// covers 512 contiguous bytes of the row) and the row's scale for its
+// 128-channel block, decodes with the gfx950 conversion instruction (exact),
+// and accumulates w * scale * value in fp32; the 8 bf16 results leave as one
+// 16-byte non-temporal store (a wave writes 1 KiB of the output row).  Eight
+// channels per lane measured about 9% faster than sixteen, whose two 16-byte
+// output stores per lane each cover only half of every cache line.
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void accumulate8_fp8(float* acc, const u32x2_vec& c, float ws,
+                                                bool valid) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false);
+  const f32x2 e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+  const float f[8] = {a.x, a.y, b.x, b.y, d.x, d.y, e.x, e.y};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = valid ? fmaf(ws, f[i], acc[i]) : acc[i];
+}
+
+// One 8-channel slice v of token t: all K code and scale loads first, then the sum.
+template <int K>
+__device__ __forceinline__ void combine_fp8_slice(const uint8_t* __restrict__ q,
+                                                  const float* __restrict__ scales,
+                                                  const int32_t* s, const float* wt, int32_t k,
+                                                  int32_t hidden, int32_t blocks, int32_t v,
+                                                  u32x4* __restrict__ dst) {
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if constexpr (K > 0) {
+    u32x2_vec c[K];
+    float sc[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t row = s[j] >= 0 ? s[j] : 0;
+      c[j] = load_nt8(q + row * hidden + 8 * v);
+      sc[j] = scales[row * blocks + v / 16];
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) accumulate8_fp8(acc, c[j], wt[j] * sc[j], s[j] >= 0);
+  } else {
+    for (int32_t j = 0; j < k; ++j) {
+      const int32_t sj = s[j];
+      if (sj < 0) continue;
+      accumulate8_fp8(acc, load_nt8(q + (int64_t)sj * hidden + 8 * v),
+                      wt[j] * scales[(int64_t)sj * blocks + v / 16], true);
+    }
+  }
+  store_nt(dst + v, pack8(acc));
+}
+
+template <int K>
+__global__ __launch_bounds__(1024) void combine_fp8_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ scales, const float* __restrict__ w,
+    const int32_t* __restrict__ slot_idx, int64_t num_tokens, int32_t k, int32_t hidden,
+    CombineMap m, u32x4* __restrict__ out) {
+  int64_t t;
+  int32_t lt;
+  if (m.tokens_per_block == 1) {
+    t = blockIdx.x;
+    lt = threadIdx.x;
+  } else {
+    t = (int64_t)blockIdx.x * m.tokens_per_block + threadIdx.x / m.lanes_per_token;
+    lt = threadIdx.x % m.lanes_per_token;
+  }
+  if (t >= num_tokens) return;
+  const int32_t vecs = hidden / 8;  // 8-channel slices per row
+  const int32_t blocks = hidden / kFp8Block;
+  const int32_t kk = K > 0 ? K : k;
+  const float* wt = w + t * kk;
+  u32x4* dst = out + t * vecs;
+  int32_t s[K > 0 ? K : 1];
+  if constexpr (K > 0) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) s[j] = slot_idx[t * K + j];
+  }
+  const int32_t* sp = K > 0 ? s : slot_idx + t * kk;
+  if (vecs <= m.lanes_per_token) {
+    // one pass covers the row: straight-line code, every load issued up front
+    if (lt < vecs) combine_fp8_slice<K>(q, scales, sp, wt, k, hidden, blocks, lt, dst);
+  } else {
+    for (int32_t v = lt; v < vecs; v += m.lanes_per_token)
+      combine_fp8_slice<K>(q, scales, sp, wt, k, hidden, blocks, v, dst);
+  }
+}
+
+template <int K>
+static void launch_fp8_k(dim3 grid, dim3 block, hipStream_t stream, const uint8_t* q,
+                         const float* scales, const float* w, const ep_layout_t& L,
+                         int32_t hidden, CombineMap m, void* out) {
+  hipLaunchKernelGGL(combine_fp8_kernel<K>, grid, block, 0, stream, q, scales, w, L.slot_idx,
+                     L.num_tokens, L.num_topk, hidden, m, static_cast<u32x4*>(out));
+}
+
+hipError_t launch_combine_fp8(const uint8_t* q, const float* scales, const float* w,
+                              const ep_layout_t& L, int32_t hidden, void* out,
+                              hipStream_t stream) {
+  const int64_t T = L.num_tokens;
+  if (T == 0) return hipSuccess;
+  const CombineMap m = combine_map(hidden / 8);
+  const dim3 grid((unsigned)((T + m.tokens_per_block - 1) / m.tokens_per_block));
+  const dim3 block(m.lanes_per_token * m.tokens_per_block);
+  switch (L.num_topk) {
+    case 1: launch_fp8_k<1>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
+    case 2: launch_fp8_k<2>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
+    case 4: launch_fp8_k<4>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
+    case 6: launch_fp8_k<6>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
+    case 8: launch_fp8_k<8>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
+    default: launch_fp8_k<0>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace ep

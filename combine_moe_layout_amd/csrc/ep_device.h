@@ -17,13 +17,17 @@ struct alignas(16) u32x4 {
 };
 typedef uint32_t u32x4_vec __attribute__((ext_vector_type(4)));
 
-// 16-byte loads and stores with the non-temporal hint, for streams touched
-// once.  Each wave instruction using them must cover whole cache lines (64
+// 16-byte (and 8-byte) loads and stores with the non-temporal hint, for
+// streams touched once.  Each wave instruction using them must cover whole cache lines (64
 // lanes x 16 contiguous bytes): a non-temporal access does not keep the line,
 // so a second instruction reading the other half of a line fetches it again.
 __device__ __forceinline__ u32x4 load_nt(const u32x4* p) {
   const u32x4_vec v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_vec*>(p));
   return u32x4{v.x, v.y, v.z, v.w};
+}
+typedef uint32_t u32x2_vec __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2_vec load_nt8(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_vec*>(p));
 }
 __device__ __forceinline__ void store_nt(u32x4* p, const u32x4& a) {
   const u32x4_vec v = {a.x, a.y, a.z, a.w};

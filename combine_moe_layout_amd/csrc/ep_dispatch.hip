@@ -57,7 +57,7 @@ __global__ __launch_bounds__(1024) void dispatch_bf16_kernel(
 // staged in LDS and written afterwards row by row by consecutive lanes, so each
 // receive row's scales leave as one contiguous run instead of 4-byte pieces
 // from separate waves.
-template <bool kHw>
+template <bool kHw, bool kPow2>
 __global__ __launch_bounds__(1024) void dispatch_fp8_kernel(
     const u32x4* __restrict__ x, int64_t num_tokens, int32_t k, int32_t hidden, TokenMap m,
     const int32_t* __restrict__ slot_idx, u32x4* __restrict__ recv, float* __restrict__ scales) {
@@ -68,8 +68,8 @@ __global__ __launch_bounds__(1024) void dispatch_fp8_kernel(
   const int32_t tok_in_block = m.tokens_per_block == 1 ? 0 : threadIdx.x / m.lanes_per_token;
   float* my_scales = s_scale + tok_in_block * (hidden / kFp8Block);
   if (t < num_tokens)  // whole 8-lane groups share t
-    fp8_token_codes<kHw>(x + t * (hidden / 8), hidden, lt, m.lanes_per_token, slot_idx + t * k,
-                         k, recv, my_scales);
+    fp8_token_codes<kHw, kPow2>(x + t * (hidden / 8), hidden, lt, m.lanes_per_token,
+                                slot_idx + t * k, k, recv, my_scales);
   __syncthreads();
   if (t < num_tokens)
     fp8_token_scales(hidden, lt, m.lanes_per_token, slot_idx + t * k, k, my_scales, scales);
@@ -93,27 +93,25 @@ static TokenMap token_map(int32_t vecs_per_row) {
   return m;
 }
 
-hipError_t launch_dispatch(const void* x, const ep_layout_t& L, int32_t hidden, bool fp8,
+hipError_t launch_dispatch(const void* x, const ep_layout_t& L, int32_t hidden, int32_t dtype,
                            void* recv_x, float* recv_scales, hipStream_t stream) {
   const int64_t T = L.num_tokens;
   if (T == 0) return hipSuccess;
+  const bool fp8 = dtype != EP_BF16;
   const TokenMap m = token_map(fp8 ? hidden / 16 : hidden / 8);
-  const int64_t blocks = (T + m.tokens_per_block - 1) / m.tokens_per_block;
-  const int32_t threads = m.lanes_per_token * m.tokens_per_block;
-  if (fp8) {
-    if (kDispatchUsesHwCast)
-      hipLaunchKernelGGL(dispatch_fp8_kernel<true>, dim3((unsigned)blocks), dim3(threads), 0,
-                         stream, static_cast<const u32x4*>(x), T, L.num_topk, hidden, m,
-                         L.slot_idx, static_cast<u32x4*>(recv_x), recv_scales);
-    else
-      hipLaunchKernelGGL(dispatch_fp8_kernel<false>, dim3((unsigned)blocks), dim3(threads), 0,
-                         stream, static_cast<const u32x4*>(x), T, L.num_topk, hidden, m,
-                         L.slot_idx, static_cast<u32x4*>(recv_x), recv_scales);
-  } else {
-    hipLaunchKernelGGL(dispatch_bf16_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                       static_cast<const u32x4*>(x), T, L.num_topk, hidden, m, L.slot_idx,
-                       static_cast<u32x4*>(recv_x));
-  }
+  const dim3 grid((unsigned)((T + m.tokens_per_block - 1) / m.tokens_per_block));
+  const dim3 block(m.lanes_per_token * m.tokens_per_block);
+  const u32x4* xv = static_cast<const u32x4*>(x);
+  u32x4* rv = static_cast<u32x4*>(recv_x);
+  if (dtype == EP_FP8_E4M3)
+    hipLaunchKernelGGL((dispatch_fp8_kernel<kDispatchUsesHwCast, false>), grid, block, 0, stream,
+                       xv, T, L.num_topk, hidden, m, L.slot_idx, rv, recv_scales);
+  else if (dtype == EP_FP8_E4M3_POW2)
+    hipLaunchKernelGGL((dispatch_fp8_kernel<kDispatchUsesHwCast, true>), grid, block, 0, stream,
+                       xv, T, L.num_topk, hidden, m, L.slot_idx, rv, recv_scales);
+  else
+    hipLaunchKernelGGL(dispatch_bf16_kernel, grid, block, 0, stream, xv, T, L.num_topk, hidden, m,
+                       L.slot_idx, rv);
   return hipGetLastError();
 }
 

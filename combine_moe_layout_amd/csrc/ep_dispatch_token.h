@@ -33,7 +33,26 @@ __device__ __forceinline__ void bf16_token_copy(const u32x4* __restrict__ src, i
 // 2v and 2v+1 given in lo / hi), stored to every valid row; the 8 lanes of a
 // 128-channel block must call it together (their maximum is reduced with lane
 // swizzles).  The block scale goes to my_scales[v / 8].
-template <bool kHw>
+// The block scale and its reciprocal.  kPow2 = false: scale = a / 448 and
+// inv = 448 / a, single correctly rounded fp32 divisions.  kPow2 = true: the
+// smallest power of two s with 448 * s >= a: with a = (1 + m) * 2^ea and
+// 448 = 1.75 * 2^8, s = 2^(ea - 8) when 1 + m <= 1.75 (mantissa bits <=
+// 0x600000), else 2^(ea - 7); inv = 1 / s exactly.  a >= 1e-4 is normal, so
+// both powers of two are normal fp32 values.
+template <bool kPow2>
+__device__ __forceinline__ void fp8_block_scale(float a, float& scale, float& inv) {
+  if constexpr (kPow2) {
+    const uint32_t bits = __float_as_uint(a);
+    const int32_t e = (int32_t)(bits >> 23) - 127 - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    scale = __uint_as_float((uint32_t)(127 + e) << 23);
+    inv = __uint_as_float((uint32_t)(127 - e) << 23);
+  } else {
+    scale = a / kFp8Max;  // correctly rounded fp32 divisions
+    inv = kFp8Max / a;
+  }
+}
+
+template <bool kHw, bool kPow2 = false>
 __device__ __forceinline__ void fp8_vector_codes(const u32x4& lo, const u32x4& hi, int32_t v,
                                                  const int32_t* slots, int32_t k,
                                                  u32x4* __restrict__ recv,
@@ -48,9 +67,8 @@ __device__ __forceinline__ void fp8_vector_codes(const u32x4& lo, const u32x4& h
   amax = fmaxf(amax, __shfl_xor(amax, 1));
   amax = fmaxf(amax, __shfl_xor(amax, 2));
   amax = fmaxf(amax, __shfl_xor(amax, 4));
-  const float a = fmaxf(amax, kScaleFloor);
-  const float scale = a / kFp8Max;  // correctly rounded fp32 divisions
-  const float inv = kFp8Max / a;
+  float scale, inv;
+  fp8_block_scale<kPow2>(fmaxf(amax, kScaleFloor), scale, inv);
   u32x4 q;
   q.x = e4m3_encode4<kHw>(clamp_fp8(f[0] * inv), clamp_fp8(f[1] * inv), clamp_fp8(f[2] * inv),
                           clamp_fp8(f[3] * inv));
@@ -71,15 +89,15 @@ __device__ __forceinline__ void fp8_vector_codes(const u32x4& lo, const u32x4& h
 // store of codes per valid row); 8 lanes make one 128-channel block.  `lanes`
 // must be a multiple of 8 so that the 8 lanes of a block step together.  The
 // block scales are left in my_scales for fp8_token_scales.
-template <bool kHw>
+template <bool kHw, bool kPow2 = false>
 __device__ __forceinline__ void fp8_token_codes(const u32x4* __restrict__ src, int32_t hidden,
                                                 int32_t lt, int32_t lanes, const int32_t* slots,
                                                 int32_t k, u32x4* __restrict__ recv,
                                                 float* my_scales) {
   const int32_t out_vec_per_row = hidden / 16;  // 16-byte vectors of codes
   for (int32_t v = lt; v < out_vec_per_row; v += lanes)
-    fp8_vector_codes<kHw>(src[2 * v], src[2 * v + 1], v, slots, k, recv, out_vec_per_row,
-                          my_scales);
+    fp8_vector_codes<kHw, kPow2>(src[2 * v], src[2 * v + 1], v, slots, k, recv, out_vec_per_row,
+                                 my_scales);
 }
 
 // After a block barrier: the token's lanes write its staged scales to each

@@ -80,7 +80,7 @@ __device__ int32_t block_exclusive_scan(const int32_t* in, int32_t* out, int n, 
   return total;
 }
 
-template <bool kFp8, bool kHw>
+template <bool kFp8, bool kHw, bool kPow2>
 __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a) {
   __shared__ int32_t s_idx[kFusedMaxPairs];  // expert of every pair, -1 if none
   __shared__ int32_t s_sum[2 * kFusedMaxTopk];
@@ -191,13 +191,13 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
   if (one_pass) {
     if (tid < vecs) {
       if constexpr (kFp8)
-        fp8_vector_codes<kHw>(pre_lo, pre_hi, tid, s_slot, k, a.recv, vecs, s_scale);
+        fp8_vector_codes<kHw, kPow2>(pre_lo, pre_hi, tid, s_slot, k, a.recv, vecs, s_scale);
       else
         for (int32_t j = 0; j < k; ++j)
           if (s_slot[j] >= 0) store_nt(a.recv + (int64_t)s_slot[j] * vecs + tid, pre_lo);
     }
   } else if constexpr (kFp8) {
-    fp8_token_codes<kHw>(src, a.hidden, tid, blockDim.x, s_slot, k, a.recv, s_scale);
+    fp8_token_codes<kHw, kPow2>(src, a.hidden, tid, blockDim.x, s_slot, k, a.recv, s_scale);
   } else {
     bf16_token_copy(src, a.hidden, tid, blockDim.x, s_slot, k, a.recv);
   }
@@ -213,8 +213,9 @@ bool fused_layout_dispatch_fits(const ep_layout_t& L) {
 }
 
 hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout_t& L,
-                                        const void* x, int32_t hidden, bool fp8, void* recv_x,
-                                        float* recv_scales, hipStream_t stream) {
+                                        const void* x, int32_t hidden, int32_t dtype,
+                                        void* recv_x, float* recv_scales, hipStream_t stream) {
+  const bool fp8 = dtype != EP_BF16;
   FusedArgs a;
   a.topk_idx = topk_idx;
   a.num_tokens = L.num_tokens;
@@ -238,11 +239,14 @@ hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout
   int32_t lanes = ((vecs + 63) / 64) * 64;
   lanes = lanes < 256 ? 256 : (lanes > 1024 ? 1024 : lanes);
   const dim3 grid((unsigned)(L.num_tokens + 1));
-  if (fp8)
-    hipLaunchKernelGGL((layout_dispatch_small_kernel<true, kDispatchUsesHwCast>), grid,
+  if (dtype == EP_FP8_E4M3)
+    hipLaunchKernelGGL((layout_dispatch_small_kernel<true, kDispatchUsesHwCast, false>), grid,
+                       dim3(lanes), 0, stream, a);
+  else if (dtype == EP_FP8_E4M3_POW2)
+    hipLaunchKernelGGL((layout_dispatch_small_kernel<true, kDispatchUsesHwCast, true>), grid,
                        dim3(lanes), 0, stream, a);
   else
-    hipLaunchKernelGGL((layout_dispatch_small_kernel<false, kDispatchUsesHwCast>), grid,
+    hipLaunchKernelGGL((layout_dispatch_small_kernel<false, kDispatchUsesHwCast, false>), grid,
                        dim3(lanes), 0, stream, a);
   return hipGetLastError();
 }

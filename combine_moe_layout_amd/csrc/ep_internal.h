@@ -27,7 +27,7 @@ size_t layout_workspace_bytes(int64_t pairs, int32_t num_experts);
 hipError_t launch_layout(const int64_t* topk_idx, const ep_layout_t& L, void* workspace,
                          hipStream_t stream);
 
-hipError_t launch_dispatch(const void* x, const ep_layout_t& L, int32_t hidden, bool fp8,
+hipError_t launch_dispatch(const void* x, const ep_layout_t& L, int32_t hidden, int32_t dtype,
                            void* recv_x, float* recv_scales, hipStream_t stream);
 
 hipError_t launch_combine(const void* y, const float* w, const ep_layout_t& L, int32_t hidden,
@@ -54,7 +54,10 @@ constexpr int kFusedMaxTopk = 8;
 bool fused_layout_dispatch_fits(const ep_layout_t& L);
 
 hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout_t& L,
-                                        const void* x, int32_t hidden, bool fp8, void* recv_x,
-                                        float* recv_scales, hipStream_t stream);
+                                        const void* x, int32_t hidden, int32_t dtype,
+                                        void* recv_x, float* recv_scales, hipStream_t stream);
+
+hipError_t launch_combine_fp8(const uint8_t* q, const float* scales, const float* w,
+                              const ep_layout_t& L, int32_t hidden, void* out, hipStream_t stream);
 
 }  // namespace ep

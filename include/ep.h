@@ -63,8 +63,9 @@ enum ep_status {
 
 /* Receive-buffer element types for ep_dispatch. */
 enum ep_dtype {
-    EP_BF16 = 0,    /* bf16 rows, a bit copy of x */
-    EP_FP8_E4M3 = 1 /* OCP FP8 E4M3 codes + one fp32 scale per 128 channels */
+    EP_BF16 = 0,         /* bf16 rows, a bit copy of x */
+    EP_FP8_E4M3 = 1,     /* OCP FP8 E4M3 codes + one fp32 scale per 128 channels */
+    EP_FP8_E4M3_POW2 = 2 /* as EP_FP8_E4M3, with each scale a power of two (see ep_dispatch) */
 };
 
 /* Bits of layout->error_flags, written by ep_get_layout. */
@@ -150,6 +151,9 @@ int ep_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* work
  *                128 channels a = max(max|x|, 1e-4), scale = a/448,
  *                code = nearest E4M3 (ties to even, sign kept) of
  *                clamp(x * (448/a), -448, 448); requires hidden % 128 == 0.
+ *   EP_FP8_E4M3_POW2: the same layout, but each block's scale is the smallest
+ *                power of two s with 448 * s >= a, and each code the nearest
+ *                E4M3 of clamp(x / s, -448, 448) (an exact rescale).
  * Rows that no slot names are left untouched.  hidden % 8 == 0.
  * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN, EP_ERR_DTYPE or EP_ERR_LAUNCH.
  */
@@ -180,6 +184,19 @@ int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void*
  */
 int ep_combine(const void* expert_out, const float* topk_weights, const ep_layout_t* layout,
                int32_t hidden, void* out, void* stream);
+
+/*
+ * Combine of FP8 expert outputs ([yololab] stage table, combine row;
+ * "FP8與低精度通訊": low precision cuts combine volume too).  expert_q: device
+ * uint8 [R, hidden] E4M3 codes; expert_scales: device fp32 [R, hidden/128], one
+ * scale per row and 128-channel block.  out[t] = bf16(sum over valid j of
+ * topk_weights[t,j] * decode(code) * scale), accumulated in fp32, rounded to
+ * nearest-even; +0 for a token with no valid pair.  hidden % 128 == 0.
+ * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN or EP_ERR_LAUNCH.
+ */
+int ep_combine_fp8(const uint8_t* expert_q, const float* expert_scales,
+                   const float* topk_weights, const ep_layout_t* layout, int32_t hidden, void* out,
+                   void* stream);
 
 /*
  * Identity-expert stand-in for FP8 receive buffers (not part of the path;

@@ -1,0 +1,173 @@
+"""GPU parity for the dispatch / combine variants: power-of-two FP8 scales
+(EP_FP8_E4M3_POW2) and the combine of FP8 expert outputs (ep_combine_fp8).
+
+Same bar as the main parity tests: codes and scales bit-exact; combine within
+|gpu - ref| <= 8e-3 * max(|ref|, 1e-3) element-wise against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_moe_layout_amd import binding as B
+from combine_moe_layout_amd import workloads as W
+from test_gpu_parity import (assert_close_bf16, dev_bf16, gpu_layout, host_bits, layout_to_host,
+                             note, sample_tokens)
+
+pytestmark = pytest.mark.gpu
+
+
+def _boundary_rows(H):
+    """Rows whose block maxima sit on and just past the power-of-two
+    boundaries 448 * 2^e, and below the 1e-4 floor."""
+    vals = [3.5, 3.515625, 448.0, 450.0, 2.0 ** -16, 0.0, 7.0, 7.03125, 0.875, 0.87890625]
+    rows = []
+    g = np.random.default_rng(17)
+    for v in vals:
+        r = (g.standard_normal(H) * v / 8).astype(np.float32)
+        r[:: 128] = v                      # every block's maximum is exactly v
+        r = np.clip(r, -v, v)
+        rows.append(r)
+    return W.float32_to_bf16_bits(np.stack(rows))
+
+
+@pytest.mark.parametrize("name,T,H", [("dsv3", 256, None), ("lowlat", None, None),
+                                       ("large", 512, None), ("dsv3", 37, 128),
+                                       ("dsv3", 9, 16512)])
+def test_dispatch_pow2_scales(name, T, H):
+    wl = W.make(name, T=T, H=H)
+    note("pow2 dispatch %s T=%d H=%d cap=%d" % (name, wl.T, wl.H, wl.cap))
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap)
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, wl.cap, with_src=False)
+    R = wl.R
+    q = torch.zeros((R, wl.H), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((R, wl.H // 128), dtype=torch.float32, device="cuda")
+    B.ep_dispatch(dev_bf16(wl.x_bits), lay, B.EP_FP8_E4M3_POW2, q, s)
+    oq, os_ = oracle.dispatch_fp8_pow2(wl.x_bits, ol["slot_idx"], R)
+    used = np.zeros(R, bool)
+    used[ol["slot_idx"][ol["slot_idx"] >= 0]] = True
+    qh, sh = q.cpu().numpy(), s.cpu().numpy()
+    assert (qh[used] == oq[used]).all()
+    assert (sh[used].view(np.uint32) == os_[used].view(np.uint32)).all()
+
+
+def test_dispatch_pow2_boundaries():
+    H = 1024
+    x = _boundary_rows(H)
+    T = x.shape[0]
+    idx = np.arange(T, dtype=np.int64).reshape(T, 1)     # token t -> expert t
+    note("pow2 dispatch at scale boundaries")
+    lay = gpu_layout(idx, T, 1, 0, with_src=False)
+    q = torch.zeros((T, H), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((T, H // 128), dtype=torch.float32, device="cuda")
+    B.ep_dispatch(dev_bf16(x), lay, B.EP_FP8_E4M3_POW2, q, s)
+    for t in range(T):
+        oq, os_ = oracle.quantize_token_fp8_pow2(x[t])
+        assert (q[t].cpu().numpy() == oq).all(), t
+        assert (s[t].cpu().numpy().view(np.uint32) == os_.view(np.uint32)).all(), t
+
+
+def test_fused_path_pow2():
+    wl = W.make("lowlat")
+    note("fused layout+dispatch with pow2 scales (lowlat)")
+    lay = B.EpLayout(wl.T, wl.k, wl.E, wl.G, wl.cap)
+    q = torch.zeros((wl.R, wl.H), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((wl.R, wl.H // 128), dtype=torch.float32, device="cuda")
+    B.ep_layout_dispatch(torch.from_numpy(wl.topk_idx).cuda(), lay, dev_bf16(wl.x_bits),
+                         B.EP_FP8_E4M3_POW2, q, s)
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap)
+    assert (layout_to_host(lay)["slot_idx"] == ol["slot_idx"]).all()
+    oq, os_ = oracle.dispatch_fp8_pow2(wl.x_bits, ol["slot_idx"], wl.R)
+    used = np.zeros(wl.R, bool)
+    used[ol["slot_idx"][ol["slot_idx"] >= 0]] = True
+    assert (q.cpu().numpy()[used] == oq[used]).all()
+    assert (s.cpu().numpy()[used].view(np.uint32) == os_[used].view(np.uint32)).all()
+
+
+def _random_fp8_rows(R, H, seed):
+    g = np.random.default_rng(seed)
+    q = g.integers(0, 256, (R, H)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x38           # no NaN codes (outside the contract)
+    sc = np.exp2(g.integers(-12, 4, (R, H // 128))).astype(np.float32) * \
+        (1 + g.random((R, H // 128))).astype(np.float32)
+    return q, sc
+
+
+def _combine_fp8_gpu(q, sc, w, lay, H):
+    out = torch.empty((lay.num_tokens, H), dtype=torch.bfloat16, device="cuda")
+    B.ep_combine_fp8(torch.from_numpy(q).cuda(), torch.from_numpy(sc).cuda(),
+                     torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda(), lay, out)
+    torch.cuda.synchronize()
+    return host_bits(out)
+
+
+@pytest.mark.parametrize("name,T,H", [("tiny", None, None), ("dsv3", 200, None),
+                                       ("lowlat", None, None), ("large", 400, None),
+                                       ("dsv3", 64, 128), ("dsv3", 21, 16512)])
+def test_combine_fp8_random_outputs(name, T, H):
+    wl = W.make(name, T=T, H=H)
+    if wl.H % 128:
+        pytest.skip("FP8 rows need hidden % 128 == 0")
+    note("combine_fp8 %s T=%d H=%d k=%d" % (name, wl.T, wl.H, wl.k))
+    q, sc = _random_fp8_rows(wl.R, wl.H, seed=3)
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap)
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, wl.cap, with_src=False)
+    got = _combine_fp8_gpu(q, sc, wl.topk_weights, lay, wl.H)
+    assert_close_bf16(got, oracle.combine_fp8(q, sc, wl.topk_weights, ol["slot_idx"]),
+                      "combine_fp8 %s" % name)
+
+
+@pytest.mark.parametrize("k", [3, 9])
+def test_combine_fp8_other_topk(k):
+    wl = W.custom(T=120, H=512, E=32, k=k, G=4, seed=k)
+    note("combine_fp8 k=%d" % k)
+    q, sc = _random_fp8_rows(wl.R, wl.H, seed=k)
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, 0, with_src=False)
+    assert_close_bf16(_combine_fp8_gpu(q, sc, wl.topk_weights, lay, wl.H),
+                      oracle.combine_fp8(q, sc, wl.topk_weights, ol["slot_idx"]), "combine_fp8 k=%d" % k)
+
+
+def test_combine_fp8_decodes_every_code_exactly():
+    """One-hot weights and power-of-two scales: each output is a decoded code
+    times its scale, exactly representable in bf16 -- every non-NaN code."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    H = 256
+    R = 8
+    q = np.resize(codes, (R, H)).astype(np.uint8)
+    sc = np.exp2(np.arange(R * 2, dtype=np.float64) - 8).astype(np.float32).reshape(R, 2)
+    T, k = R, 2
+    w = np.zeros((T, k), np.float32)
+    w[:, 0] = 1.0
+    note("combine_fp8 decode of all codes")
+    # layout with one expert per row so that slot t*2+0 = row t: route pair (t,0) to expert t
+    idx = np.stack([np.arange(T), np.full(T, -1)], 1).astype(np.int64)
+    lay = gpu_layout(idx, R, 1, 1, with_src=False)   # padded, capacity 1: expert t owns row t
+    got = _combine_fp8_gpu(q, sc, w, lay, H)
+    ol = oracle.layout(idx, R, 1, 1)
+    ref = oracle.combine_fp8(q, sc, w, ol["slot_idx"])
+    assert (got == ref).all()
+
+
+def test_whole_path_fp8_combine_full_size():
+    """dsv3 at full size, FP8 dispatch, identity experts kept in FP8 (the
+    receive codes and scales are the expert outputs), FP8 combine; sampled
+    tokens through the oracle's own chain."""
+    wl = W.make("dsv3")
+    note("whole path with FP8 combine, dsv3 full size")
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, 0, with_src=False)
+    q = torch.empty((wl.R, wl.H), dtype=torch.uint8, device="cuda")
+    s = torch.empty((wl.R, wl.H // 128), dtype=torch.float32, device="cuda")
+    B.ep_dispatch(dev_bf16(wl.x_bits), lay, B.EP_FP8_E4M3, q, s)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    B.ep_combine_fp8(q, s, torch.from_numpy(wl.topk_weights).cuda(), lay, out)
+    got = host_bits(out)
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
+    toks = sample_tokens(wl.T, 48)
+    ref = np.empty((toks.size, wl.H), np.uint16)
+    for i, t in enumerate(toks):
+        qt, st = oracle.quantize_token_fp8(wl.x_bits[t])
+        local = np.where(ol["slot_idx"][t] >= 0, 0, -1).astype(np.int32).reshape(1, -1)
+        ref[i] = oracle.combine_fp8(qt.reshape(1, -1), st.reshape(1, -1),
+                                    wl.topk_weights[t:t + 1], local)[0]
+    assert_close_bf16(got[toks], ref, "whole path FP8 combine")
