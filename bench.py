@@ -31,7 +31,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["ep_combine.hip", "ep_dispatch.hip", "ep_layout.hip", "ep_device.h"]
+KERNEL_SOURCES = ["ep_combine.hip", "ep_dispatch.hip", "ep_dispatch_token.h", "ep_layout.hip",
+                  "ep_device.h", "ep_internal.h", "ep_aux.hip"]
 
 
 def ideal_bytes(T: int, H: int, E: int, G: int, k: int, R_used: int, fp8: bool,

@@ -53,11 +53,22 @@ __global__ __launch_bounds__(256) void cast_bits_kernel(uint32_t first, int64_t 
   }
 }
 
-__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
-                                                   u32x4* __restrict__ dst, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    dst[i] = src[i];
+// Streaming copy: each workgroup moves 16 KiB, every lane four 16-byte vectors
+// 4 KiB apart (so each wave instruction covers 1 KiB), all four loads issued
+// before the stores, non-temporal both ways like the dispatch and combine rows.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyVecs = 4;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_kernel(const u32x4* __restrict__ src,
+                                                            u32x4* __restrict__ dst, int64_t n) {
+  const int64_t base = (int64_t)blockIdx.x * (kCopyThreads * kCopyVecs) + threadIdx.x;
+  u32x4 v[kCopyVecs];
+#pragma unroll
+  for (int u = 0; u < kCopyVecs; ++u)
+    if (base + u * kCopyThreads < n) v[u] = load_nt(src + base + u * kCopyThreads);
+#pragma unroll
+  for (int u = 0; u < kCopyVecs; ++u)
+    if (base + u * kCopyThreads < n) store_nt(dst + base + u * kCopyThreads, v[u]);
 }
 
 static unsigned grid_for(int64_t work, int per_block) {
@@ -92,7 +103,10 @@ hipError_t launch_cast_e4m3_bits(uint32_t first, int64_t n, int32_t method, uint
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
   const int64_t n = (int64_t)(bytes / 16);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream,
+  const int64_t per_block = kCopyThreads * kCopyVecs;
+  const int64_t blocks = (n + per_block - 1) / per_block;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, stream,
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
   return hipGetLastError();
 }
