@@ -65,6 +65,10 @@ def _load(path: str) -> ctypes.CDLL:
     L.ep_oracle_dispatch_fp8_pow2.argtypes = [vp, i64, i32, i32, vp, vp, vp]
     L.ep_oracle_combine_fp8.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp]
     L.ep_oracle_combine_fp8_tokens.argtypes = [vp, vp, vp, vp, i32, i32, vp, i64, vp]
+    L.ep_oracle_group_layout.restype = ctypes.c_int
+    L.ep_oracle_group_layout.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.ep_oracle_combine_groups.argtypes = [vp, vp, i64, i32, i32, vp]
+    L.ep_oracle_combine_groups_tokens.argtypes = [vp, vp, i32, i32, vp, i64, vp]
     return L
 
 
@@ -299,4 +303,64 @@ def combine_fp8_tokens(q, scales, w, slot_idx, tokens) -> np.ndarray:
     out = np.empty((tokens.size, H), np.uint16)
     lib().ep_oracle_combine_fp8_tokens(_p(q), _p(scales), _p(w), _p(slot_idx), k, H, _p(tokens),
                                        tokens.size, _p(out))
+    return out
+
+
+# ----------------------------------------------------------------------------- dedup variant
+def group_layout(topk_idx: np.ndarray, topk_weights: np.ndarray | None, E: int, G: int):
+    """Per-group dedup layout (readings R15, R16).  Returns a dict:
+    group_idx [T,kg], num_tokens_per_group [G], group_offsets [G+1],
+    group_slot [T,kg], recv_token [T*kg] (-1 in unused rows),
+    recv_topk_idx [T*kg,k] (-1 in unused rows), recv_topk_weights [T*kg,k]
+    (0 in unused rows, or None without weights), error_flags, kg, rows_used."""
+    topk_idx = _c(topk_idx, np.int64)
+    T, k = topk_idx.shape
+    kg = min(k, G)
+    R = T * kg
+    gidx = np.empty((T, kg), np.int32)
+    cnt = np.zeros(G, np.int32)
+    off = np.zeros(G + 1, np.int32)
+    slot = np.empty((T, kg), np.int32)
+    tok = np.full(R, -1, np.int32)
+    ridx = np.full((R, k), -1, np.int64)
+    rw = None
+    if topk_weights is not None:
+        topk_weights = _c(topk_weights, np.float32)
+        rw = np.zeros((R, k), np.float32)
+    flags = np.zeros(1, np.int32)
+    has = T > 0
+    rc = lib().ep_oracle_group_layout(_p(topk_idx) if has else None,
+                                      _p(topk_weights) if rw is not None and has else None,
+                                      T, k, E, G, _p(gidx) if has else None, _p(cnt), _p(off),
+                                      _p(slot) if has else None, _p(tok) if R else None,
+                                      _p(ridx) if R else None, _p(rw) if rw is not None and R else None,
+                                      _p(flags))
+    if rc != 0:
+        raise ValueError("oracle group layout rejected its arguments (status %d)" % rc)
+    return dict(group_idx=gidx, num_tokens_per_group=cnt, group_offsets=off, group_slot=slot,
+                recv_token=tok, recv_topk_idx=ridx, recv_topk_weights=rw,
+                error_flags=int(flags[0]), kg=kg, rows_used=int(off[G]))
+
+
+def combine_groups(z_bits: np.ndarray, group_slot: np.ndarray) -> np.ndarray:
+    """Group combine of the dedup variant (reading R17): unit-weight sum of a
+    token's group rows."""
+    z_bits = _c(z_bits, np.uint16)
+    group_slot = _c(group_slot, np.int32)
+    T, kg = group_slot.shape
+    H = z_bits.shape[1]
+    out = np.empty((T, H), np.uint16)
+    lib().ep_oracle_combine_groups(_p(z_bits), _p(group_slot), T, kg, H, _p(out))
+    return out
+
+
+def combine_groups_tokens(z_bits: np.ndarray, group_slot: np.ndarray, tokens) -> np.ndarray:
+    z_bits = _c(z_bits, np.uint16)
+    group_slot = _c(group_slot, np.int32)
+    tokens = _c(tokens, np.int64).reshape(-1)
+    kg = group_slot.shape[1]
+    H = z_bits.shape[1]
+    out = np.empty((tokens.size, H), np.uint16)
+    lib().ep_oracle_combine_groups_tokens(_p(z_bits), _p(group_slot), kg, H, _p(tokens),
+                                          tokens.size, _p(out))
     return out

@@ -61,6 +61,15 @@
  *       448 * s >= a; codes from the exact rescale x / s.
  *   R14 FP8 combine variant: expert outputs as E4M3 codes + per-block fp32
  *       scales, decoded exactly inside the weighted sum.
+ *   R15 Per-group dedup variant: a token goes once to every group holding at
+ *       least one of its valid experts.  Its groups, in ascending order, are
+ *       its entries (padded with -1 to kg = min(k, G)); receive rows are
+ *       group-major and, inside a group, in ascending token order.
+ *   R16 Receiver metadata of the dedup variant: the row of (t, g) carries
+ *       t's top-k list masked to group g (other entries -1, weight 0).
+ *   R17 Group combine of the dedup variant: the expert side has already
+ *       weighted and summed its experts' outputs into one row per (t, g);
+ *       out[t] = bf16(sum of t's group rows), unit weights, rounded once.
  */
 #include <math.h>
 #include <stdint.h>
@@ -437,4 +446,117 @@ EXPORT void ep_oracle_combine_fp8_tokens(const uint8_t* q, const float* scales, 
                                          const int64_t* tokens, int64_t n, uint16_t* out_rows) {
     for (int64_t i = 0; i < n; ++i)
         combine_fp8_one(q, scales, w, slot_idx, tokens[i], k, H, out_rows + i * H);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Variant: per-group dedup ([yololab] "Load Imbalance" lists the bytes each   */
+/* rank sends and receives; [backyes] 五.2 gives the no-dedup volume; this     */
+/* variant sends a token once per group instead of once per expert)            */
+/* ------------------------------------------------------------------------- */
+
+/* R15, R16.  Outputs (kg = min(k, G), Rg = T * kg rows at most):
+ *   group_idx [T, kg]          t's groups, ascending, then -1
+ *   num_tokens_per_group [G]   tokens that reach group g
+ *   group_offsets [G+1]        exclusive prefix sum of those counts
+ *   group_slot [T, kg]         receive row of entry i of token t, or -1
+ *   recv_token [Rg]            source token of each used row (optional)
+ *   recv_topk_idx [Rg, k]      t's expert ids masked to the row's group (optional)
+ *   recv_topk_weights [Rg, k]  the matching weights, 0 elsewhere (optional)
+ *   error_flags                bit 0: an expert id outside [-1, E)          */
+EXPORT int ep_oracle_group_layout(const int64_t* topk_idx, const float* topk_weights, int64_t T,
+                                  int32_t k, int32_t E, int32_t G, int32_t* group_idx,
+                                  int32_t* num_tokens_per_group, int32_t* group_offsets,
+                                  int32_t* group_slot, int32_t* recv_token,
+                                  int64_t* recv_topk_idx, float* recv_topk_weights,
+                                  int32_t* error_flags) {
+    if (T < 0 || k < 1 || E < 1 || G < 1 || E % G != 0) return ORACLE_ERR_SHAPE;
+    if ((T > 0 && (!topk_idx || !group_idx || !group_slot)) || !num_tokens_per_group ||
+        !group_offsets || !error_flags || (recv_topk_weights && !topk_weights))
+        return ORACLE_ERR_NULL;
+    int32_t kg = k < G ? k : G;
+    int32_t per_group = E / G;
+    int32_t flags = 0;
+
+    /* 1. which groups each token reaches */
+    unsigned char* in_group = (unsigned char*)calloc((size_t)(T > 0 ? T : 1) * (size_t)G, 1);
+    if (!in_group) return ORACLE_ERR_NULL;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            int64_t e = topk_idx[t * k + j];
+            if (e == -1) continue;
+            if (e < 0 || e >= E) { flags |= 1; continue; }
+            in_group[t * G + e / per_group] = 1;
+        }
+    }
+
+    /* 2. each token's groups in ascending order, padded with -1 */
+    for (int64_t t = 0; t < T; ++t) {
+        int32_t i = 0;
+        for (int32_t g = 0; g < G; ++g)
+            if (in_group[t * G + g]) group_idx[t * kg + i++] = g;
+        while (i < kg) group_idx[t * kg + i++] = -1;
+    }
+
+    /* 3. per-group counts and their exclusive prefix sum */
+    for (int32_t g = 0; g < G; ++g) {
+        int32_t c = 0;
+        for (int64_t t = 0; t < T; ++t) c += in_group[t * G + g];
+        num_tokens_per_group[g] = c;
+    }
+    group_offsets[0] = 0;
+    for (int32_t g = 0; g < G; ++g) group_offsets[g + 1] = group_offsets[g] + num_tokens_per_group[g];
+
+    /* 4. rows: walk the tokens in order with one running cursor per group */
+    int32_t* cursor = (int32_t*)calloc((size_t)G, sizeof(int32_t));
+    if (!cursor) { free(in_group); return ORACLE_ERR_NULL; }
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t i = 0; i < kg; ++i) {
+            int32_t g = group_idx[t * kg + i];
+            if (g < 0) { group_slot[t * kg + i] = -1; continue; }
+            int32_t row = group_offsets[g] + cursor[g]++;
+            group_slot[t * kg + i] = row;
+            if (recv_token) recv_token[row] = (int32_t)t;
+
+            /* 5. the row's copy of t's top-k list, masked to group g (R16) */
+            for (int32_t j = 0; j < k; ++j) {
+                int64_t e = topk_idx[t * k + j];
+                int mine = e >= 0 && e < E && e / per_group == g;
+                if (recv_topk_idx) recv_topk_idx[(int64_t)row * k + j] = mine ? e : -1;
+                if (recv_topk_weights)
+                    recv_topk_weights[(int64_t)row * k + j] = mine ? topk_weights[t * k + j] : 0.0f;
+            }
+        }
+    }
+    free(cursor);
+    free(in_group);
+    *error_flags = flags;
+    return ORACLE_OK;
+}
+
+/* R17: out[t] = bf16(sum over i of z[group_slot[t, i]]), skipping -1 entries,
+ * summed in fp64 in ascending i (ascending group) and rounded once,
+ * nearest-even.  A token with no entry gives +0. */
+static void combine_groups_one(const uint16_t* z, const int32_t* group_slot, int64_t t,
+                               int32_t kg, int32_t H, uint16_t* out_row) {
+    for (int32_t c = 0; c < H; ++c) {
+        double acc = 0.0;
+        for (int32_t i = 0; i < kg; ++i) {
+            int32_t r = group_slot[t * kg + i];
+            if (r < 0) continue;
+            acc += ep_oracle_bf16_to_double(z[(int64_t)r * H + c]);
+        }
+        out_row[c] = ep_oracle_bf16_from_double(acc);
+    }
+}
+
+EXPORT void ep_oracle_combine_groups(const uint16_t* z, const int32_t* group_slot, int64_t T,
+                                     int32_t kg, int32_t H, uint16_t* out) {
+    for (int64_t t = 0; t < T; ++t) combine_groups_one(z, group_slot, t, kg, H, out + t * H);
+}
+
+EXPORT void ep_oracle_combine_groups_tokens(const uint16_t* z, const int32_t* group_slot,
+                                            int32_t kg, int32_t H, const int64_t* tokens,
+                                            int64_t n, uint16_t* out_rows) {
+    for (int64_t i = 0; i < n; ++i)
+        combine_groups_one(z, group_slot, tokens[i], kg, H, out_rows + i * H);
 }

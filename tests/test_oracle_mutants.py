@@ -22,6 +22,7 @@ if os.path.dirname(HERE) not in sys.path:
     sys.path.insert(0, os.path.dirname(HERE))
 
 import oracle
+import test_oracle_dedup as pins_dd
 import test_oracle_dispatch_combine as pins_dc
 import test_oracle_formats as pins_fmt
 import test_oracle_layout as pins_lay
@@ -70,6 +71,22 @@ MUTANTS = [
      "(double)scales[(int64_t)s * nb];"),
     ("FP8 combine forgets the weight", "acc += (double)w[t * k + j] * ep_oracle_e4m3_decode(",
      "acc += ep_oracle_e4m3_decode("),
+    ("dedup groups listed in descending order",
+     "for (int32_t g = 0; g < G; ++g)\n            if (in_group[t * G + g]) group_idx[t * kg + i++] = g;",
+     "for (int32_t g = G - 1; g >= 0; --g)\n            if (in_group[t * G + g]) group_idx[t * kg + i++] = g;"),
+    ("dedup group of an expert by modulo", "in_group[t * G + e / per_group] = 1;",
+     "in_group[t * G + e % G] = 1;"),
+    ("dedup counts pairs instead of tokens", "in_group[t * G + e / per_group] = 1;",
+     "in_group[t * G + e / per_group] += 1;"),
+    ("dedup rows start one row late", "int32_t row = group_offsets[g] + cursor[g]++;",
+     "int32_t row = group_offsets[g] + ++cursor[g];"),
+    ("dedup receiver keeps other groups' experts", "int mine = e >= 0 && e < E && e / per_group == g;",
+     "int mine = e >= 0 && e < E;"),
+    ("dedup receiver weights not masked", "mine ? topk_weights[t * k + j] : 0.0f",
+     "topk_weights[t * k + j]"),
+    ("group combine drops the last group",
+     "for (int32_t i = 0; i < kg; ++i) {\n            int32_t r = group_slot[t * kg + i];",
+     "for (int32_t i = 0; i < kg - 1; ++i) {\n            int32_t r = group_slot[t * kg + i];"),
 ]
 
 
@@ -103,6 +120,14 @@ def _battery():
                pins_var.test_combine_fp8_one_hot_is_the_dequantisation,
                pins_var.test_combine_fp8_vs_float64_sum,
                lambda: pins_var.test_pow2_scale_is_the_smallest_power_of_two("dsv3")]
+    checks += [pins_dd.test_group_layout_golden, pins_dd.test_combine_groups_golden,
+               pins_dd.test_one_group_and_one_group_per_expert,
+               pins_dd.test_combine_groups_is_the_unit_weight_combine,
+               lambda: pins_dd.test_group_layout_matches_a_stable_sort("dsv3"),
+               lambda: pins_dd.test_second_level_layout_is_the_expert_layout("lowlat"),
+               lambda: pins_dd.test_receiver_metadata_partitions_each_token("dsv3"),
+               lambda: pins_dd.test_dedup_round_trip("tiny")]
+    checks += [lambda s=s: pins_dd.test_group_layout_brute_force_tiny(s) for s in range(8)]
     return checks
 
 
