@@ -60,6 +60,10 @@ SIGNATURES = {
     "ep_layout_dispatch": (ctypes.c_int, [_vp, _LP, _vp, _sz, _vp, _i32, _i32, _vp, _vp, _vp]),
     "ep_combine": (ctypes.c_int, [_vp, _vp, _LP, _i32, _vp, _vp]),
     "ep_combine_fp8": (ctypes.c_int, [_vp, _vp, _vp, _LP, _i32, _vp, _vp]),
+    "ep_group_layout_init": (ctypes.c_int, [_LP, _i64, _i32, _i32]),
+    "ep_group_layout_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "ep_get_group_layout": (ctypes.c_int, [_vp, _vp, _i32, _i32, _LP, _vp, _vp, _vp, _sz, _vp]),
+    "ep_combine_groups": (ctypes.c_int, [_vp, _LP, _i32, _vp, _vp]),
     "ep_dequant_fp8": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp]),
     "ep_cast_e4m3_bits": (ctypes.c_int, [_u32, _i64, _i32, _vp, _vp]),
     "ep_copy": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
@@ -124,23 +128,27 @@ class EpLayout:
         self.struct = ep_layout_t()
         _check("ep_layout_init", lib().ep_layout_init(ctypes.byref(self.struct), num_tokens,
                                                       num_topk, num_experts, num_groups, capacity))
+        self._alloc(with_recv_src, device,
+                    lib().ep_layout_workspace_bytes(num_tokens, num_topk, num_experts))
+
+    def _alloc(self, with_recv_src: bool, device, workspace_bytes: int) -> None:
+        """Device arrays for the sizes in self.struct, and the struct's pointers to them."""
+        s = self.struct
         dev = torch.device("cuda") if device is None else torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
-        self.num_tokens_per_expert = torch.empty(num_experts, **i32)
-        self.expert_offsets = torch.empty(num_experts + 1, **i32)
-        self.num_tokens_per_group = torch.empty(num_groups, **i32)
-        self.slot_idx = torch.empty((num_tokens, num_topk), **i32)
-        self.recv_src = torch.empty(self.struct.num_recv_rows, **i32) if with_recv_src else None
+        self.num_tokens_per_expert = torch.empty(s.num_experts, **i32)
+        self.expert_offsets = torch.empty(s.num_experts + 1, **i32)
+        self.num_tokens_per_group = torch.empty(s.num_groups, **i32)
+        self.slot_idx = torch.empty((s.num_tokens, s.num_topk), **i32)
+        self.recv_src = torch.empty(s.num_recv_rows, **i32) if with_recv_src else None
         self.error_flags = torch.empty(1, **i32)
-        s = self.struct
         s.num_tokens_per_expert = self.num_tokens_per_expert.data_ptr()
         s.expert_offsets = self.expert_offsets.data_ptr()
         s.num_tokens_per_group = self.num_tokens_per_group.data_ptr()
-        s.slot_idx = self.slot_idx.data_ptr() if num_tokens > 0 else None
+        s.slot_idx = self.slot_idx.data_ptr() if s.num_tokens > 0 else None
         s.recv_src = self.recv_src.data_ptr() if with_recv_src and self.recv_src.numel() else None
         s.error_flags = self.error_flags.data_ptr()
-        nbytes = lib().ep_layout_workspace_bytes(num_tokens, num_topk, num_experts)
-        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.workspace = torch.empty(workspace_bytes, dtype=torch.uint8, device=dev)
 
     @property
     def num_tokens(self) -> int:
@@ -157,6 +165,22 @@ class EpLayout:
     @property
     def num_recv_rows(self) -> int:
         return self.struct.num_recv_rows
+
+
+class EpGroupLayout(EpLayout):
+    """The per-group dedup layout: an EpLayout whose "experts" are the G groups,
+    with kg = min(k, G) entries per token (ep_group_layout_init).  It is
+    accepted wherever an EpLayout is, so ep_dispatch sends to the groups."""
+
+    def __init__(self, num_tokens: int, num_topk: int, num_experts: int, num_groups: int,
+                 with_recv_src: bool = False, device=None):
+        self.struct = ep_layout_t()
+        _check("ep_group_layout_init", lib().ep_group_layout_init(
+            ctypes.byref(self.struct), num_tokens, num_topk, num_groups))
+        self.source_topk = num_topk
+        self.source_experts = num_experts
+        self._alloc(with_recv_src, device,
+                    lib().ep_group_layout_workspace_bytes(num_tokens, num_topk, num_groups))
 
 
 # ----------------------------------------------------------------------------- entry points
@@ -237,6 +261,44 @@ def ep_combine_fp8(expert_q: torch.Tensor, expert_scales: torch.Tensor, topk_wei
     _check("ep_combine_fp8", lib().ep_combine_fp8(
         _ptr(expert_q, "expert_q", torch.uint8), _ptr(expert_scales, "expert_scales", torch.float32),
         _ptr(topk_weights, "topk_weights", torch.float32), ctypes.byref(layout.struct), H,
+        _ptr(out, "out", torch.bfloat16), _stream(stream)))
+
+
+def ep_get_group_layout(topk_idx: torch.Tensor, topk_weights: torch.Tensor | None,
+                        layout: EpGroupLayout, recv_topk_idx: torch.Tensor | None = None,
+                        recv_topk_weights: torch.Tensor | None = None, stream=None) -> EpGroupLayout:
+    """topk_idx int64 [T, k] (and topk_weights fp32 [T, k] when
+    recv_topk_weights is wanted) -> the group layout's arrays, plus optional
+    recv_topk_idx int64 [T*kg, k] / recv_topk_weights fp32 [T*kg, k]."""
+    T, k = layout.num_tokens, layout.source_topk
+    if tuple(topk_idx.shape) != (T, k):
+        raise ValueError("topk_idx shape %s does not match the layout" % (tuple(topk_idx.shape),))
+    rows = (layout.num_recv_rows, k)
+    for name, t in (("topk_weights", topk_weights),):
+        if t is not None and tuple(t.shape) != (T, k):
+            raise ValueError("%s shape does not match the layout" % name)
+    for name, t in (("recv_topk_idx", recv_topk_idx), ("recv_topk_weights", recv_topk_weights)):
+        if t is not None and tuple(t.shape) != rows:
+            raise ValueError("%s must have shape %s" % (name, rows))
+    _check("ep_get_group_layout", lib().ep_get_group_layout(
+        _ptr(topk_idx, "topk_idx", torch.int64) if topk_idx.numel() else None,
+        _ptr(topk_weights, "topk_weights", torch.float32) if topk_weights is not None and topk_weights.numel() else None,
+        k, layout.source_experts, ctypes.byref(layout.struct),
+        _ptr(recv_topk_idx, "recv_topk_idx", torch.int64) if recv_topk_idx is not None and recv_topk_idx.numel() else None,
+        _ptr(recv_topk_weights, "recv_topk_weights", torch.float32) if recv_topk_weights is not None and recv_topk_weights.numel() else None,
+        layout.workspace.data_ptr(), layout.workspace.numel(), _stream(stream)))
+    return layout
+
+
+def ep_combine_groups(z: torch.Tensor, layout: EpGroupLayout, out: torch.Tensor,
+                      stream=None) -> None:
+    """z bf16 [T*kg, H] (one already-weighted row per (token, group)) -> out
+    bf16 [T, H], the unit-weight sum of each token's group rows."""
+    H = z.shape[-1]
+    if z.shape[0] != layout.num_recv_rows or tuple(out.shape) != (layout.num_tokens, H):
+        raise ValueError("group combine buffers do not match the layout")
+    _check("ep_combine_groups", lib().ep_combine_groups(
+        _ptr(z, "z", torch.bfloat16), ctypes.byref(layout.struct), H,
         _ptr(out, "out", torch.bfloat16), _stream(stream)))
 
 

@@ -164,6 +164,67 @@ int ep_combine_fp8(const uint8_t* expert_q, const float* expert_scales,
                                               hidden, out, static_cast<hipStream_t>(stream)));
 }
 
+int ep_group_layout_init(ep_layout_t* group_layout, int64_t num_tokens, int32_t num_topk,
+                         int32_t num_groups) {
+  if (group_layout == nullptr) return EP_ERR_NULL;
+  if (num_tokens < 0 || num_topk < 1 || num_topk > EP_MAX_TOPK || num_groups < 1 ||
+      num_groups > EP_MAX_EXPERTS || num_tokens > kInt32Limit / num_topk)
+    return EP_ERR_SHAPE;
+  const int32_t kg = num_topk < num_groups ? num_topk : num_groups;
+  return ep_layout_init(group_layout, num_tokens, kg, num_groups, num_groups, 0);
+}
+
+size_t ep_group_layout_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_groups) {
+  ep_layout_t tmp;
+  if (ep_group_layout_init(&tmp, num_tokens, num_topk, num_groups) != EP_OK) return 0;
+  return ep::group_layout_workspace_bytes(num_tokens, num_topk, num_groups);
+}
+
+int ep_get_group_layout(const int64_t* topk_idx, const float* topk_weights, int32_t num_topk,
+                        int32_t num_experts, const ep_layout_t* group_layout,
+                        int64_t* recv_topk_idx, float* recv_topk_weights, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int rc = check_layout(group_layout);
+  if (rc != EP_OK) return rc;
+  const ep_layout_t& GL = *group_layout;
+  const int32_t G = GL.num_experts;
+  if (num_topk < 1 || num_topk > EP_MAX_TOPK || num_experts < 1 ||
+      num_experts > EP_MAX_EXPERTS || num_experts % G != 0 || GL.num_groups != G ||
+      GL.capacity != 0 || GL.num_topk != (num_topk < G ? num_topk : G) ||
+      GL.num_tokens > kInt32Limit / num_topk)
+    return EP_ERR_SHAPE;
+  const bool any = GL.num_tokens > 0;
+  if ((any && topk_idx == nullptr) || GL.num_tokens_per_expert == nullptr ||
+      GL.expert_offsets == nullptr || GL.num_tokens_per_group == nullptr ||
+      GL.error_flags == nullptr || workspace == nullptr ||
+      (any && recv_topk_weights != nullptr && topk_weights == nullptr))
+    return EP_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      (reinterpret_cast<uintptr_t>(topk_weights) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(recv_topk_idx) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(recv_topk_weights) & 3u) != 0)
+    return EP_ERR_ALIGN;
+  if (workspace_bytes < ep::group_layout_workspace_bytes(GL.num_tokens, num_topk, G))
+    return EP_ERR_WORKSPACE;
+  return launch_status(ep::launch_group_layout(topk_idx, topk_weights, num_topk, num_experts, GL,
+                                               recv_topk_idx, recv_topk_weights, workspace,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine_groups(const void* z, const ep_layout_t* group_layout, int32_t hidden, void* out,
+                      void* stream) {
+  int rc = check_layout(group_layout);
+  if (rc != EP_OK) return rc;
+  if (group_layout->capacity != 0 || group_layout->num_experts != group_layout->num_groups)
+    return EP_ERR_SHAPE;
+  if (hidden < 8 || hidden > EP_MAX_HIDDEN || hidden % 8 != 0) return EP_ERR_SHAPE;
+  if (group_layout->num_tokens == 0) return EP_OK;
+  if (z == nullptr || out == nullptr) return EP_ERR_NULL;
+  if (!aligned16(z) || !aligned16(out)) return EP_ERR_ALIGN;
+  return launch_status(ep::launch_combine_groups(z, *group_layout, hidden, out,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int ep_dequant_fp8(const uint8_t* q, const float* scales, int64_t rows, int32_t hidden, void* y,
                    void* stream) {
   if (rows < 0 || hidden < 128 || hidden > EP_MAX_HIDDEN || hidden % 128 != 0)

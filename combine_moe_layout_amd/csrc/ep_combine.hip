@@ -54,18 +54,20 @@ __device__ __forceinline__ bool combine_token(const CombineMap& m, int64_t num_t
 }
 
 // K > 0: compile-time top-k.  K == 0: any top-k, one row at a time.
-template <int K, bool kWhole>
+// kUnit: every weight is 1 and w is not read (the group combine of the dedup
+// variant, whose rows arrive already weighted).
+template <int K, bool kUnit>
 __global__ __launch_bounds__(1024) void combine_kernel(
     const u32x4* __restrict__ y, const float* __restrict__ w,
     const int32_t* __restrict__ slot_idx, int64_t num_tokens, int32_t k, int32_t hidden,
     CombineMap m, u32x4* __restrict__ out) {
   int64_t t;
   int32_t lt;
-  if (!combine_token<kWhole>(m, num_tokens, t, lt)) return;
+  if (!combine_token<false>(m, num_tokens, t, lt)) return;
   const int32_t vec_per_row = hidden / 8;
   const int32_t kk = K > 0 ? K : k;
   const int32_t* slots = slot_idx + t * kk;
-  const float* wt = w + t * kk;
+  const float* wt = kUnit ? nullptr : w + t * kk;
   u32x4* dst = out + t * vec_per_row;
 
   if constexpr (K > 0) {
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       s[j] = slots[j];
-      ww[j] = wt[j];
+      ww[j] = kUnit ? 1.0f : wt[j];
     }
     for (int32_t v = lt; v < vec_per_row; v += m.lanes_per_token) {
       u32x4 d[K];
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(
       for (int32_t j = 0; j < k; ++j) {
         const int32_t sj = slots[j];
         if (sj < 0) continue;
-        accumulate8(acc, load_nt(y + (int64_t)sj * vec_per_row + v), wt[j], true);
+        accumulate8(acc, load_nt(y + (int64_t)sj * vec_per_row + v), kUnit ? 1.0f : wt[j], true);
       }
       store_nt(dst + v, pack8(acc));
     }
@@ -122,33 +124,44 @@ static CombineMap combine_map(int32_t vecs_per_row) {
 // token per workgroup): its slots and weights then arrive as per-lane vector
 // loads, which measured about 4% faster here than the scalar loads of the
 // uniform-token form (179 vs 187 us at 8192 tokens x 7168, top-8).
-template <int K>
+template <int K, bool kUnit>
 static void launch_k(dim3 grid, dim3 block, hipStream_t stream, const void* y, const float* w,
                      const ep_layout_t& L, int32_t hidden, CombineMap m, void* out) {
-  hipLaunchKernelGGL((combine_kernel<K, false>), grid, block, 0, stream,
+  hipLaunchKernelGGL((combine_kernel<K, kUnit>), grid, block, 0, stream,
                      static_cast<const u32x4*>(y), w, L.slot_idx, L.num_tokens, L.num_topk,
                      hidden, m, static_cast<u32x4*>(out));
 }
 
-hipError_t launch_combine(const void* y, const float* w, const ep_layout_t& L, int32_t hidden,
-                          void* out, hipStream_t stream) {
+template <bool kUnit>
+static hipError_t launch_combine_weights(const void* y, const float* w, const ep_layout_t& L,
+                                         int32_t hidden, void* out, hipStream_t stream) {
   const int64_t T = L.num_tokens;
   if (T == 0) return hipSuccess;
   const CombineMap m = combine_map(hidden / 8);
   const dim3 grid((unsigned)((T + m.tokens_per_block - 1) / m.tokens_per_block));
   const dim3 block(m.lanes_per_token * m.tokens_per_block);
   switch (L.num_topk) {
-    case 1: launch_k<1>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 2: launch_k<2>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 3: launch_k<3>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 4: launch_k<4>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 5: launch_k<5>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 6: launch_k<6>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 7: launch_k<7>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 8: launch_k<8>(grid, block, stream, y, w, L, hidden, m, out); break;
-    default: launch_k<0>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 1: launch_k<1, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 2: launch_k<2, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 3: launch_k<3, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 4: launch_k<4, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 5: launch_k<5, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 6: launch_k<6, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 7: launch_k<7, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 8: launch_k<8, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
+    default: launch_k<0, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const void* y, const float* w, const ep_layout_t& L, int32_t hidden,
+                          void* out, hipStream_t stream) {
+  return launch_combine_weights<false>(y, w, L, hidden, out, stream);
+}
+
+hipError_t launch_combine_groups(const void* z, const ep_layout_t& GL, int32_t hidden, void* out,
+                                 hipStream_t stream) {
+  return launch_combine_weights<true>(z, nullptr, GL, hidden, out, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,0 +1,143 @@
+// ep_group.hip -- per-group dedup layout on gfx950.
+//
+// A variant of the routing layout in which a token is sent once to every group
+// of experts (a rank, in a multi-GPU deployment) that holds at least one of its
+// top-k experts, instead of once per expert.  The pages count the bytes each
+// rank sends and receives ("DeepEP是什麼？…" (yololab.net), section "Load
+// Imbalance") and give the per-expert volume batch x top_k x hidden
+// ("DeepEP 编址服务深度对抗分析", section 五.2); sending per group cuts that
+// volume whenever several of a token's experts share a group.
+//
+// What it computes (expert e belongs to group e / (E/G)):
+//   - a token's entries are the groups it reaches, ascending, padded with -1
+//     to kg = min(k, G) entries;
+//   - receive rows are group-major and ascending in token inside a group: the
+//     ordinary counting-sort layout over the entries, with the G groups in the
+//     role of the experts;
+//   - each used row carries the token's top-k list masked to the row's group
+//     (other entries -1, weight 0), which is what the receiving side needs to
+//     run its own experts.
+//
+// How: three steps on the caller's stream.
+//   1. group_table_kernel: one lane per (token, k) pair, tokens in segments
+//      of lanes (top-k rounded up to a power of two).  Each lane finds, with
+//      shuffles inside its segment, whether its group is the first occurrence
+//      in the token and how many distinct groups of the token are smaller:
+//      that is the entry's position in the ascending list.  The int64 table
+//      lands in the workspace; each workgroup writes one bad-id flag entry
+//      (plain stores, no atomics, no memset).
+//   2. the layout kernels over that table (E := G, k := kg); they OR the
+//      table's flag entries into error_flags.
+//   3. group_meta_kernel: lane (t, j) writes column j of every row of token t.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+
+constexpr int kGroupThreads = 256;
+
+struct GroupSeg {
+  int32_t seg;               // lanes per token: top-k rounded up to a power of two (<= 64)
+  int32_t tokens_per_block;  // kGroupThreads / seg
+};
+
+static GroupSeg group_seg(int32_t k) {
+  int32_t s = 1;
+  while (s < k) s *= 2;
+  return GroupSeg{s, kGroupThreads / s};
+}
+
+static int64_t group_table_blocks(int64_t T, int32_t k) {
+  const GroupSeg g = group_seg(k);
+  return (T + g.tokens_per_block - 1) / g.tokens_per_block;
+}
+
+static size_t group_table_bytes(int64_t T, int32_t kg) {
+  return (((size_t)(T * kg) * sizeof(int64_t) + 255) / 256) * 256;
+}
+
+size_t group_layout_workspace_bytes(int64_t T, int32_t k, int32_t G) {
+  const int32_t kg = k < G ? k : G;
+  return group_table_bytes(T, kg) + layout_workspace_bytes(T * kg, G, group_table_blocks(T, k));
+}
+
+__global__ __launch_bounds__(kGroupThreads) void group_table_kernel(
+    const int64_t* __restrict__ topk_idx, int64_t T, int32_t k, int32_t E, int32_t per_group,
+    int32_t kg, GroupSeg sg, int64_t* __restrict__ table, int32_t* __restrict__ block_flags) {
+  const int64_t t = (int64_t)blockIdx.x * sg.tokens_per_block + threadIdx.x / sg.seg;
+  const int32_t j = threadIdx.x % sg.seg;
+  const bool live = t < T && j < k;
+  const int64_t e = live ? topk_idx[t * k + j] : -1;
+  const bool valid = e >= 0 && e < E;
+  const bool bad = live && !valid && e != -1;
+  const int32_t g = valid ? (int32_t)(e / per_group) : -1;
+
+  // Every lane takes part in the shuffles; a segment never straddles a wave.
+  const int32_t base = (int32_t)(threadIdx.x % kWave) - j;
+  bool first = g >= 0;
+  for (int32_t d = 0; d < sg.seg; ++d) {
+    const int32_t gd = __shfl(g, base + d);
+    if (d < j && gd == g) first = false;
+  }
+  int32_t rank = 0, ndist = 0;
+  for (int32_t d = 0; d < sg.seg; ++d) {
+    const int32_t gd = __shfl(g, base + d);
+    const int32_t fd = __shfl(first ? 1 : 0, base + d);
+    rank += (fd && gd < g) ? 1 : 0;
+    ndist += fd;
+  }
+  // rank < ndist <= kg for a first occurrence; the padding positions
+  // [ndist, kg) each have exactly one lane with that j
+  if (t < T) {
+    if (first) table[t * kg + rank] = g;
+    if (j >= ndist && j < kg) table[t * kg + j] = -1;
+  }
+  const int any_bad = __syncthreads_or(bad ? 1 : 0);
+  if (threadIdx.x == 0) block_flags[blockIdx.x] = any_bad ? EP_FLAG_BAD_EXPERT : 0;
+}
+
+__global__ __launch_bounds__(kGroupThreads) void group_meta_kernel(
+    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int64_t T,
+    int32_t k, int32_t E, int32_t per_group, int32_t kg, GroupSeg sg,
+    const int64_t* __restrict__ table, const int32_t* __restrict__ group_slot,
+    int64_t* __restrict__ recv_idx, float* __restrict__ recv_w) {
+  const int64_t t = (int64_t)blockIdx.x * sg.tokens_per_block + threadIdx.x / sg.seg;
+  const int32_t j = threadIdx.x % sg.seg;
+  if (t >= T || j >= k) return;
+  const int64_t e = topk_idx[t * k + j];
+  const bool valid = e >= 0 && e < E;
+  const int32_t g = valid ? (int32_t)(e / per_group) : -1;
+  const float w = recv_w != nullptr ? topk_weights[t * k + j] : 0.0f;
+  for (int32_t i = 0; i < kg; ++i) {
+    const int32_t r = group_slot[t * kg + i];
+    if (r < 0) break;  // the entries after the token's groups are all padding
+    const bool mine = g >= 0 && (int64_t)g == table[t * kg + i];
+    if (recv_idx != nullptr) recv_idx[(int64_t)r * k + j] = mine ? e : -1;
+    if (recv_w != nullptr) recv_w[(int64_t)r * k + j] = mine ? w : 0.0f;
+  }
+}
+
+hipError_t launch_group_layout(const int64_t* topk_idx, const float* topk_weights, int32_t k,
+                               int32_t E, const ep_layout_t& GL, int64_t* recv_idx,
+                               float* recv_w, void* workspace, hipStream_t stream) {
+  const int64_t T = GL.num_tokens;
+  const int32_t G = GL.num_experts;
+  const int32_t kg = GL.num_topk;
+  const GroupSeg sg = group_seg(k);
+  const int64_t blocks = group_table_blocks(T, k);
+  int64_t* table = static_cast<int64_t*>(workspace);
+  void* layout_ws = static_cast<char*>(workspace) + group_table_bytes(T, kg);
+  if (blocks > 0)
+    hipLaunchKernelGGL(group_table_kernel, dim3((unsigned)blocks), dim3(kGroupThreads), 0, stream,
+                       topk_idx, T, k, E, E / G, kg, sg, table,
+                       layout_extra_flags(GL, layout_ws));
+  hipError_t err = launch_layout_ids(table, GL, layout_ws, (int32_t)blocks, stream);
+  if (err != hipSuccess) return err;
+  if (blocks > 0 && (recv_idx != nullptr || recv_w != nullptr))
+    hipLaunchKernelGGL(group_meta_kernel, dim3((unsigned)blocks), dim3(kGroupThreads), 0, stream,
+                       topk_idx, topk_weights, T, k, E, E / G, kg, sg, table, GL.slot_idx,
+                       recv_idx, recv_w);
+  return hipGetLastError();
+}
+
+}  // namespace ep

@@ -22,10 +22,18 @@ static_assert((1 << kExpertBits) >= EP_MAX_EXPERTS, "expert id must fit the pack
 
 inline int64_t layout_num_chunks(int64_t pairs) { return (pairs + kChunkPairs - 1) / kChunkPairs; }
 
-size_t layout_workspace_bytes(int64_t pairs, int32_t num_experts);
+// Bytes of layout workspace: per-chunk counts and flags, plus extra_flags
+// flag entries for a kernel that prepares the ids (the group layout's table).
+size_t layout_workspace_bytes(int64_t pairs, int32_t num_experts, int64_t extra_flags = 0);
 
 hipError_t launch_layout(const int64_t* topk_idx, const ep_layout_t& L, void* workspace,
                          hipStream_t stream);
+
+// The layout over an id table that another kernel wrote, which also left
+// extra_flags bad-id flag entries at layout_extra_flags(L, workspace).
+hipError_t launch_layout_ids(const int64_t* ids, const ep_layout_t& L, void* workspace,
+                             int32_t extra_flags, hipStream_t stream);
+int32_t* layout_extra_flags(const ep_layout_t& L, void* workspace);
 
 hipError_t launch_dispatch(const void* x, const ep_layout_t& L, int32_t hidden, int32_t dtype,
                            void* recv_x, float* recv_scales, hipStream_t stream);
@@ -59,5 +67,16 @@ hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout
 
 hipError_t launch_combine_fp8(const uint8_t* q, const float* scales, const float* w,
                               const ep_layout_t& L, int32_t hidden, void* out, hipStream_t stream);
+
+// Per-group dedup variant: the group layout (a layout whose experts are the
+// G groups, with kg = min(k, G) entries per token) and its unit-weight combine.
+size_t group_layout_workspace_bytes(int64_t T, int32_t k, int32_t G);
+
+hipError_t launch_group_layout(const int64_t* topk_idx, const float* topk_weights, int32_t k,
+                               int32_t E, const ep_layout_t& GL, int64_t* recv_idx,
+                               float* recv_w, void* workspace, hipStream_t stream);
+
+hipError_t launch_combine_groups(const void* z, const ep_layout_t& GL, int32_t hidden, void* out,
+                                 hipStream_t stream);
 
 }  // namespace ep

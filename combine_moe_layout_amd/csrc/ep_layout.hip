@@ -47,9 +47,9 @@ struct LayoutShared {
   int32_t wave[kLayoutWaves];
 };
 
-size_t layout_workspace_bytes(int64_t pairs, int32_t num_experts) {
+size_t layout_workspace_bytes(int64_t pairs, int32_t num_experts, int64_t extra_flags) {
   int64_t chunks = layout_num_chunks(pairs);
-  size_t bytes = (size_t)(chunks * num_experts + chunks) * sizeof(int32_t);
+  size_t bytes = (size_t)(chunks * num_experts + chunks + extra_flags) * sizeof(int32_t);
   return ((bytes + 255) / 256) * 256 + 256;
 }
 
@@ -195,10 +195,12 @@ __device__ __forceinline__ void chunk_totals(int32_t E, int32_t num_chunks, int6
 
 // Phase 2 for chunk c, given every chunk's totals in memory.  kSingleChunk:
 // there is only this chunk, sh.tot and sh.pre are already set by the caller
-// and known_bad is its bad-id flag.
+// and known_bad is its bad-id flag.  chunk_flags holds num_flags entries: one
+// per chunk, then any written by a kernel that prepared the ids.
 template <bool kSingleChunk>
 __device__ __forceinline__ void finish_chunk(
     int64_t num_pairs, int32_t E, int32_t num_groups, int32_t capacity, int32_t num_chunks,
+    int32_t num_flags,
     int64_t c, const int32_t* __restrict__ chunk_count, const int32_t* __restrict__ chunk_flags,
     LayoutShared& sh, const int32_t (&eid)[kLayoutItems], const int32_t (&local)[kLayoutItems],
     int32_t* __restrict__ slot_idx, int32_t* __restrict__ recv_src,
@@ -272,12 +274,10 @@ __device__ __forceinline__ void finish_chunk(
       for (int e = g * per_group; e < (g + 1) * per_group; ++e) s += sh.tot[e];
       num_tokens_per_group[g] = s;
     }
-    int32_t bad = 0;
-    if constexpr (kSingleChunk) {
-      bad = known_bad;
-    } else {
-      for (int cc = tid; cc < num_chunks; cc += kLayoutThreads) bad |= chunk_flags[cc];
-    }
+    // the single chunk's own flag is known_bad; every other entry is read
+    int32_t bad = kSingleChunk ? known_bad : 0;
+    for (int cc = tid + (kSingleChunk ? 1 : 0); cc < num_flags; cc += kLayoutThreads)
+      bad |= chunk_flags[cc];
     const int any_bad = __syncthreads_or(bad);
     const int any_over = __syncthreads_or(over ? 1 : 0);
     if (tid == 0)
@@ -288,7 +288,7 @@ __device__ __forceinline__ void finish_chunk(
 struct LayoutArgs {
   const int64_t* topk_idx;
   int64_t num_pairs;
-  int32_t num_experts, expert_bits, num_groups, capacity, num_chunks;
+  int32_t num_experts, expert_bits, num_groups, capacity, num_chunks, num_flags;
   int32_t* chunk_count;
   int32_t* chunk_flags;
   int32_t* slot_idx;
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(LayoutArg
     local[i] = v >= 0 ? (v >> kExpertBits) : 0;
   }
   finish_chunk<false>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, a.num_chunks,
-                      blockIdx.x, a.chunk_count, a.chunk_flags, sh, eid, local, a.slot_idx,
+                      a.num_flags, blockIdx.x, a.chunk_count, a.chunk_flags, sh, eid, local, a.slot_idx,
                       a.recv_src, a.num_tokens_per_expert, a.expert_offsets,
                       a.num_tokens_per_group, a.error_flags, 0);
 }
@@ -338,7 +338,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(LayoutArg
                               sh.counts, a.chunk_count, a.chunk_flags, sh.tot, eid, local);
   for (int e = threadIdx.x; e < a.num_experts; e += kLayoutThreads) sh.pre[e] = 0;
   __syncthreads();
-  finish_chunk<true>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, 1, 0, a.chunk_count,
+  finish_chunk<true>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, 1, a.num_flags, 0,
+                     a.chunk_count,
                      a.chunk_flags, sh, eid, local, a.slot_idx, a.recv_src,
                      a.num_tokens_per_expert, a.expert_offsets, a.num_tokens_per_group,
                      a.error_flags, bad);
@@ -346,6 +347,16 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(LayoutArg
 
 hipError_t launch_layout(const int64_t* topk_idx, const ep_layout_t& L, void* workspace,
                          hipStream_t stream) {
+  return launch_layout_ids(topk_idx, L, workspace, 0, stream);
+}
+
+int32_t* layout_extra_flags(const ep_layout_t& L, void* workspace) {
+  const int64_t chunks = layout_num_chunks(L.num_tokens * (int64_t)L.num_topk);
+  return static_cast<int32_t*>(workspace) + chunks * L.num_experts + chunks;
+}
+
+hipError_t launch_layout_ids(const int64_t* topk_idx, const ep_layout_t& L, void* workspace,
+                             int32_t extra_flags, hipStream_t stream) {
   LayoutArgs a;
   a.topk_idx = topk_idx;
   a.num_pairs = L.num_tokens * (int64_t)L.num_topk;
@@ -357,6 +368,7 @@ hipError_t launch_layout(const int64_t* topk_idx, const ep_layout_t& L, void* wo
   a.num_groups = L.num_groups;
   a.capacity = L.capacity;
   a.num_chunks = (int32_t)chunks;
+  a.num_flags = (int32_t)chunks + extra_flags;
   a.chunk_count = static_cast<int32_t*>(workspace);
   a.chunk_flags = a.chunk_count + chunks * L.num_experts;
   a.slot_idx = L.slot_idx;

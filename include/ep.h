@@ -177,7 +177,7 @@ int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void*
  * Combine ([yololab] stage table, combine row: back to token order with a
  * weighted reduction).  expert_out: device bf16 [R, hidden]; topk_weights:
  * device fp32 [T, k].  out[t] = bf16(sum over j with slot_idx[t*k+j] >= 0 of
- * topk_weights[t,k] * expert_out[slot]), accumulated in fp32, rounded to
+ * topk_weights[t,j] * expert_out[slot]), accumulated in fp32, rounded to
  * nearest-even; a token with no valid pair gets +0.  No renormalisation.
  * out: device bf16 [T, hidden], must not alias the inputs.  hidden % 8 == 0.
  * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN or EP_ERR_LAUNCH.
@@ -197,6 +197,73 @@ int ep_combine(const void* expert_out, const float* topk_weights, const ep_layou
 int ep_combine_fp8(const uint8_t* expert_q, const float* expert_scales,
                    const float* topk_weights, const ep_layout_t* layout, int32_t hidden, void* out,
                    void* stream);
+
+/*
+ * Per-group dedup variant.  A token goes once to every group of experts that
+ * holds at least one of its top-k experts (a group is what one EP rank would
+ * own), instead of once per expert: the pages count each rank's send and
+ * receive bytes ([yololab] "Load Imbalance") and give the per-expert volume
+ * ([backyes] 五.2), which this variant cuts whenever several of a token's
+ * experts share a group.
+ *
+ * The group layout is an ep_layout_t whose "experts" are the G groups:
+ *   num_tokens = T, num_topk = kg = min(k, G), num_experts = num_groups = G,
+ *   capacity = 0, num_recv_rows = T * kg.
+ * Its arrays, written by ep_get_group_layout:
+ *   num_tokens_per_expert [G]   tokens that reach each group (so do
+ *   num_tokens_per_group  [G]   both arrays)
+ *   expert_offsets        [G+1] first receive row of each group; [G] = rows used
+ *   slot_idx              [T*kg] receive row of entry i of token t: the token's
+ *                               groups in ascending order, then -1; rows are
+ *                               group-major and ascending in t inside a group
+ *   recv_src              [T*kg] optional: entry index t*kg + i of each used row
+ *   error_flags           [1]   EP_FLAG_BAD_EXPERT if some topk_idx entry is
+ *                               outside [-1, num_experts) (that entry is skipped)
+ * Dispatching to the groups is ep_dispatch(x, group_layout, ...), every dtype.
+ */
+
+/* Fill the size fields of a group layout (arrays NULL).  Requires
+ * 0 <= num_tokens, 1 <= num_topk <= EP_MAX_TOPK, 1 <= num_groups <=
+ * EP_MAX_EXPERTS, num_tokens * num_topk below 2^31.  Host only. */
+int ep_group_layout_init(ep_layout_t* group_layout, int64_t num_tokens, int32_t num_topk,
+                         int32_t num_groups);
+
+/* Bytes of device workspace ep_get_group_layout needs; 0 if the sizes are invalid.  Host only. */
+size_t ep_group_layout_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_groups);
+
+/*
+ * Group layout and the receiving side's routing metadata.
+ * topk_idx: device int64 [T, num_topk]; topk_weights: device fp32
+ * [T, num_topk] (needed only for recv_topk_weights).  num_experts must be a
+ * multiple of the group layout's G; expert e belongs to group e / (E/G).
+ * Writes every array of *group_layout and, for each used row r of token t and
+ * group g (both optional, NULL to skip):
+ *   recv_topk_idx     int64 [T*kg, num_topk]: topk_idx[t, j] if that expert is
+ *                     valid and in group g, else -1
+ *   recv_topk_weights fp32  [T*kg, num_topk]: topk_weights[t, j] for the same
+ *                     entries, else 0
+ * Rows past the used ones are left untouched.  workspace: at least
+ * ep_group_layout_workspace_bytes(T, num_topk, G) bytes, 256-byte aligned,
+ * scratch.  Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN,
+ * EP_ERR_WORKSPACE or EP_ERR_LAUNCH.
+ */
+int ep_get_group_layout(const int64_t* topk_idx, const float* topk_weights, int32_t num_topk,
+                        int32_t num_experts, const ep_layout_t* group_layout,
+                        int64_t* recv_topk_idx, float* recv_topk_weights, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Group combine: the sending side's reduction of the rows that come back.
+ * The receiving side has already weighted and summed its experts' outputs
+ * into one row per (token, group), so the weights here are all 1:
+ * out[t] = bf16(sum over i with slot_idx[t*kg+i] >= 0 of z[slot]) in ascending
+ * group order, accumulated in fp32, rounded to nearest-even; +0 for a token
+ * with no group.  z: device bf16 [T*kg, hidden]; out: device bf16 [T, hidden],
+ * not aliasing z.  hidden % 8 == 0.
+ * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN or EP_ERR_LAUNCH.
+ */
+int ep_combine_groups(const void* z, const ep_layout_t* group_layout, int32_t hidden, void* out,
+                      void* stream);
 
 /*
  * Identity-expert stand-in for FP8 receive buffers (not part of the path;

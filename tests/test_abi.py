@@ -150,6 +150,50 @@ def test_entry_points_reject_bad_arguments(L):
     assert L.ep_copy(None, None, 0, None) == 0
 
 
+def test_group_layout_sizes_and_validation(L):
+    s = binding.ep_layout_t()
+    by = ctypes.byref
+    # kg = min(k, G); the group layout's experts and groups are the G groups
+    assert L.ep_group_layout_init(by(s), 8192, 8, 8) == 0
+    assert (s.num_topk, s.num_experts, s.num_groups, s.capacity, s.num_recv_rows) == (8, 8, 8, 0, 65536)
+    assert L.ep_group_layout_init(by(s), 100, 8, 3) == 0 and (s.num_topk, s.num_recv_rows) == (3, 300)
+    assert L.ep_group_layout_init(by(s), 0, 4, 16) == 0 and s.num_recv_rows == 0
+    for args in ((-1, 8, 8), (10, 0, 8), (10, 65, 8), (10, 8, 0), (10, 8, 1025), (1 << 28, 16, 8)):
+        assert L.ep_group_layout_init(by(s), *args) == -2, args
+    assert L.ep_group_layout_init(None, 1, 1, 1) == -1
+    prev = 0
+    for T in (0, 1, 255, 256, 2048, 8192, 65536):
+        b = L.ep_group_layout_workspace_bytes(T, 8, 8)
+        assert b % 256 == 0 and b >= 8 * T * 8 and b >= prev
+        prev = b
+    assert L.ep_group_layout_workspace_bytes(10, 0, 8) == 0
+
+    fake = 1 << 20
+    g = binding.ep_layout_t()
+    assert L.ep_group_layout_init(by(g), 64, 4, 8) == 0           # kg = 4
+    g.num_tokens_per_expert = g.expert_offsets = g.num_tokens_per_group = fake
+    g.slot_idx = g.error_flags = fake
+    need = L.ep_group_layout_workspace_bytes(64, 4, 8)
+    assert L.ep_get_group_layout(fake, fake, 4, 60, by(g), None, None, fake, need, None) == -2   # E % G
+    assert L.ep_get_group_layout(fake, fake, 3, 64, by(g), None, None, fake, need, None) == -2   # kg != min(k, G)
+    assert L.ep_get_group_layout(None, None, 4, 64, by(g), None, None, fake, need, None) == -1   # topk_idx
+    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, fake, fake, need, None) == -1   # weights needed
+    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, None, None, need, None) == -1   # workspace
+    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, None, fake + 64, need, None) == -3
+    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), fake + 4, None, fake, need, None) == -3
+    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, None, fake, need - 1, None) == -4
+    e = binding.ep_layout_t()
+    assert L.ep_layout_init(by(e), 64, 4, 16, 4, 0) == 0             # an expert layout is not a group layout
+    e.num_tokens_per_expert = e.expert_offsets = e.num_tokens_per_group = e.slot_idx = e.error_flags = fake
+    assert L.ep_combine_groups(fake, by(e), 256, fake, None) == -2
+    assert L.ep_combine_groups(None, by(g), 256, fake, None) == -1
+    assert L.ep_combine_groups(fake, by(g), 256, fake + 8, None) == -3
+    assert L.ep_combine_groups(fake, by(g), 12, fake, None) == -2
+    assert L.ep_combine_fp8(fake, fake, fake, by(e), 200, fake, None) == -2   # H % 128
+    assert L.ep_combine_fp8(fake, None, fake, by(e), 256, fake, None) == -1
+    assert L.ep_combine_fp8(fake, fake + 2, fake, by(e), 256, fake, None) == -3
+
+
 def test_status_strings(L):
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert L.ep_status_string(code).decode() not in ("", "unknown status")
