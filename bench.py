@@ -57,6 +57,26 @@ def ideal_bytes(T: int, H: int, E: int, G: int, k: int, R_used: int, fp8: bool,
     return dict(layout=layout, dispatch=dispatch, combine=combine)
 
 
+def ideal_bytes_dedup(T: int, H: int, G: int, k: int, kg: int, used: int, fp8: bool) -> dict:
+    """Algorithmic HBM bytes of one pass of the per-group dedup variant, with
+    `used` receive rows (one per token and group it reaches).
+
+    layout:   read topk_idx and topk_weights (12 B per pair), write the group
+              rows (4 B per entry) and each used row's masked top-k ids and
+              weights (12 B per row and k), plus counts and offsets.
+    dispatch: read x once (2H B per token) and the entries' rows (4 B each);
+              write one receive row per used row (H + 4*H/128 B FP8, 2H bf16).
+    combine:  read one bf16 row per used row and the entries' rows (4 B
+              each); write one bf16 row per token.
+    """
+    P = T * k
+    layout = 12 * P + 4 * T * kg + 12 * used * k + 4 * (3 * G + 1)
+    row = H + 4 * (H // 128) if fp8 else 2 * H
+    dispatch = 2 * H * T + 4 * T * kg + row * used
+    combine = 2 * H * used + 4 * T * kg + 2 * H * T
+    return dict(layout=layout, dispatch=dispatch, combine=combine)
+
+
 def sources_digest() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -137,7 +157,13 @@ def main() -> int:
     ap.add_argument("--fused", action="store_true",
                     help="layout and dispatch through ep_layout_dispatch (one launch for batches "
                          "of at most 2048 pairs); the layout/dispatch split is then not reported")
+    ap.add_argument("--dedup", action="store_true",
+                    help="per-group dedup variant: ep_get_group_layout (with the receiving "
+                         "side's metadata), dispatch to the groups, ep_combine_groups")
     args = ap.parse_args()
+    if args.dedup and (args.fused or args.fp8_combine or args.graph):
+        print("--dedup times its own three calls; it combines with --pow2 only", file=sys.stderr)
+        return 2
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the path runs on a single MI355X and has no "
@@ -191,6 +217,33 @@ def main() -> int:
     torch.cuda.synchronize()
     used = int((lay.slot_idx >= 0).sum().item())
     nbytes = ideal_bytes(T, H, E, G, k, used, fp8, args.fp8_combine)
+    dedup = None
+    if args.dedup:
+        # the per-expert buffers above only measure how many rows that path
+        # would move; the dedup step has buffers of its own
+        del y, recv_q, recv_s
+        glay = B.EpGroupLayout(T, k, E, G, device=dev)
+        Rg, kg = glay.num_recv_rows, glay.num_topk
+        g_ridx = torch.empty((Rg, k), dtype=torch.int64, device=dev)
+        g_rw = torch.empty((Rg, k), dtype=torch.float32, device=dev)
+        g_q = torch.empty((Rg, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+        g_s = torch.empty((Rg, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+        g_z = torch.empty((Rg, H), dtype=torch.bfloat16, device=dev)
+        B.ep_get_group_layout(topk_idx, topk_w, glay, g_ridx, g_rw)
+        B.ep_dispatch(x, glay, dtype_enum, g_q, g_s)
+        # identity experts on the receiving side, untimed: one row per (token, group)
+        if fp8:
+            B.ep_dequant_fp8(g_q, g_s, g_z)
+        else:
+            B.ep_copy(g_q, g_z)
+        torch.cuda.synchronize()
+        g_used = int(glay.expert_offsets[-1].item())
+        row_b = H + 4 * (H // 128) if fp8 else 2 * H
+        dedup = {"rows": g_used, "rows_per_expert_path": used,
+                 "row_ratio": round(g_used / max(used, 1), 4),
+                 "dispatch_row_bytes": g_used * row_b, "dispatch_row_bytes_per_expert_path": used * row_b,
+                 "combine_row_bytes": g_used * 2 * H, "combine_row_bytes_per_expert_path": used * 2 * H}
+        nbytes = ideal_bytes_dedup(T, H, G, k, kg, g_used, fp8)
     step_bytes = sum(nbytes.values())
 
     def step(ev=None, s=None):
@@ -198,6 +251,17 @@ def main() -> int:
         # the capture stream while a graph is being recorded)
         if ev is not None:
             ev[0].record(s)
+        if args.dedup:
+            B.ep_get_group_layout(topk_idx, topk_w, glay, g_ridx, g_rw, s)
+            if ev is not None:
+                ev[1].record(s)
+            B.ep_dispatch(x, glay, dtype_enum, g_q, g_s, s)
+            if ev is not None:
+                ev[2].record(s)
+            B.ep_combine_groups(g_z, glay, out, s)
+            if ev is not None:
+                ev[3].record(s)
+            return
         if args.fused:
             B.ep_layout_dispatch(topk_idx, lay, x, dtype_enum, recv_q, recv_s, s)
             if ev is not None:
@@ -286,7 +350,7 @@ def main() -> int:
         dc_gbps = combine_gbps = dispatch_gbps = None
     digest = sources_digest()
     # the committed counters cover the bf16-input combine kernel only
-    traffic = None if args.fp8_combine else committed_traffic("combine", name, digest)
+    traffic = None if (args.fp8_combine or args.dedup) else committed_traffic("combine", name, digest)
 
     result = {
         "metric": "dispatch+combine effective HBM GB/s (% peak) at 8K tok×7168, top-8/256",
@@ -306,7 +370,8 @@ def main() -> int:
                    "dispatch_dtype": ("fp8_e4m3+pow2 scale/128ch" if args.pow2 else
                                       "fp8_e4m3+fp32 scale/128ch") if fp8 else "bf16",
                    "combine_dtype": "fp8_e4m3 in, bf16 out" if args.fp8_combine else "bf16",
-                   "step": "layout_dispatch (fused call)+combine" if args.fused
+                   "step": "group_layout+dispatch_to_groups+combine_groups (per-group dedup)"
+                   if args.dedup else "layout_dispatch (fused call)+combine" if args.fused
                    else "layout+dispatch+combine"},
         "pct_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "ideal_bytes": nbytes,
@@ -321,14 +386,17 @@ def main() -> int:
         result["dispatch_plus_combine_pct_peak"] = round(100 * dc_gbps / HBM_PEAK_GBPS, 2)
         result["dispatch_gbps"] = round(dispatch_gbps, 1)
         result["roofline"] = {
-            "kernel": "combine_fp8" if args.fp8_combine else "combine", "bound": "hbm",
+            "kernel": "combine_groups" if args.dedup else "combine_fp8" if args.fp8_combine
+            else "combine", "bound": "hbm",
             "achieved": round(combine_gbps, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(combine_gbps / HBM_PEAK_GBPS, 4),
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
             "algorithmic_bytes": nbytes["combine"]}
     else:
         result["config"]["step"] += " (HIP graph replay)"
-    if not args.no_cpu_baseline and name == "dsv3":
+    if dedup is not None:
+        result["dedup"] = dedup
+    if not args.no_cpu_baseline and name == "dsv3" and not args.dedup:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)
     return 0

@@ -82,8 +82,16 @@ __global__ __launch_bounds__(1024) void combine_kernel(
       u32x4 d[K];
 #pragma unroll
       for (int j = 0; j < K; ++j) {
-        const int64_t row = s[j] >= 0 ? s[j] : 0;
-        d[j] = load_nt(y + row * vec_per_row + v);
+        if constexpr (kUnit) {
+          // group rows: a token's entries are its rows, then padding; with
+          // many padded entries (skewed routing) loading only the real rows
+          // saves most of the row-0 loads
+          d[j] = u32x4{0u, 0u, 0u, 0u};
+          if (s[j] >= 0) d[j] = load_nt(y + (int64_t)s[j] * vec_per_row + v);
+        } else {
+          const int64_t row = s[j] >= 0 ? s[j] : 0;
+          d[j] = load_nt(y + row * vec_per_row + v);
+        }
       }
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
