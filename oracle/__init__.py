@@ -69,6 +69,15 @@ def _load(path: str) -> ctypes.CDLL:
     L.ep_oracle_group_layout.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     L.ep_oracle_combine_groups.argtypes = [vp, vp, i64, i32, i32, vp]
     L.ep_oracle_combine_groups_tokens.argtypes = [vp, vp, i32, i32, vp, i64, vp]
+    L.ep_oracle_quantize_token_mxfp8.argtypes = [vp, i32, vp, vp]
+    L.ep_oracle_dispatch_mxfp8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    L.ep_oracle_dequant_mxfp8.argtypes = [vp, vp, i64, i32, vp]
+    L.ep_oracle_f16_to_double.restype = ctypes.c_double
+    L.ep_oracle_f16_to_double.argtypes = [ctypes.c_uint16]
+    L.ep_oracle_f16_from_double.restype = ctypes.c_uint16
+    L.ep_oracle_f16_from_double.argtypes = [ctypes.c_double]
+    L.ep_oracle_combine_f16.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+    L.ep_oracle_combine_f16_tokens.argtypes = [vp, vp, vp, i32, i32, vp, i64, vp]
     return L
 
 
@@ -363,4 +372,68 @@ def combine_groups_tokens(z_bits: np.ndarray, group_slot: np.ndarray, tokens) ->
     out = np.empty((tokens.size, H), np.uint16)
     lib().ep_oracle_combine_groups_tokens(_p(z_bits), _p(group_slot), kg, H, _p(tokens),
                                           tokens.size, _p(out))
+    return out
+
+
+# ----------------------------------------------------------------------------- MXFP8 and FP16 variants
+def quantize_token_mxfp8(x_row_bits: np.ndarray):
+    """MXFP8 (reading R18): codes [H] and E8M0 scale bytes [H/32]."""
+    x_row_bits = _c(x_row_bits, np.uint16).reshape(-1)
+    H = x_row_bits.size
+    q = np.empty(H, np.uint8)
+    s = np.empty(H // 32, np.uint8)
+    lib().ep_oracle_quantize_token_mxfp8(_p(x_row_bits), H, _p(q), _p(s))
+    return q, s
+
+
+def dispatch_mxfp8(x_bits: np.ndarray, slot_idx: np.ndarray, R: int):
+    x_bits = _c(x_bits, np.uint16)
+    slot_idx = _c(slot_idx, np.int32)
+    T, H = x_bits.shape
+    k = slot_idx.shape[1]
+    q = np.zeros((R, H), np.uint8)
+    s = np.zeros((R, H // 32), np.uint8)
+    lib().ep_oracle_dispatch_mxfp8(_p(x_bits), T, k, H, _p(slot_idx), _p(q), _p(s))
+    return q, s
+
+
+def dequant_mxfp8(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    q = _c(q, np.uint8)
+    scales = _c(scales, np.uint8)
+    R, H = q.shape
+    y = np.empty((R, H), np.uint16)
+    lib().ep_oracle_dequant_mxfp8(_p(q), _p(scales), R, H, _p(y))
+    return y
+
+
+def f16_to_double(bits: int) -> float:
+    return float(lib().ep_oracle_f16_to_double(int(bits)))
+
+
+def f16_from_double(v: float) -> int:
+    return int(lib().ep_oracle_f16_from_double(float(v)))
+
+
+def combine_f16(y_bits: np.ndarray, w: np.ndarray, slot_idx: np.ndarray) -> np.ndarray:
+    """fp16 combine (reading R19): y and out are binary16 bit patterns."""
+    y_bits = _c(y_bits, np.uint16)
+    w = _c(w, np.float32)
+    slot_idx = _c(slot_idx, np.int32)
+    T, k = slot_idx.shape
+    H = y_bits.shape[1]
+    out = np.empty((T, H), np.uint16)
+    lib().ep_oracle_combine_f16(_p(y_bits), _p(w), _p(slot_idx), T, k, H, _p(out))
+    return out
+
+
+def combine_f16_tokens(y_bits: np.ndarray, w: np.ndarray, slot_idx: np.ndarray, tokens) -> np.ndarray:
+    y_bits = _c(y_bits, np.uint16)
+    w = _c(w, np.float32)
+    slot_idx = _c(slot_idx, np.int32)
+    tokens = _c(tokens, np.int64).reshape(-1)
+    k = slot_idx.shape[1]
+    H = y_bits.shape[1]
+    out = np.empty((tokens.size, H), np.uint16)
+    lib().ep_oracle_combine_f16_tokens(_p(y_bits), _p(w), _p(slot_idx), k, H, _p(tokens),
+                                       tokens.size, _p(out))
     return out

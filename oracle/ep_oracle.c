@@ -70,6 +70,14 @@
  *   R17 Group combine of the dedup variant: the expert side has already
  *       weighted and summed its experts' outputs into one row per (t, g);
  *       out[t] = bf16(sum of t's group rows), unit weights, rounded once.
+ *   R18 MXFP8 variant (the microscaling format gfx950's scaled matrix
+ *       instructions consume): one E8M0 scale byte per block of 32 channels,
+ *       from the OCP Microscaling (MX) v1.0 conversion: shared exponent
+ *       floor(log2(amax)) - 8, clamped to [-127, 127] (-127 for an all-zero
+ *       block); codes saturate at +-448.
+ *   R19 FP16 I/O variant: fp16 rows are dispatched as a bit copy; the fp16
+ *       combine rounds the exact weighted sum once to binary16, nearest-even,
+ *       subnormals kept, overflow to infinity.
  */
 #include <math.h>
 #include <stdint.h>
@@ -559,4 +567,141 @@ EXPORT void ep_oracle_combine_groups_tokens(const uint16_t* z, const int32_t* gr
                                             int64_t n, uint16_t* out_rows) {
     for (int64_t i = 0; i < n; ++i)
         combine_groups_one(z, group_slot, tokens[i], kg, H, out_rows + i * H);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Variants: MXFP8 dispatch and FP16 I/O ([yololab] "FP8與低精度通訊": check   */
+/* the scale's granularity and format; "Benchmark矩陣": BF16, FP16 and FP8)    */
+/* ------------------------------------------------------------------------- */
+
+/* R18.  Per block of 32 channels: amax = largest |x|; the shared exponent is
+ * se = floor(log2(amax)) - 8, where 8 is the exponent of E4M3's largest
+ * normal (448 = 1.75 * 2^8), clamped to [-127, 127]; an all-zero block takes
+ * -127.  The block's scale byte is se + 127 (E8M0: the value 2^se).  Each
+ * code is the nearest E4M3 value of clamp(x / 2^se, -448, 448), ties to even
+ * (x / 2^se is an exact power-of-two rescale; amax / 2^se lies in [256, 512),
+ * so the block's largest values may saturate at 448). */
+EXPORT void ep_oracle_quantize_token_mxfp8(const uint16_t* x_row, int32_t H, uint8_t* q_row,
+                                           uint8_t* scale_row) {
+    const int32_t B = 32;
+    for (int32_t b = 0; b < H / B; ++b) {
+        double amax = 0.0;
+        for (int32_t c = b * B; c < (b + 1) * B; ++c) {
+            double m = fabs(ep_oracle_bf16_to_double(x_row[c]));
+            if (m > amax) amax = m;
+        }
+        int se = -127;
+        if (amax > 0.0) {
+            int e;
+            frexp(amax, &e);             /* amax in [2^(e-1), 2^e): floor(log2) = e - 1 */
+            se = (e - 1) - 8;
+            if (se < -127) se = -127;
+            if (se > 127) se = 127;
+        }
+        scale_row[b] = (uint8_t)(se + 127);
+        for (int32_t c = b * B; c < (b + 1) * B; ++c) {
+            double v = ldexp(ep_oracle_bf16_to_double(x_row[c]), -se);
+            if (v > 448.0) v = 448.0;
+            if (v < -448.0) v = -448.0;
+            q_row[c] = ep_oracle_e4m3_encode((float)v);
+        }
+    }
+}
+
+EXPORT void ep_oracle_dispatch_mxfp8(const uint16_t* x, int64_t T, int32_t k, int32_t H,
+                                     const int32_t* slot_idx, uint8_t* recv_q,
+                                     uint8_t* recv_scales) {
+    int32_t nb = H / 32;
+    uint8_t* q = (uint8_t*)malloc((size_t)H);
+    uint8_t* sc = (uint8_t*)malloc((size_t)nb);
+    if (!q || !sc) { free(q); free(sc); return; }
+    for (int64_t t = 0; t < T; ++t) {
+        ep_oracle_quantize_token_mxfp8(x + t * H, H, q, sc);
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t s = slot_idx[t * k + j];
+            if (s < 0) continue;
+            memcpy(recv_q + (int64_t)s * H, q, (size_t)H);
+            memcpy(recv_scales + (int64_t)s * nb, sc, (size_t)nb);
+        }
+    }
+    free(q);
+    free(sc);
+}
+
+/* Identity expert stand-in for MXFP8 rows (harness only): the bf16 nearest to
+ * decode(q) * 2^(byte - 127), rounded once from the exact product. */
+EXPORT void ep_oracle_dequant_mxfp8(const uint8_t* q, const uint8_t* scales, int64_t R, int32_t H,
+                                    uint16_t* y) {
+    int32_t nb = H / 32;
+    for (int64_t r = 0; r < R; ++r)
+        for (int32_t c = 0; c < H; ++c)
+            y[r * H + c] = ep_oracle_bf16_from_double(
+                ep_oracle_e4m3_decode(q[r * H + c]) * ldexp(1.0, (int)scales[r * nb + c / 32] - 127));
+}
+
+/* fp16 (IEEE 754 binary16: 1 sign bit, 5 exponent bits with bias 15, 10
+ * stored significand bits) -> real number. */
+EXPORT double ep_oracle_f16_to_double(uint16_t h) {
+    int sign = h >> 15;
+    int e = (h >> 10) & 0x1F;
+    int m = h & 0x3FF;
+    double v;
+    if (e == 0) v = ldexp((double)m, -24);                  /* subnormal: m * 2^-14 / 2^10 */
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexp(1024.0 + m, e - 15 - 10);
+    return sign ? -v : v;
+}
+
+/* The binary16 value nearest to v, ties to even; magnitudes that round past
+ * the largest finite value 65504 become infinity (the default IEEE rounding).
+ * From the definition, as for bf16: the quantum of v's binade, an integer
+ * rounding with ties to even, scaled back. */
+EXPORT uint16_t ep_oracle_f16_from_double(double v) {
+    if (isnan(v)) return (uint16_t)(signbit(v) ? 0xFE00u : 0x7E00u);
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (isinf(a)) return (uint16_t)(sign | 0x7C00u);
+    if (a == 0.0) return sign;
+    double quantum;
+    if (a < ldexp(1.0, -14)) {
+        quantum = ldexp(1.0, -24);           /* subnormal spacing: 2^-14 / 2^10 */
+    } else {
+        int ex;
+        frexp(a, &ex);                       /* a in [2^(ex-1), 2^ex) */
+        quantum = ldexp(1.0, ex - 1 - 10);   /* 10 stored significand bits */
+    }
+    double r = nearbyint(a / quantum) * quantum;   /* ties to even */
+    if (r > 65504.0) return (uint16_t)(sign | 0x7C00u);
+    if (r < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+    int ex;
+    double m = frexp(r, &ex);                /* r = m * 2^ex, m in [0.5, 1) */
+    uint16_t bits = (uint16_t)(((ex - 1 + 15) << 10) | (uint16_t)(ldexp(m, 11) - 1024.0));
+    return (uint16_t)(sign | bits);
+}
+
+/* R19 fp16 combine: out[t] = f16(sum_j w[t,j] * y[slot[t,j]]) over valid
+ * pairs, each product exact in fp64 (24 + 11 significand bits), the sum in
+ * fp64, rounded once; +0 for a token with no valid pair. */
+static void combine_f16_one(const uint16_t* y, const float* w, const int32_t* slot_idx, int64_t t,
+                            int32_t k, int32_t H, uint16_t* out_row) {
+    for (int32_t c = 0; c < H; ++c) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t s = slot_idx[t * k + j];
+            if (s < 0) continue;
+            acc += (double)w[t * k + j] * ep_oracle_f16_to_double(y[(int64_t)s * H + c]);
+        }
+        out_row[c] = ep_oracle_f16_from_double(acc);
+    }
+}
+
+EXPORT void ep_oracle_combine_f16(const uint16_t* y, const float* w, const int32_t* slot_idx,
+                                  int64_t T, int32_t k, int32_t H, uint16_t* out) {
+    for (int64_t t = 0; t < T; ++t) combine_f16_one(y, w, slot_idx, t, k, H, out + t * H);
+}
+
+EXPORT void ep_oracle_combine_f16_tokens(const uint16_t* y, const float* w, const int32_t* slot_idx,
+                                         int32_t k, int32_t H, const int64_t* tokens, int64_t n,
+                                         uint16_t* out_rows) {
+    for (int64_t i = 0; i < n; ++i) combine_f16_one(y, w, slot_idx, tokens[i], k, H, out_rows + i * H);
 }

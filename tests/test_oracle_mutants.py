@@ -24,6 +24,7 @@ if os.path.dirname(HERE) not in sys.path:
 import oracle
 import test_oracle_dedup as pins_dd
 import test_oracle_dispatch_combine as pins_dc
+import test_oracle_mx_f16 as pins_mx
 import test_oracle_formats as pins_fmt
 import test_oracle_layout as pins_lay
 import test_oracle_variants as pins_var
@@ -84,6 +85,21 @@ MUTANTS = [
      "int mine = e >= 0 && e < E;"),
     ("dedup receiver weights not masked", "mine ? topk_weights[t * k + j] : 0.0f",
      "topk_weights[t * k + j]"),
+    ("MX shared exponent one too high", "se = (e - 1) - 8;", "se = e - 8;"),
+    ("MX uses 7 as E4M3's largest exponent", "se = (e - 1) - 8;", "se = (e - 1) - 7;"),
+    ("MX shared exponent not clamped below", "if (se < -127) se = -127;\n            if (se > 127)",
+     "if (se > 127)"),
+    ("MX amax of signed values", "double m = fabs(ep_oracle_bf16_to_double(x_row[c]));",
+     "double m = ep_oracle_bf16_to_double(x_row[c]);"),
+    ("MX dequant scale bias off by one", "(int)scales[r * nb + c / 32] - 127", "(int)scales[r * nb + c / 32] - 128"),
+    ("fp16 ties away from zero", "double r = nearbyint(a / quantum) * quantum;",
+     "double r = floor(a / quantum + 0.5) * quantum;"),
+    ("fp16 overflows at the largest finite value", "if (r > 65504.0)", "if (r >= 65504.0)"),
+    ("fp16 subnormal spacing", "quantum = ldexp(1.0, -24);           /* subnormal spacing",
+     "quantum = ldexp(1.0, -25);           /* subnormal spacing"),
+    ("fp16 decode exponent bias", "ldexp(1024.0 + m, e - 15 - 10)", "ldexp(1024.0 + m, e - 14 - 10)"),
+    ("fp16 combine forgets the weight", "acc += (double)w[t * k + j] * ep_oracle_f16_to_double(",
+     "acc += ep_oracle_f16_to_double("),
     ("group combine drops the last group",
      "for (int32_t i = 0; i < kg; ++i) {\n            int32_t r = group_slot[t * kg + i];",
      "for (int32_t i = 0; i < kg - 1; ++i) {\n            int32_t r = group_slot[t * kg + i];"),
@@ -128,6 +144,13 @@ def _battery():
                lambda: pins_dd.test_receiver_metadata_partitions_each_token("dsv3"),
                lambda: pins_dd.test_dedup_round_trip("tiny")]
     checks += [lambda s=s: pins_dd.test_group_layout_brute_force_tiny(s) for s in range(8)]
+    checks += [pins_mx.test_mxfp8_golden_blocks, pins_mx.test_mxfp8_error_bound_and_saturation,
+               pins_mx.test_mxfp8_dispatch_and_dequant,
+               lambda: pins_mx.test_mxfp8_shared_exponent_and_codes("dsv3"),
+               pins_mx.test_f16_golden_values, pins_mx.test_f16_rounding_against_numpy,
+               pins_mx.test_combine_f16_golden,
+               pins_mx.test_combine_f16_one_hot_is_a_gather_and_round_trip_is_exact,
+               pins_mx.test_combine_f16_is_the_rounded_exact_sum]
     return checks
 
 

@@ -1,0 +1,206 @@
+"""Pins for the oracle's MXFP8 and FP16 variants (CPU only).
+
+MXFP8 (reading R18): E4M3 codes with one E8M0 scale byte per 32 channels, the
+OCP Microscaling conversion.  Pinned by hand-worked blocks, torch's E8M0 and
+E4M3 types (an independent implementation of both formats), the shared
+exponent's defining bracket and the error bound.
+
+FP16 (reading R19): binary16 rounding and the fp16 combine.  Pinned by
+hand-worked values, numpy's float16 (decoded exhaustively, rounding on random
+values and constructed ties), and exact sums.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_moe_layout_amd import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+bf = workloads.float32_to_bf16_bits
+unbf = workloads.bf16_bits_to_float32
+
+
+def _ev(expr):
+    return float(eval(expr, {"__builtins__": {}}, {}))
+
+
+def _e4m3_values(q):
+    return torch.from_numpy(np.ascontiguousarray(q)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _e8m0_values(b):
+    return torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e8m0fnu).double().numpy()
+
+
+# --------------------------------------------------------------------------- MXFP8
+def test_mxfp8_golden_blocks():
+    with open(os.path.join(GOLDEN, "mxfp8_block.json")) as f:
+        blocks = json.load(f)["blocks"]
+    for blk in blocks:
+        x = np.zeros(32, np.float32)
+        want = np.zeros(32, np.uint8)
+        for i, (expr, code) in enumerate(blk["x"]):
+            x[i] = _ev(expr)
+            want[i] = int(code, 16)
+        assert (unbf(bf(x)) == x).all(), blk["why"]
+        q, s = oracle.quantize_token_mxfp8(bf(x))
+        assert s.tolist() == [blk["byte"]], (blk["why"], s)
+        assert (q == want).all(), (blk["why"], [(i, hex(a), hex(b)) for i, (a, b) in enumerate(zip(q, want)) if a != b])
+
+
+def _mx_rows(name, T=24):
+    wl = workloads.make(name, T=T)
+    rows = [wl.x_bits[t] for t in range(wl.T)]
+    # blocks with wide dynamic range, exact powers of two and near-powers, tiny and zero blocks
+    g = np.random.default_rng(5)
+    H = wl.H
+    for scale in (2.0 ** -120, 2.0 ** -60, 1e-3, 1.0, 255.75, 448.0, 3.0e5, 2.0 ** 100):
+        r = (g.standard_normal(H) * scale).astype(np.float32)
+        r[::37] = 0.0
+        r[1::32] = scale                      # block maxima on the scale itself
+        rows.append(bf(r))
+    rows.append(np.zeros(H, np.uint16))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("name", ["dsv3", "large"])
+def test_mxfp8_shared_exponent_and_codes(name):
+    rows = _mx_rows(name)
+    H = rows.shape[1]
+    for r in rows:
+        q, s = oracle.quantize_token_mxfp8(r)
+        x = unbf(r).astype(np.float64).reshape(H // 32, 32)
+        amax = np.abs(x).max(1)
+        X = _e8m0_values(s)                                   # torch's E8M0 decode: 2**(b - 127)
+        assert (X == np.ldexp(1.0, s.astype(np.int64) - 127)).all()
+        live = amax >= 2.0 ** -119                            # no clamp at -127 for these
+        assert (amax[live] / X[live] >= 256).all() and (amax[live] / X[live] < 512).all()
+        assert (s[(amax > 0) & ~live] == 0).all() and (s[amax == 0] == 0).all()
+        # codes: torch's E4M3 cast of the exact rescale, clamped
+        v = np.clip(x / X[:, None], -448, 448).astype(np.float32).reshape(-1)
+        ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert (q == ref).all()
+
+
+def test_mxfp8_error_bound_and_saturation():
+    rows = _mx_rows("dsv3")
+    H = rows.shape[1]
+    for r in rows:
+        q, s = oracle.quantize_token_mxfp8(r)
+        x = unbf(r).astype(np.float64).reshape(H // 32, 32)
+        X = _e8m0_values(s)[:, None]
+        got = _e4m3_values(q).reshape(H // 32, 32) * X
+        inside = np.abs(x) <= 448 * X
+        err = np.abs(got - x)
+        # half an E4M3 ulp: 2**-4 relative for normals, 2**-10 * X for subnormals
+        assert (err[inside] <= (2.0 ** -4 * np.abs(x) + 2.0 ** -10 * X)[inside]).all()
+        # above 448 * X the code saturates at +-448
+        assert (np.abs(got[~inside]) == 448 * np.broadcast_to(X, x.shape)[~inside]).all()
+        assert (np.sign(got[~inside]) == np.sign(x[~inside])).all()
+
+
+def test_mxfp8_dispatch_and_dequant():
+    wl = workloads.make("dsv3", T=16, H=256)
+    lay = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
+    R = lay["num_recv_rows"]
+    q, s = oracle.dispatch_mxfp8(wl.x_bits, lay["slot_idx"], R)
+    for t in range(wl.T):
+        tq, ts = oracle.quantize_token_mxfp8(wl.x_bits[t])
+        for slot in lay["slot_idx"][t]:
+            assert (q[slot] == tq).all() and (s[slot] == ts).all()
+    y = oracle.dequant_mxfp8(q, s)
+    # the product decode(q) * 2**(b - 127) is exact in fp32 here, so torch's
+    # single fp32 -> bf16 rounding is the reference
+    prod = (_e4m3_values(q) * np.repeat(_e8m0_values(s), 32, axis=1)).astype(np.float32)
+    ref = torch.from_numpy(prod).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (y == ref).all()
+
+
+# --------------------------------------------------------------------------- FP16
+def _f16():
+    with open(os.path.join(GOLDEN, "f16_values.json")) as f:
+        return json.load(f)
+
+
+def test_f16_golden_values():
+    g = _f16()
+    for expr, bits, why in g["round"]:
+        assert oracle.f16_from_double(_ev(expr)) == int(bits, 16), (expr, why)
+    for bits, expr in g["decode"]:
+        assert oracle.f16_to_double(int(bits, 16)) == _ev(expr), (bits, expr)
+
+
+def test_f16_decode_exhaustive_against_numpy():
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = pats.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_double(int(p)) for p in pats])
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == ref[~nan]).all()
+    assert (np.signbit(got[~nan]) == np.signbit(ref[~nan])).all()
+
+
+def test_f16_rounding_against_numpy():
+    g = np.random.default_rng(3)
+    vals = list(g.standard_normal(20000) * np.exp2(g.integers(-30, 18, 20000)))
+    # exact midpoints between neighbouring binary16 values, and their neighbours
+    pats = g.integers(0, 0x7BFF, 4000).astype(np.uint16)
+    lo = pats.view(np.float16).astype(np.float64)
+    hi = (pats + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    mid = (lo + hi) / 2
+    vals += list(mid) + list(-mid) + list(np.nextafter(mid, 0)) + list(np.nextafter(mid, np.inf))
+    vals += [65504.0, 65519.999, 65520.0, 70000.0, 1e300, 2.0 ** -24, 2.0 ** -25, 2.0 ** -26, 0.0, -0.0]
+    vals = np.array(vals, np.float64)
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f16_from_double(v) for v in vals], np.uint16)
+    assert (got == ref).all(), vals[got != ref][:5]
+
+
+def test_combine_f16_golden():
+    c = _f16()["combine"]
+    out = oracle.combine_f16(np.array(c["y"], np.uint16), np.array(c["w"], np.float32),
+                             np.array(c["slot_idx"], np.int32))
+    assert out.tolist() == c["out"], c["why"]
+
+
+def test_combine_f16_one_hot_is_a_gather_and_round_trip_is_exact():
+    g = np.random.default_rng(8)
+    R, H, T, k = 40, 64, 10, 4
+    y = (g.standard_normal((R, H)) * 100).astype(np.float16).view(np.uint16)
+    slot = g.integers(-1, R, size=(T, k)).astype(np.int32)
+    slot[:, 0] = g.integers(0, R, T)
+    w = np.zeros((T, k), np.float32)
+    w[:, 0] = 1.0
+    assert (oracle.combine_f16(y, w, slot) == y[slot[:, 0]]).all()
+    # the same row under weights that sum to 1 exactly: the row itself
+    same = np.repeat(slot[:, :1], k, axis=1)
+    w2 = np.tile(np.array([0.5, 0.25, 0.125, 0.125], np.float32), (T, 1))
+    out = oracle.combine_f16(y, w2, same)
+    assert ((out & 0x7FFF) == (y[slot[:, 0]] & 0x7FFF)).all()
+
+
+def test_combine_f16_is_the_rounded_exact_sum():
+    """Weights with few significant bits and values in a narrow binade range
+    make every fp64 sum exact; numpy's float16 rounding of it is the reference."""
+    g = np.random.default_rng(9)
+    R, H, T, k = 30, 48, 12, 6
+    y = (g.standard_normal((R, H)) * 8).astype(np.float16).view(np.uint16)
+    slot = g.integers(-1, R, size=(T, k)).astype(np.int32)
+    w = (g.integers(-64, 65, size=(T, k)) / 64.0).astype(np.float32)
+    out = oracle.combine_f16(y, w, slot)
+    yv = y.view(np.float16)
+    for t in range(T):
+        for c in range(H):
+            acc = Fraction(0)
+            for j in range(k):
+                if slot[t, j] >= 0:
+                    acc += Fraction(float(w[t, j])) * Fraction(float(yv[slot[t, j], c]))
+            exact = float(acc)
+            assert Fraction(exact) == acc
+            assert out[t, c] == np.float16(exact).view(np.uint16) or (exact == 0 and out[t, c] == 0)
