@@ -18,6 +18,9 @@ EP_OK = 0
 EP_BF16 = 0
 EP_FP8_E4M3 = 1
 EP_FP8_E4M3_POW2 = 2
+EP_MXFP8_E4M3 = 3
+EP_F16 = 4
+_FP8_DTYPES = (EP_FP8_E4M3, EP_FP8_E4M3_POW2, EP_MXFP8_E4M3)
 EP_FLAG_BAD_EXPERT = 1
 EP_FLAG_OVERFLOW = 2
 EP_MAX_EXPERTS = 1024
@@ -60,6 +63,8 @@ SIGNATURES = {
     "ep_layout_dispatch": (ctypes.c_int, [_vp, _LP, _vp, _sz, _vp, _i32, _i32, _vp, _vp, _vp]),
     "ep_combine": (ctypes.c_int, [_vp, _vp, _LP, _i32, _vp, _vp]),
     "ep_combine_fp8": (ctypes.c_int, [_vp, _vp, _vp, _LP, _i32, _vp, _vp]),
+    "ep_combine_f16": (ctypes.c_int, [_vp, _vp, _LP, _i32, _vp, _vp]),
+    "ep_dequant_mxfp8": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp]),
     "ep_group_layout_init": (ctypes.c_int, [_LP, _i64, _i32, _i32]),
     "ep_group_layout_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "ep_get_group_layout": (ctypes.c_int, [_vp, _vp, _i32, _i32, _LP, _vp, _vp, _vp, _sz, _vp]),
@@ -203,17 +208,29 @@ def ep_get_layout(topk_idx: torch.Tensor, layout: EpLayout, stream=None) -> EpLa
     return layout
 
 
+def _dispatch_types(recv_dtype: int):
+    """(x dtype, recv_x dtype, recv_scales dtype) of a receive dtype."""
+    if recv_dtype == EP_F16:
+        return torch.float16, torch.float16, None
+    if recv_dtype == EP_MXFP8_E4M3:
+        return torch.bfloat16, torch.uint8, torch.uint8
+    if recv_dtype in _FP8_DTYPES:
+        return torch.bfloat16, torch.uint8, torch.float32
+    return torch.bfloat16, torch.bfloat16, None
+
+
 def ep_dispatch(x: torch.Tensor, layout: EpLayout, recv_dtype: int, recv_x: torch.Tensor,
                 recv_scales: torch.Tensor | None = None, stream=None) -> None:
-    """x bf16 [T, H] -> recv_x (bf16 [R, H], or uint8 [R, H] FP8 codes with
-    recv_scales fp32 [R, H/128])."""
+    """x bf16 [T, H] -> recv_x: bf16 [R, H]; uint8 [R, H] FP8 codes with
+    recv_scales fp32 [R, H/128] (EP_FP8_E4M3, EP_FP8_E4M3_POW2) or uint8
+    [R, H/32] E8M0 bytes (EP_MXFP8_E4M3).  EP_F16: x and recv_x fp16."""
     T, H = layout.num_tokens, x.shape[-1]
     if tuple(x.shape) != (T, H) or recv_x.shape[0] != layout.num_recv_rows or recv_x.shape[-1] != H:
         raise ValueError("dispatch buffers do not match the layout")
-    want = torch.bfloat16 if recv_dtype == EP_BF16 else torch.uint8
+    xt, rt, st = _dispatch_types(recv_dtype)
     _check("ep_dispatch", lib().ep_dispatch(
-        _ptr(x, "x", torch.bfloat16), ctypes.byref(layout.struct), H, recv_dtype,
-        _ptr(recv_x, "recv_x", want), _ptr(recv_scales, "recv_scales", torch.float32),
+        _ptr(x, "x", xt), ctypes.byref(layout.struct), H, recv_dtype,
+        _ptr(recv_x, "recv_x", rt), _ptr(recv_scales, "recv_scales", st),
         _stream(stream)))
 
 
@@ -226,12 +243,12 @@ def ep_layout_dispatch(topk_idx: torch.Tensor, layout: EpLayout, x: torch.Tensor
         raise ValueError("topk_idx shape %s does not match the layout" % (tuple(topk_idx.shape),))
     if tuple(x.shape) != (T, H) or recv_x.shape[0] != layout.num_recv_rows or recv_x.shape[-1] != H:
         raise ValueError("dispatch buffers do not match the layout")
-    want = torch.bfloat16 if recv_dtype == EP_BF16 else torch.uint8
+    xt, rt, st = _dispatch_types(recv_dtype)
     _check("ep_layout_dispatch", lib().ep_layout_dispatch(
         _ptr(topk_idx, "topk_idx", torch.int64) if topk_idx.numel() else None,
         ctypes.byref(layout.struct), layout.workspace.data_ptr(), layout.workspace.numel(),
-        _ptr(x, "x", torch.bfloat16), H, recv_dtype, _ptr(recv_x, "recv_x", want),
-        _ptr(recv_scales, "recv_scales", torch.float32), _stream(stream)))
+        _ptr(x, "x", xt), H, recv_dtype, _ptr(recv_x, "recv_x", rt),
+        _ptr(recv_scales, "recv_scales", st), _stream(stream)))
     return layout
 
 
@@ -246,6 +263,19 @@ def ep_combine(expert_out: torch.Tensor, topk_weights: torch.Tensor, layout: EpL
     _check("ep_combine", lib().ep_combine(
         _ptr(expert_out, "expert_out", torch.bfloat16), _ptr(topk_weights, "topk_weights", torch.float32),
         ctypes.byref(layout.struct), H, _ptr(out, "out", torch.bfloat16), _stream(stream)))
+
+
+def ep_combine_f16(expert_out: torch.Tensor, topk_weights: torch.Tensor, layout: EpLayout,
+                   out: torch.Tensor, stream=None) -> None:
+    """expert_out fp16 [R, H], topk_weights fp32 [T, k] -> out fp16 [T, H]."""
+    H = expert_out.shape[-1]
+    if (expert_out.shape[0] != layout.num_recv_rows
+            or tuple(topk_weights.shape) != (layout.num_tokens, layout.num_topk)
+            or tuple(out.shape) != (layout.num_tokens, H)):
+        raise ValueError("combine buffers do not match the layout")
+    _check("ep_combine_f16", lib().ep_combine_f16(
+        _ptr(expert_out, "expert_out", torch.float16), _ptr(topk_weights, "topk_weights", torch.float32),
+        ctypes.byref(layout.struct), H, _ptr(out, "out", torch.float16), _stream(stream)))
 
 
 def ep_combine_fp8(expert_q: torch.Tensor, expert_scales: torch.Tensor, topk_weights: torch.Tensor,
@@ -308,6 +338,15 @@ def ep_dequant_fp8(q: torch.Tensor, scales: torch.Tensor, y: torch.Tensor, strea
         raise ValueError("dequant buffers disagree")
     _check("ep_dequant_fp8", lib().ep_dequant_fp8(
         _ptr(q, "q", torch.uint8), _ptr(scales, "scales", torch.float32), rows, H,
+        _ptr(y, "y", torch.bfloat16), _stream(stream)))
+
+
+def ep_dequant_mxfp8(q: torch.Tensor, scales: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    rows, H = q.shape
+    if tuple(y.shape) != (rows, H) or tuple(scales.shape) != (rows, H // 32):
+        raise ValueError("dequant buffers disagree")
+    _check("ep_dequant_mxfp8", lib().ep_dequant_mxfp8(
+        _ptr(q, "q", torch.uint8), _ptr(scales, "scales", torch.uint8), rows, H,
         _ptr(y, "y", torch.bfloat16), _stream(stream)))
 
 

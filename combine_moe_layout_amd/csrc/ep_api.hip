@@ -54,10 +54,10 @@ int check_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* w
 
 // Checks shared by ep_dispatch and ep_layout_dispatch (after the layout's).
 int check_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,
-                   void* recv_x, float* recv_scales) {
-  if (recv_dtype != EP_BF16 && recv_dtype != EP_FP8_E4M3 && recv_dtype != EP_FP8_E4M3_POW2)
+                   void* recv_x, void* recv_scales) {
+  if (recv_dtype != EP_BF16 && recv_dtype != EP_F16 && !ep::dtype_is_fp8(recv_dtype))
     return EP_ERR_DTYPE;
-  const bool fp8 = recv_dtype != EP_BF16;
+  const bool fp8 = ep::dtype_is_fp8(recv_dtype);
   if (hidden < 8 || hidden > EP_MAX_HIDDEN || hidden % 8 != 0 || (fp8 && hidden % 128 != 0))
     return EP_ERR_SHAPE;
   if (layout->num_tokens == 0) return EP_OK;
@@ -108,7 +108,7 @@ int ep_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* work
 }
 
 int ep_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,
-                void* recv_x, float* recv_scales, void* stream) {
+                void* recv_x, void* recv_scales, void* stream) {
   int rc = check_layout(layout);
   if (rc != EP_OK) return rc;
   rc = check_dispatch(x, layout, hidden, recv_dtype, recv_x, recv_scales);
@@ -119,7 +119,7 @@ int ep_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_
 
 int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
                        size_t workspace_bytes, const void* x, int32_t hidden, int32_t recv_dtype,
-                       void* recv_x, float* recv_scales, void* stream) {
+                       void* recv_x, void* recv_scales, void* stream) {
   int rc = check_get_layout(topk_idx, layout, workspace, workspace_bytes);
   if (rc != EP_OK) return rc;
   rc = check_dispatch(x, layout, hidden, recv_dtype, recv_x, recv_scales);
@@ -145,6 +145,20 @@ int ep_combine(const void* expert_out, const float* topk_weights, const ep_layou
     return EP_ERR_ALIGN;
   return launch_status(ep::launch_combine(expert_out, topk_weights, *layout, hidden, out,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine_f16(const void* expert_out, const float* topk_weights, const ep_layout_t* layout,
+                   int32_t hidden, void* out, void* stream) {
+  int rc = check_layout(layout);
+  if (rc != EP_OK) return rc;
+  if (hidden < 8 || hidden > EP_MAX_HIDDEN || hidden % 8 != 0) return EP_ERR_SHAPE;
+  if (layout->num_tokens == 0) return EP_OK;
+  if (expert_out == nullptr || topk_weights == nullptr || out == nullptr) return EP_ERR_NULL;
+  if (!aligned16(expert_out) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(topk_weights) & 3u) != 0)
+    return EP_ERR_ALIGN;
+  return launch_status(ep::launch_combine_f16(expert_out, topk_weights, *layout, hidden, out,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int ep_combine_fp8(const uint8_t* expert_q, const float* expert_scales,
@@ -235,6 +249,17 @@ int ep_dequant_fp8(const uint8_t* q, const float* scales, int64_t rows, int32_t 
     return EP_ERR_ALIGN;
   return launch_status(
       ep::launch_dequant_fp8(q, scales, rows, hidden, y, static_cast<hipStream_t>(stream)));
+}
+
+int ep_dequant_mxfp8(const uint8_t* q, const uint8_t* scales, int64_t rows, int32_t hidden,
+                     void* y, void* stream) {
+  if (rows < 0 || hidden < 128 || hidden > EP_MAX_HIDDEN || hidden % 128 != 0)
+    return EP_ERR_SHAPE;
+  if (rows == 0) return EP_OK;
+  if (q == nullptr || scales == nullptr || y == nullptr) return EP_ERR_NULL;
+  if (!aligned16(q) || !aligned16(y)) return EP_ERR_ALIGN;
+  return launch_status(
+      ep::launch_dequant_mxfp8(q, scales, rows, hidden, y, static_cast<hipStream_t>(stream)));
 }
 
 int ep_cast_e4m3_bits(uint32_t first, int64_t n, int32_t method, uint8_t* out, void* stream) {

@@ -87,6 +87,46 @@ hipError_t launch_dequant_fp8(const uint8_t* q, const float* scales, int64_t row
   return hipGetLastError();
 }
 
+// y = bf16 of decode(q) * 2^(byte - 127) for MXFP8 rows (one E8M0 byte per
+// 32 channels): the product of a 4-significant-bit code and a power of two
+// between 2^-127 and 2^119 is exact in fp32 (subnormal results included), so
+// one rounding to bf16 gives the nearest value.
+__global__ __launch_bounds__(256) void dequant_mxfp8_kernel(const u32x4* __restrict__ q,
+                                                            const uint8_t* __restrict__ scales,
+                                                            int64_t units, int32_t units_per_row,
+                                                            int32_t blocks_per_row,
+                                                            u32x4* __restrict__ y) {
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = u / units_per_row;
+    const int32_t c16 = (int32_t)(u % units_per_row);
+    const int32_t e = (int32_t)scales[r * blocks_per_row + c16 / 2] - 127;
+    const u32x4 codes = q[u];
+    const uint32_t words[4] = {codes.x, codes.y, codes.z, codes.w};
+    uint32_t outw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t word = words[i / 2];
+      const int sh = (i % 2) * 16;
+      const float a = ldexpf(e4m3_decode((word >> sh) & 0xFFu), e);
+      const float b = ldexpf(e4m3_decode((word >> (sh + 8)) & 0xFFu), e);
+      outw[i] = bf16_rne(a) | (bf16_rne(b) << 16);
+    }
+    y[2 * u] = u32x4{outw[0], outw[1], outw[2], outw[3]};
+    y[2 * u + 1] = u32x4{outw[4], outw[5], outw[6], outw[7]};
+  }
+}
+
+hipError_t launch_dequant_mxfp8(const uint8_t* q, const uint8_t* scales, int64_t rows,
+                                int32_t hidden, void* y, hipStream_t stream) {
+  const int64_t units = rows * (int64_t)(hidden / 16);
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_mxfp8_kernel, dim3(grid_for(units, 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(q), scales, units, hidden / 16, hidden / 32,
+                     static_cast<u32x4*>(y));
+  return hipGetLastError();
+}
+
 hipError_t launch_cast_e4m3_bits(uint32_t first, int64_t n, int32_t method, uint8_t* out,
                                  hipStream_t stream) {
   if (n == 0) return hipSuccess;

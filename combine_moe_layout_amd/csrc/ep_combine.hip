@@ -26,16 +26,43 @@ struct CombineMap {
   int32_t tokens_per_block;
 };
 
+// Rows hold 2-byte elements: bf16, or IEEE fp16 when kF16 (decoded exactly
+// by the conversion instruction; results rounded to nearest-even by it, with
+// fp16 subnormals kept and overflow to infinity).
+template <bool kF16>
+__device__ __forceinline__ float elem_lo(uint32_t w) {
+  if constexpr (kF16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+  else return bf16_lo(w);
+}
+
+template <bool kF16>
+__device__ __forceinline__ float elem_hi(uint32_t w) {
+  if constexpr (kF16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  else return bf16_hi(w);
+}
+
+template <bool kF16>
+__device__ __forceinline__ uint32_t pack_elem2(float a, float b) {
+  if constexpr (kF16)
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+  else
+    return pack_bf16x2(a, b);
+}
+
+template <bool kF16 = false>
 __device__ __forceinline__ void accumulate8(float* acc, const u32x4& d, float w, bool valid) {
-  const float f[8] = {bf16_lo(d.x), bf16_hi(d.x), bf16_lo(d.y), bf16_hi(d.y),
-                      bf16_lo(d.z), bf16_hi(d.z), bf16_lo(d.w), bf16_hi(d.w)};
+  const float f[8] = {elem_lo<kF16>(d.x), elem_hi<kF16>(d.x), elem_lo<kF16>(d.y),
+                      elem_hi<kF16>(d.y), elem_lo<kF16>(d.z), elem_hi<kF16>(d.z),
+                      elem_lo<kF16>(d.w), elem_hi<kF16>(d.w)};
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = valid ? fmaf(w, f[i], acc[i]) : acc[i];
 }
 
+template <bool kF16 = false>
 __device__ __forceinline__ u32x4 pack8(const float* acc) {
-  return u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-               pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  return u32x4{pack_elem2<kF16>(acc[0], acc[1]), pack_elem2<kF16>(acc[2], acc[3]),
+               pack_elem2<kF16>(acc[4], acc[5]), pack_elem2<kF16>(acc[6], acc[7])};
 }
 
 // Token and lane of this thread.  kWhole: one token per workgroup, so the token
@@ -55,8 +82,8 @@ __device__ __forceinline__ bool combine_token(const CombineMap& m, int64_t num_t
 
 // K > 0: compile-time top-k.  K == 0: any top-k, one row at a time.
 // kUnit: every weight is 1 and w is not read (the group combine of the dedup
-// variant, whose rows arrive already weighted).
-template <int K, bool kUnit>
+// variant, whose rows arrive already weighted).  kF16: fp16 rows and output.
+template <int K, bool kUnit, bool kF16 = false>
 __global__ __launch_bounds__(1024) void combine_kernel(
     const u32x4* __restrict__ y, const float* __restrict__ w,
     const int32_t* __restrict__ slot_idx, int64_t num_tokens, int32_t k, int32_t hidden,
@@ -95,8 +122,8 @@ __global__ __launch_bounds__(1024) void combine_kernel(
       }
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < K; ++j) accumulate8(acc, d[j], ww[j], s[j] >= 0);
-      store_nt(dst + v, pack8(acc));
+      for (int j = 0; j < K; ++j) accumulate8<kF16>(acc, d[j], ww[j], s[j] >= 0);
+      store_nt(dst + v, pack8<kF16>(acc));
     }
   } else {
     for (int32_t v = lt; v < vec_per_row; v += m.lanes_per_token) {
@@ -104,9 +131,10 @@ __global__ __launch_bounds__(1024) void combine_kernel(
       for (int32_t j = 0; j < k; ++j) {
         const int32_t sj = slots[j];
         if (sj < 0) continue;
-        accumulate8(acc, load_nt(y + (int64_t)sj * vec_per_row + v), kUnit ? 1.0f : wt[j], true);
+        accumulate8<kF16>(acc, load_nt(y + (int64_t)sj * vec_per_row + v), kUnit ? 1.0f : wt[j],
+                          true);
       }
-      store_nt(dst + v, pack8(acc));
+      store_nt(dst + v, pack8<kF16>(acc));
     }
   }
 }
@@ -132,15 +160,15 @@ static CombineMap combine_map(int32_t vecs_per_row) {
 // token per workgroup): its slots and weights then arrive as per-lane vector
 // loads, which measured about 4% faster here than the scalar loads of the
 // uniform-token form (179 vs 187 us at 8192 tokens x 7168, top-8).
-template <int K, bool kUnit>
+template <int K, bool kUnit, bool kF16>
 static void launch_k(dim3 grid, dim3 block, hipStream_t stream, const void* y, const float* w,
                      const ep_layout_t& L, int32_t hidden, CombineMap m, void* out) {
-  hipLaunchKernelGGL((combine_kernel<K, kUnit>), grid, block, 0, stream,
+  hipLaunchKernelGGL((combine_kernel<K, kUnit, kF16>), grid, block, 0, stream,
                      static_cast<const u32x4*>(y), w, L.slot_idx, L.num_tokens, L.num_topk,
                      hidden, m, static_cast<u32x4*>(out));
 }
 
-template <bool kUnit>
+template <bool kUnit, bool kF16 = false>
 static hipError_t launch_combine_weights(const void* y, const float* w, const ep_layout_t& L,
                                          int32_t hidden, void* out, hipStream_t stream) {
   const int64_t T = L.num_tokens;
@@ -149,15 +177,15 @@ static hipError_t launch_combine_weights(const void* y, const float* w, const ep
   const dim3 grid((unsigned)((T + m.tokens_per_block - 1) / m.tokens_per_block));
   const dim3 block(m.lanes_per_token * m.tokens_per_block);
   switch (L.num_topk) {
-    case 1: launch_k<1, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 2: launch_k<2, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 3: launch_k<3, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 4: launch_k<4, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 5: launch_k<5, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 6: launch_k<6, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 7: launch_k<7, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
-    case 8: launch_k<8, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
-    default: launch_k<0, kUnit>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 1: launch_k<1, kUnit, kF16>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 2: launch_k<2, kUnit, kF16>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 3: launch_k<3, kUnit, kF16>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 4: launch_k<4, kUnit, kF16>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 5: launch_k<5, kUnit, kF16>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 6: launch_k<6, kUnit, kF16>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 7: launch_k<7, kUnit, kF16>(grid, block, stream, y, w, L, hidden, m, out); break;
+    case 8: launch_k<8, kUnit, kF16>(grid, block, stream, y, w, L, hidden, m, out); break;
+    default: launch_k<0, kUnit, kF16>(grid, block, stream, y, w, L, hidden, m, out); break;
   }
   return hipGetLastError();
 }
@@ -170,6 +198,11 @@ hipError_t launch_combine(const void* y, const float* w, const ep_layout_t& L, i
 hipError_t launch_combine_groups(const void* z, const ep_layout_t& GL, int32_t hidden, void* out,
                                  hipStream_t stream) {
   return launch_combine_weights<true>(z, nullptr, GL, hidden, out, stream);
+}
+
+hipError_t launch_combine_f16(const void* y, const float* w, const ep_layout_t& L,
+                              int32_t hidden, void* out, hipStream_t stream) {
+  return launch_combine_weights<false, true>(y, w, L, hidden, out, stream);
 }
 
 // ---------------------------------------------------------------------------

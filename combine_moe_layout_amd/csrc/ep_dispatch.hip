@@ -1,6 +1,6 @@
 // ep_dispatch.hip -- MoE dispatch on gfx950: token rows -> expert-ordered
-// receive rows, as a bf16 bit copy or as OCP FP8 E4M3 codes with one fp32
-// scale per 128 channels.
+// receive rows, as a bf16 / fp16 bit copy, or as OCP FP8 E4M3 codes with one
+// fp32 scale per 128 channels or one E8M0 scale per 32 channels (MXFP8).
 //
 // What it computes: every (token, k) pair with a receive row gets a copy of
 // the token's hidden state ("DeepEP是什麼？…" (yololab.net), section
@@ -57,18 +57,18 @@ __global__ __launch_bounds__(1024) void dispatch_bf16_kernel(
 // staged in LDS and written afterwards row by row by consecutive lanes, so each
 // receive row's scales leave as one contiguous run instead of 4-byte pieces
 // from separate waves.
-template <bool kHw, bool kPow2>
+template <bool kHw, int kMode>
 __global__ __launch_bounds__(1024) void dispatch_fp8_kernel(
     const u32x4* __restrict__ x, int64_t num_tokens, int32_t k, int32_t hidden, TokenMap m,
-    const int32_t* __restrict__ slot_idx, u32x4* __restrict__ recv, float* __restrict__ scales) {
-  __shared__ float s_scale[kMaxScalesPerBlock];
+    const int32_t* __restrict__ slot_idx, u32x4* __restrict__ recv, uint32_t* __restrict__ scales) {
+  __shared__ uint32_t s_scale[kMaxScalesPerBlock];
   int64_t t;
   int32_t lt;
   token_of_thread(m, t, lt);
   const int32_t tok_in_block = m.tokens_per_block == 1 ? 0 : threadIdx.x / m.lanes_per_token;
-  float* my_scales = s_scale + tok_in_block * (hidden / kFp8Block);
+  uint32_t* my_scales = s_scale + tok_in_block * (hidden / kFp8Block);
   if (t < num_tokens)  // whole 8-lane groups share t
-    fp8_token_codes<kHw, kPow2>(x + t * (hidden / 8), hidden, lt, m.lanes_per_token,
+    fp8_token_codes<kHw, kMode>(x + t * (hidden / 8), hidden, lt, m.lanes_per_token,
                                 slot_idx + t * k, k, recv, my_scales);
   __syncthreads();
   if (t < num_tokens)
@@ -94,22 +94,26 @@ static TokenMap token_map(int32_t vecs_per_row) {
 }
 
 hipError_t launch_dispatch(const void* x, const ep_layout_t& L, int32_t hidden, int32_t dtype,
-                           void* recv_x, float* recv_scales, hipStream_t stream) {
+                           void* recv_x, void* recv_scales, hipStream_t stream) {
   const int64_t T = L.num_tokens;
   if (T == 0) return hipSuccess;
-  const bool fp8 = dtype != EP_BF16;
+  const bool fp8 = dtype_is_fp8(dtype);
+  uint32_t* sw = static_cast<uint32_t*>(recv_scales);
   const TokenMap m = token_map(fp8 ? hidden / 16 : hidden / 8);
   const dim3 grid((unsigned)((T + m.tokens_per_block - 1) / m.tokens_per_block));
   const dim3 block(m.lanes_per_token * m.tokens_per_block);
   const u32x4* xv = static_cast<const u32x4*>(x);
   u32x4* rv = static_cast<u32x4*>(recv_x);
   if (dtype == EP_FP8_E4M3)
-    hipLaunchKernelGGL((dispatch_fp8_kernel<kDispatchUsesHwCast, false>), grid, block, 0, stream,
-                       xv, T, L.num_topk, hidden, m, L.slot_idx, rv, recv_scales);
+    hipLaunchKernelGGL((dispatch_fp8_kernel<kDispatchUsesHwCast, kScaleF32>), grid, block, 0,
+                       stream, xv, T, L.num_topk, hidden, m, L.slot_idx, rv, sw);
   else if (dtype == EP_FP8_E4M3_POW2)
-    hipLaunchKernelGGL((dispatch_fp8_kernel<kDispatchUsesHwCast, true>), grid, block, 0, stream,
-                       xv, T, L.num_topk, hidden, m, L.slot_idx, rv, recv_scales);
-  else
+    hipLaunchKernelGGL((dispatch_fp8_kernel<kDispatchUsesHwCast, kScalePow2>), grid, block, 0,
+                       stream, xv, T, L.num_topk, hidden, m, L.slot_idx, rv, sw);
+  else if (dtype == EP_MXFP8_E4M3)
+    hipLaunchKernelGGL((dispatch_fp8_kernel<kDispatchUsesHwCast, kScaleMx>), grid, block, 0,
+                       stream, xv, T, L.num_topk, hidden, m, L.slot_idx, rv, sw);
+  else  // EP_BF16 and EP_F16: a bit copy of 2-byte elements
     hipLaunchKernelGGL(dispatch_bf16_kernel, grid, block, 0, stream, xv, T, L.num_topk, hidden, m,
                        L.slot_idx, rv);
   return hipGetLastError();

@@ -11,8 +11,15 @@
 
 namespace ep {
 
-// Scales of one token fit in LDS: hidden <= EP_MAX_HIDDEN gives at most 512.
+// Scales of one token fit in LDS: hidden <= EP_MAX_HIDDEN gives at most 512
+// scale words (one 4-byte word per 128 channels in every scale format).
 constexpr int kMaxScalesPerBlock = EP_MAX_HIDDEN / kFp8Block;
+
+// Scale formats of FP8 dispatch.  kScaleF32 / kScalePow2: one fp32 scale per
+// 128 channels.  kScaleMx: MXFP8, one E8M0 byte per 32 channels, i.e. four
+// bytes (one word) per 128 channels, so the scale rows have the same size and
+// the same word-wise store pattern in every format.
+enum ScaleMode : int { kScaleF32 = 0, kScalePow2 = 1, kScaleMx = 2 };
 
 // bf16: 8 channels (one 16-byte vector) per lane and step, copied to every
 // valid row with non-temporal stores (the rows are written once).
@@ -29,10 +36,6 @@ __device__ __forceinline__ void bf16_token_copy(const u32x4* __restrict__ src, i
   }
 }
 
-// FP8 codes of one 16-channel slice (vector v of the code row: bf16 vectors
-// 2v and 2v+1 given in lo / hi), stored to every valid row; the 8 lanes of a
-// 128-channel block must call it together (their maximum is reduced with lane
-// swizzles).  The block scale goes to my_scales[v / 8].
 // The block scale and its reciprocal.  kPow2 = false: scale = a / 448 and
 // inv = 448 / a, single correctly rounded fp32 divisions.  kPow2 = true: the
 // smallest power of two s with 448 * s >= a: with a = (1 + m) * 2^ea and
@@ -52,11 +55,31 @@ __device__ __forceinline__ void fp8_block_scale(float a, float& scale, float& in
   }
 }
 
-template <bool kHw, bool kPow2 = false>
+// MXFP8 shared exponent of a 32-channel block (the OCP Microscaling
+// conversion): se = floor(log2(amax)) - 8, where 8 is the exponent of E4M3's
+// largest normal (448 = 1.75 * 2^8), clamped to [-127, 127].  For amax >= 0
+// floor(log2(amax)) is the biased exponent field minus 127; a zero or fp32
+// subnormal maximum (field 0) lies below 2^-126 and clamps to -127, and the
+// largest finite amax gives 119, so only the lower clamp can act.  Returns the
+// E8M0 byte se + 127 and sets inv = 2^-se (a normal fp32 power of two).
+__device__ __forceinline__ uint32_t mx_block_scale(float amax, float& inv) {
+  const int32_t field = (int32_t)(__float_as_uint(amax) >> 23);
+  const int32_t se = field == 0 ? -127 : (field - 135 < -127 ? -127 : field - 135);
+  inv = __uint_as_float((uint32_t)(127 - se) << 23);
+  return (uint32_t)(se + 127);
+}
+
+// FP8 codes of one 16-channel slice (vector v of the code row: bf16 vectors
+// 2v and 2v+1 given in lo / hi), stored to every valid row; the lanes of one
+// scale block must call it together (their maximum is reduced with lane
+// swizzles: 8 lanes per 128-channel block, 2 lanes per 32-channel MX block).
+// The block's scale word goes to word v / 8 of my_scales (MX: the block's
+// E8M0 byte to byte v / 2).
+template <bool kHw, int kMode = kScaleF32>
 __device__ __forceinline__ void fp8_vector_codes(const u32x4& lo, const u32x4& hi, int32_t v,
                                                  const int32_t* slots, int32_t k,
                                                  u32x4* __restrict__ recv,
-                                                 int32_t out_vec_per_row, float* my_scales) {
+                                                 int32_t out_vec_per_row, uint32_t* my_scales) {
   float f[16] = {bf16_lo(lo.x), bf16_hi(lo.x), bf16_lo(lo.y), bf16_hi(lo.y),
                  bf16_lo(lo.z), bf16_hi(lo.z), bf16_lo(lo.w), bf16_hi(lo.w),
                  bf16_lo(hi.x), bf16_hi(hi.x), bf16_lo(hi.y), bf16_hi(hi.y),
@@ -65,10 +88,17 @@ __device__ __forceinline__ void fp8_vector_codes(const u32x4& lo, const u32x4& h
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  amax = fmaxf(amax, __shfl_xor(amax, 4));
-  float scale, inv;
-  fp8_block_scale<kPow2>(fmaxf(amax, kScaleFloor), scale, inv);
+  float inv;
+  if constexpr (kMode == kScaleMx) {
+    const uint32_t byte = mx_block_scale(amax, inv);
+    if ((v & 1) == 0) reinterpret_cast<uint8_t*>(my_scales)[v / 2] = (uint8_t)byte;
+  } else {
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    float scale;
+    fp8_block_scale<kMode == kScalePow2>(fmaxf(amax, kScaleFloor), scale, inv);
+    if ((v & 7) == 0) my_scales[v / 8] = __float_as_uint(scale);
+  }
   u32x4 q;
   q.x = e4m3_encode4<kHw>(clamp_fp8(f[0] * inv), clamp_fp8(f[1] * inv), clamp_fp8(f[2] * inv),
                           clamp_fp8(f[3] * inv));
@@ -78,7 +108,6 @@ __device__ __forceinline__ void fp8_vector_codes(const u32x4& lo, const u32x4& h
                           clamp_fp8(f[10] * inv), clamp_fp8(f[11] * inv));
   q.w = e4m3_encode4<kHw>(clamp_fp8(f[12] * inv), clamp_fp8(f[13] * inv),
                           clamp_fp8(f[14] * inv), clamp_fp8(f[15] * inv));
-  if ((v & 7) == 0) my_scales[v / 8] = scale;
   for (int32_t j = 0; j < k; ++j) {
     const int32_t s = slots[j];
     if (s >= 0) store_nt(recv + (int64_t)s * out_vec_per_row + v, q);
@@ -89,25 +118,26 @@ __device__ __forceinline__ void fp8_vector_codes(const u32x4& lo, const u32x4& h
 // store of codes per valid row); 8 lanes make one 128-channel block.  `lanes`
 // must be a multiple of 8 so that the 8 lanes of a block step together.  The
 // block scales are left in my_scales for fp8_token_scales.
-template <bool kHw, bool kPow2 = false>
+template <bool kHw, int kMode = kScaleF32>
 __device__ __forceinline__ void fp8_token_codes(const u32x4* __restrict__ src, int32_t hidden,
                                                 int32_t lt, int32_t lanes, const int32_t* slots,
                                                 int32_t k, u32x4* __restrict__ recv,
-                                                float* my_scales) {
+                                                uint32_t* my_scales) {
   const int32_t out_vec_per_row = hidden / 16;  // 16-byte vectors of codes
   for (int32_t v = lt; v < out_vec_per_row; v += lanes)
-    fp8_vector_codes<kHw, kPow2>(src[2 * v], src[2 * v + 1], v, slots, k, recv, out_vec_per_row,
+    fp8_vector_codes<kHw, kMode>(src[2 * v], src[2 * v + 1], v, slots, k, recv, out_vec_per_row,
                                  my_scales);
 }
 
-// After a block barrier: the token's lanes write its staged scales to each
-// valid row, consecutive lanes on consecutive blocks, so every row's scales
-// leave as one contiguous run.  Ordinary stores, so that partial cache lines
-// shared with neighbouring rows can merge in the caches.
+// After a block barrier: the token's lanes write its staged scale words to
+// each valid row, consecutive lanes on consecutive words, so every row's
+// scales leave as one contiguous run.  Ordinary stores, so that partial cache
+// lines shared with neighbouring rows can merge in the caches.  The words are
+// copied as integers (a word of E8M0 bytes may look like a NaN as an fp32).
 __device__ __forceinline__ void fp8_token_scales(int32_t hidden, int32_t lt, int32_t lanes,
                                                  const int32_t* slots, int32_t k,
-                                                 const float* my_scales,
-                                                 float* __restrict__ scales) {
+                                                 const uint32_t* my_scales,
+                                                 uint32_t* __restrict__ scales) {
   const int32_t blocks_per_row = hidden / kFp8Block;
   const int32_t n = k * blocks_per_row;
   for (int32_t i = lt; i < n; i += lanes) {

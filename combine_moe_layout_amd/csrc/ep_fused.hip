@@ -30,7 +30,7 @@ struct FusedArgs {
   int32_t k, num_experts, num_groups, capacity, hidden;
   const u32x4* x;
   u32x4* recv;
-  float* scales;
+  uint32_t* scales;
   int32_t* slot_idx;
   int32_t* recv_src;
   int32_t* num_tokens_per_expert;
@@ -80,7 +80,7 @@ __device__ int32_t block_exclusive_scan(const int32_t* in, int32_t* out, int n, 
   return total;
 }
 
-template <bool kFp8, bool kHw, bool kPow2>
+template <bool kFp8, bool kHw, int kMode>
 __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a) {
   __shared__ int32_t s_idx[kFusedMaxPairs];  // expert of every pair, -1 if none
   __shared__ int32_t s_sum[2 * kFusedMaxTopk];
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
   __shared__ int32_t s_hist[EP_MAX_EXPERTS];
   __shared__ int32_t s_off[EP_MAX_EXPERTS];
   __shared__ int32_t s_wave[1024 / kWave];
-  __shared__ float s_scale[kMaxScalesPerBlock];
+  __shared__ uint32_t s_scale[kMaxScalesPerBlock];
   const int tid = threadIdx.x;
   const int E = a.num_experts, k = a.k;
   const int32_t P = (int32_t)(a.num_tokens * k);
@@ -191,13 +191,13 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
   if (one_pass) {
     if (tid < vecs) {
       if constexpr (kFp8)
-        fp8_vector_codes<kHw, kPow2>(pre_lo, pre_hi, tid, s_slot, k, a.recv, vecs, s_scale);
+        fp8_vector_codes<kHw, kMode>(pre_lo, pre_hi, tid, s_slot, k, a.recv, vecs, s_scale);
       else
         for (int32_t j = 0; j < k; ++j)
           if (s_slot[j] >= 0) store_nt(a.recv + (int64_t)s_slot[j] * vecs + tid, pre_lo);
     }
   } else if constexpr (kFp8) {
-    fp8_token_codes<kHw, kPow2>(src, a.hidden, tid, blockDim.x, s_slot, k, a.recv, s_scale);
+    fp8_token_codes<kHw, kMode>(src, a.hidden, tid, blockDim.x, s_slot, k, a.recv, s_scale);
   } else {
     bf16_token_copy(src, a.hidden, tid, blockDim.x, s_slot, k, a.recv);
   }
@@ -214,8 +214,8 @@ bool fused_layout_dispatch_fits(const ep_layout_t& L) {
 
 hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout_t& L,
                                         const void* x, int32_t hidden, int32_t dtype,
-                                        void* recv_x, float* recv_scales, hipStream_t stream) {
-  const bool fp8 = dtype != EP_BF16;
+                                        void* recv_x, void* recv_scales, hipStream_t stream) {
+  const bool fp8 = dtype_is_fp8(dtype);
   FusedArgs a;
   a.topk_idx = topk_idx;
   a.num_tokens = L.num_tokens;
@@ -226,7 +226,7 @@ hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout
   a.hidden = hidden;
   a.x = static_cast<const u32x4*>(x);
   a.recv = static_cast<u32x4*>(recv_x);
-  a.scales = recv_scales;
+  a.scales = static_cast<uint32_t*>(recv_scales);
   a.slot_idx = L.slot_idx;
   a.recv_src = L.recv_src;
   a.num_tokens_per_expert = L.num_tokens_per_expert;
@@ -240,13 +240,16 @@ hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout
   lanes = lanes < 256 ? 256 : (lanes > 1024 ? 1024 : lanes);
   const dim3 grid((unsigned)(L.num_tokens + 1));
   if (dtype == EP_FP8_E4M3)
-    hipLaunchKernelGGL((layout_dispatch_small_kernel<true, kDispatchUsesHwCast, false>), grid,
+    hipLaunchKernelGGL((layout_dispatch_small_kernel<true, kDispatchUsesHwCast, kScaleF32>), grid,
                        dim3(lanes), 0, stream, a);
   else if (dtype == EP_FP8_E4M3_POW2)
-    hipLaunchKernelGGL((layout_dispatch_small_kernel<true, kDispatchUsesHwCast, true>), grid,
+    hipLaunchKernelGGL((layout_dispatch_small_kernel<true, kDispatchUsesHwCast, kScalePow2>), grid,
                        dim3(lanes), 0, stream, a);
-  else
-    hipLaunchKernelGGL((layout_dispatch_small_kernel<false, kDispatchUsesHwCast, false>), grid,
+  else if (dtype == EP_MXFP8_E4M3)
+    hipLaunchKernelGGL((layout_dispatch_small_kernel<true, kDispatchUsesHwCast, kScaleMx>), grid,
+                       dim3(lanes), 0, stream, a);
+  else  // EP_BF16 and EP_F16: a bit copy
+    hipLaunchKernelGGL((layout_dispatch_small_kernel<false, kDispatchUsesHwCast, kScaleF32>), grid,
                        dim3(lanes), 0, stream, a);
   return hipGetLastError();
 }

@@ -35,14 +35,29 @@ hipError_t launch_layout_ids(const int64_t* ids, const ep_layout_t& L, void* wor
                              int32_t extra_flags, hipStream_t stream);
 int32_t* layout_extra_flags(const ep_layout_t& L, void* workspace);
 
+// Receive dtypes whose rows are E4M3 codes with a scale row (the others are a
+// bit copy of 2-byte elements).
+inline bool dtype_is_fp8(int32_t dtype) {
+  return dtype == EP_FP8_E4M3 || dtype == EP_FP8_E4M3_POW2 || dtype == EP_MXFP8_E4M3;
+}
+
+// recv_scales: fp32 [R, hidden/128] or, for EP_MXFP8_E4M3, E8M0 bytes
+// [R, hidden/32]: hidden/128 4-byte words per row either way.
 hipError_t launch_dispatch(const void* x, const ep_layout_t& L, int32_t hidden, int32_t dtype,
-                           void* recv_x, float* recv_scales, hipStream_t stream);
+                           void* recv_x, void* recv_scales, hipStream_t stream);
 
 hipError_t launch_combine(const void* y, const float* w, const ep_layout_t& L, int32_t hidden,
                           void* out, hipStream_t stream);
 
+// Combine with fp16 expert outputs and fp16 output.
+hipError_t launch_combine_f16(const void* y, const float* w, const ep_layout_t& L,
+                              int32_t hidden, void* out, hipStream_t stream);
+
 hipError_t launch_dequant_fp8(const uint8_t* q, const float* scales, int64_t rows, int32_t hidden,
                               void* y, hipStream_t stream);
+
+hipError_t launch_dequant_mxfp8(const uint8_t* q, const uint8_t* scales, int64_t rows,
+                                int32_t hidden, void* y, hipStream_t stream);
 
 hipError_t launch_cast_e4m3_bits(uint32_t first, int64_t n, int32_t method, uint8_t* out,
                                  hipStream_t stream);
@@ -63,7 +78,7 @@ bool fused_layout_dispatch_fits(const ep_layout_t& L);
 
 hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout_t& L,
                                         const void* x, int32_t hidden, int32_t dtype,
-                                        void* recv_x, float* recv_scales, hipStream_t stream);
+                                        void* recv_x, void* recv_scales, hipStream_t stream);
 
 hipError_t launch_combine_fp8(const uint8_t* q, const float* scales, const float* w,
                               const ep_layout_t& L, int32_t hidden, void* out, hipStream_t stream);

@@ -63,9 +63,11 @@ enum ep_status {
 
 /* Receive-buffer element types for ep_dispatch. */
 enum ep_dtype {
-    EP_BF16 = 0,         /* bf16 rows, a bit copy of x */
-    EP_FP8_E4M3 = 1,     /* OCP FP8 E4M3 codes + one fp32 scale per 128 channels */
-    EP_FP8_E4M3_POW2 = 2 /* as EP_FP8_E4M3, with each scale a power of two (see ep_dispatch) */
+    EP_BF16 = 0,          /* bf16 rows, a bit copy of x */
+    EP_FP8_E4M3 = 1,      /* OCP FP8 E4M3 codes + one fp32 scale per 128 channels */
+    EP_FP8_E4M3_POW2 = 2, /* as EP_FP8_E4M3, with each scale a power of two (see ep_dispatch) */
+    EP_MXFP8_E4M3 = 3,    /* OCP MXFP8: E4M3 codes + one E8M0 scale byte per 32 channels */
+    EP_F16 = 4            /* fp16 rows: x is fp16 and the rows are a bit copy of it */
 };
 
 /* Bits of layout->error_flags, written by ep_get_layout. */
@@ -154,11 +156,20 @@ int ep_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* work
  *   EP_FP8_E4M3_POW2: the same layout, but each block's scale is the smallest
  *                power of two s with 448 * s >= a, and each code the nearest
  *                E4M3 of clamp(x / s, -448, 448) (an exact rescale).
+ *   EP_MXFP8_E4M3: recv_x uint8 [R, hidden] E4M3 codes and recv_scales uint8
+ *                [R, hidden/32] E8M0 bytes (the OCP Microscaling MXFP8 format
+ *                that gfx950's scaled matrix instructions consume; the same
+ *                bytes per row as the fp32 scales): per block of 32 channels
+ *                se = floor(log2(max|x|)) - 8 clamped to [-127, 127] (-127 for
+ *                an all-zero block), byte = se + 127, code = nearest E4M3 (ties
+ *                to even) of clamp(x / 2^se, -448, 448); requires hidden % 128 == 0.
+ *   EP_F16:      x is fp16 [T, hidden] and recv_x fp16 [R, hidden], a bit copy.
+ * recv_scales (fp32 or E8M0 rows) must be 4-byte aligned.
  * Rows that no slot names are left untouched.  hidden % 8 == 0.
  * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN, EP_ERR_DTYPE or EP_ERR_LAUNCH.
  */
 int ep_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,
-                void* recv_x, float* recv_scales, void* stream);
+                void* recv_x, void* recv_scales, void* stream);
 
 /*
  * Layout and dispatch in one call: the same results as ep_get_layout followed
@@ -171,7 +182,7 @@ int ep_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_
  */
 int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
                        size_t workspace_bytes, const void* x, int32_t hidden, int32_t recv_dtype,
-                       void* recv_x, float* recv_scales, void* stream);
+                       void* recv_x, void* recv_scales, void* stream);
 
 /*
  * Combine ([yololab] stage table, combine row: back to token order with a
@@ -184,6 +195,18 @@ int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void*
  */
 int ep_combine(const void* expert_out, const float* topk_weights, const ep_layout_t* layout,
                int32_t hidden, void* out, void* stream);
+
+/*
+ * Combine with fp16 expert outputs and fp16 output (the pages' benchmark
+ * matrix lists BF16, FP16 and FP8 as the precisions to cover: [yololab]
+ * "Benchmark矩陣").  As ep_combine, with expert_out fp16 [R, hidden] and
+ * out fp16 [T, hidden]: out[t] = fp16(sum over valid j of topk_weights[t,j] *
+ * expert_out[slot]) accumulated in fp32, rounded to nearest-even with fp16
+ * subnormals kept and overflow to infinity; +0 for a token with no valid pair.
+ * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN or EP_ERR_LAUNCH.
+ */
+int ep_combine_f16(const void* expert_out, const float* topk_weights, const ep_layout_t* layout,
+                   int32_t hidden, void* out, void* stream);
 
 /*
  * Combine of FP8 expert outputs ([yololab] stage table, combine row;
@@ -274,6 +297,14 @@ int ep_combine_groups(const void* z, const ep_layout_t* group_layout, int32_t hi
  */
 int ep_dequant_fp8(const uint8_t* q, const float* scales, int64_t rows, int32_t hidden, void* y,
                    void* stream);
+
+/* Identity-expert stand-in for MXFP8 receive buffers (not part of the path):
+ * y[r, c] = the bf16 nearest (ties to even) to decode(q[r, c]) *
+ * 2^(scales[r, c/32] - 127), an exact product rounded once.  q uint8
+ * [rows, hidden], scales uint8 [rows, hidden/32], y bf16 [rows, hidden];
+ * hidden % 128 == 0. */
+int ep_dequant_mxfp8(const uint8_t* q, const uint8_t* scales, int64_t rows, int32_t hidden,
+                     void* y, void* stream);
 
 /*
  * The FP8 encoder that ep_dispatch applies to x * inv, exposed for

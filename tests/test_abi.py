@@ -138,7 +138,18 @@ def test_entry_points_reject_bad_arguments(L):
     assert L.ep_combine(fake, fake, by(s), 256, fake + 4, None) == -3
     assert L.ep_combine(fake, fake, by(s), 0, fake, None) == -2
     assert L.ep_combine(fake, fake, by(s), 65536 + 8, fake, None) == -2
+    # MXFP8 and fp16 receive dtypes
+    assert L.ep_dispatch(fake, by(s), 200, 3, fake, fake, None) == -2       # MXFP8 needs H % 128
+    assert L.ep_dispatch(fake, by(s), 256, 3, fake, None, None) == -1       # MXFP8 needs scales
+    assert L.ep_dispatch(fake, by(s), 256, 3, fake, fake + 1, None) == -3   # scale words aligned
+    assert L.ep_dispatch(fake, by(s), 256, 5, fake, None, None) == -6       # no dtype 5
+    assert L.ep_dispatch(fake + 2, by(s), 256, 4, fake, None, None) == -3   # fp16 x alignment
+    assert L.ep_combine_f16(None, fake, by(s), 256, fake, None) == -1
+    assert L.ep_combine_f16(fake, fake, by(s), 252, fake, None) == -2
+    assert L.ep_combine_f16(fake, fake, by(s), 256, fake + 8, None) == -3
     # auxiliaries
+    assert L.ep_dequant_mxfp8(fake, fake, 4, 96, fake, None) == -2
+    assert L.ep_dequant_mxfp8(fake, None, 4, 128, fake, None) == -1
     assert L.ep_dequant_fp8(fake, fake, 4, 100, fake, None) == -2
     assert L.ep_cast_e4m3_bits(0, 16, 3, fake, None) == -2
     assert L.ep_copy(fake, fake, 17, None) == -2
@@ -147,6 +158,7 @@ def test_entry_points_reject_bad_arguments(L):
     e = _layout(T=0)
     assert L.ep_dispatch(None, by(e), 256, 0, None, None, None) == 0
     assert L.ep_combine(None, None, by(e), 256, None, None) == 0
+    assert L.ep_combine_f16(None, None, by(e), 256, None, None) == 0
     assert L.ep_copy(None, None, 0, None) == 0
 
 
