@@ -157,12 +157,21 @@ def main() -> int:
     ap.add_argument("--fused", action="store_true",
                     help="layout and dispatch through ep_layout_dispatch (one launch for batches "
                          "of at most 2048 pairs); the layout/dispatch split is then not reported")
+    ap.add_argument("--mx", action="store_true",
+                    help="MXFP8 dispatch (EP_MXFP8_E4M3: one E8M0 scale byte per 32 channels)")
+    ap.add_argument("--f16", action="store_true",
+                    help="fp16 path: EP_F16 dispatch and ep_combine_f16 (a bf16 workload's shapes)")
     ap.add_argument("--dedup", action="store_true",
                     help="per-group dedup variant: ep_get_group_layout (with the receiving "
                          "side's metadata), dispatch to the groups, ep_combine_groups")
     args = ap.parse_args()
-    if args.dedup and (args.fused or args.fp8_combine or args.graph):
-        print("--dedup times its own three calls; it combines with --pow2 only", file=sys.stderr)
+    if args.dedup and (args.fused or args.fp8_combine or args.graph or args.f16):
+        print("--dedup times its own three calls; it combines with --pow2 and --mx only",
+              file=sys.stderr)
+        return 2
+    if args.mx and (args.pow2 or args.fp8_combine):
+        print("--mx is its own scale format; it does not combine with --pow2 or --fp8-combine",
+              file=sys.stderr)
         return 2
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -190,26 +199,39 @@ def main() -> int:
     if args.fp8_combine and not fp8:
         print("--fp8-combine needs an FP8 workload", file=sys.stderr)
         return 2
-    dtype_enum = (B.EP_FP8_E4M3_POW2 if args.pow2 else B.EP_FP8_E4M3) if fp8 else B.EP_BF16
-    x = torch.from_numpy(wl.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    if args.f16:
+        fp8 = False  # the fp16 path moves 2-byte rows both ways
+    if fp8:
+        dtype_enum = B.EP_MXFP8_E4M3 if args.mx else B.EP_FP8_E4M3_POW2 if args.pow2 else B.EP_FP8_E4M3
+    else:
+        dtype_enum = B.EP_F16 if args.f16 else B.EP_BF16
+    if args.f16:
+        # fp16 activations of the same distribution (the bf16 values, converted)
+        x = torch.from_numpy(wl.x_bits.view(np.int16)).to(dev).view(torch.bfloat16).to(torch.float16)
+    else:
+        x = torch.from_numpy(wl.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    row_dtype = torch.float16 if args.f16 else torch.bfloat16
     topk_idx = torch.from_numpy(wl.topk_idx).to(dev)
     topk_w = torch.from_numpy(wl.topk_weights).to(dev)
     lay = B.EpLayout(T, k, E, G, wl.cap, device=dev)
     R = lay.num_recv_rows
     if fp8:
         recv_q = torch.empty((R, H), dtype=torch.uint8, device=dev)
-        recv_s = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+        recv_s = (torch.empty((R, H // 32), dtype=torch.uint8, device=dev) if args.mx else
+                  torch.empty((R, H // 128), dtype=torch.float32, device=dev))
     else:
-        recv_q = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+        recv_q = torch.empty((R, H), dtype=row_dtype, device=dev)
         recv_s = None
-    y = None if args.fp8_combine else torch.empty((R, H), dtype=torch.bfloat16, device=dev)
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    y = None if args.fp8_combine else torch.empty((R, H), dtype=row_dtype, device=dev)
+    out = torch.empty((T, H), dtype=row_dtype, device=dev)
 
     # identity expert, once, untimed; y is its own buffer, as an expert's output would be
     B.ep_get_layout(topk_idx, lay)
     B.ep_dispatch(x, lay, dtype_enum, recv_q, recv_s)
     if args.fp8_combine:
         pass  # the FP8 receive buffer itself is the expert output
+    elif fp8 and args.mx:
+        B.ep_dequant_mxfp8(recv_q, recv_s, y)
     elif fp8:
         B.ep_dequant_fp8(recv_q, recv_s, y)
     else:
@@ -227,12 +249,17 @@ def main() -> int:
         g_ridx = torch.empty((Rg, k), dtype=torch.int64, device=dev)
         g_rw = torch.empty((Rg, k), dtype=torch.float32, device=dev)
         g_q = torch.empty((Rg, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
-        g_s = torch.empty((Rg, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+        g_s = None
+        if fp8:
+            g_s = (torch.empty((Rg, H // 32), dtype=torch.uint8, device=dev) if args.mx else
+                   torch.empty((Rg, H // 128), dtype=torch.float32, device=dev))
         g_z = torch.empty((Rg, H), dtype=torch.bfloat16, device=dev)
         B.ep_get_group_layout(topk_idx, topk_w, glay, g_ridx, g_rw)
         B.ep_dispatch(x, glay, dtype_enum, g_q, g_s)
         # identity experts on the receiving side, untimed: one row per (token, group)
-        if fp8:
+        if fp8 and args.mx:
+            B.ep_dequant_mxfp8(g_q, g_s, g_z)
+        elif fp8:
             B.ep_dequant_fp8(g_q, g_s, g_z)
         else:
             B.ep_copy(g_q, g_z)
@@ -275,6 +302,8 @@ def main() -> int:
             ev[2].record(s)
         if args.fp8_combine:
             B.ep_combine_fp8(recv_q, recv_s, topk_w, lay, out, s)
+        elif args.f16:
+            B.ep_combine_f16(y, topk_w, lay, out, s)
         else:
             B.ep_combine(y, topk_w, lay, out, s)
         if ev is not None:
@@ -350,7 +379,8 @@ def main() -> int:
         dc_gbps = combine_gbps = dispatch_gbps = None
     digest = sources_digest()
     # the committed counters cover the bf16-input combine kernel only
-    traffic = None if (args.fp8_combine or args.dedup) else committed_traffic("combine", name, digest)
+    traffic = (None if (args.fp8_combine or args.dedup or args.f16) else
+               committed_traffic("combine", name, digest))
 
     result = {
         "metric": "dispatch+combine effective HBM GB/s (% peak) at 8K tok×7168, top-8/256",
@@ -367,9 +397,12 @@ def main() -> int:
         "data": "synthetic (seeded: x ~ N(0,1) bf16; routing %s)" % W.CONFIGS[name][7],
         "config": {"workload": W.DESCRIPTIONS[name], "name": name, "T": T, "hidden": H,
                    "experts": E, "groups": G, "topk": k, "capacity": wl.cap,
-                   "dispatch_dtype": ("fp8_e4m3+pow2 scale/128ch" if args.pow2 else
-                                      "fp8_e4m3+fp32 scale/128ch") if fp8 else "bf16",
-                   "combine_dtype": "fp8_e4m3 in, bf16 out" if args.fp8_combine else "bf16",
+                   "dispatch_dtype": ("mxfp8 (e4m3+e8m0 scale/32ch)" if args.mx else
+                                      "fp8_e4m3+pow2 scale/128ch" if args.pow2 else
+                                      "fp8_e4m3+fp32 scale/128ch") if fp8 else
+                                     "fp16" if args.f16 else "bf16",
+                   "combine_dtype": "fp8_e4m3 in, bf16 out" if args.fp8_combine else
+                                    "fp16" if args.f16 else "bf16",
                    "step": "group_layout+dispatch_to_groups+combine_groups (per-group dedup)"
                    if args.dedup else "layout_dispatch (fused call)+combine" if args.fused
                    else "layout+dispatch+combine"},
@@ -387,7 +420,7 @@ def main() -> int:
         result["dispatch_gbps"] = round(dispatch_gbps, 1)
         result["roofline"] = {
             "kernel": "combine_groups" if args.dedup else "combine_fp8" if args.fp8_combine
-            else "combine", "bound": "hbm",
+            else "combine_f16" if args.f16 else "combine", "bound": "hbm",
             "achieved": round(combine_gbps, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(combine_gbps / HBM_PEAK_GBPS, 4),
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
@@ -396,7 +429,8 @@ def main() -> int:
         result["config"]["step"] += " (HIP graph replay)"
     if dedup is not None:
         result["dedup"] = dedup
-    if not args.no_cpu_baseline and name == "dsv3" and not args.dedup:
+    default_path = not (args.dedup or args.mx or args.f16 or args.pow2 or args.fp8_combine)
+    if not args.no_cpu_baseline and name == "dsv3" and default_path:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)
     return 0
