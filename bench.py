@@ -196,8 +196,9 @@ def main() -> int:
         return 2
     wl = W.make(name, seed=args.seed)
     T, H, E, G, k, fp8 = wl.T, wl.H, wl.E, wl.G, wl.k, wl.fp8
-    if args.fp8_combine and not fp8:
-        print("--fp8-combine needs an FP8 workload", file=sys.stderr)
+    if (args.fp8_combine or args.mx or args.pow2) and not fp8:
+        print("--fp8-combine, --mx and --pow2 need an FP8 workload (dsv3, lowlat, large)",
+              file=sys.stderr)
         return 2
     if args.f16:
         fp8 = False  # the fp16 path moves 2-byte rows both ways
