@@ -144,6 +144,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the extra steps timed after emptying L2 and the MALL")
     ap.add_argument("--workload", default="dsv3",
                     help="dsv3 (default: the metric's configuration), tiny, skewed, lowlat or large")
     ap.add_argument("--graph", action="store_true",
@@ -353,6 +355,30 @@ def main() -> int:
     p50 = {kname: float(np.percentile(v, 50)) * 1e3 for kname, v in per.items()}
     p95 = {kname: float(np.percentile(v, 95)) * 1e3 for kname, v in per.items()}
 
+    # The same step with the caches emptied first: before each of these steps a
+    # 512 MiB buffer (twice the 256 MB MALL) is read, outside the events, so
+    # nothing of the previous step is left in L2 or the MALL and the dirty
+    # lines it left are written back before the step starts.  (Writing the
+    # buffer instead would leave the MALL full of dirty lines whose write-back
+    # the next step's writes would pay for.)  Per-kernel event times only; the
+    # timed loop above is the steady state.
+    flushed = None
+    if graph is None and not args.no_flush:
+        flush_buf = torch.zeros((512 << 20) // 8, dtype=torch.int64, device=dev)
+        n_flush = min(args.steps, 50)
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_flush)]
+        for i in range(n_flush):
+            flush_buf.sum()
+            step(fev[i], stream)
+        torch.cuda.synchronize()
+        first = "layout_dispatch" if args.fused else "layout"
+        fper = {first: [ev[0].elapsed_time(ev[1]) for ev in fev]}
+        if not args.fused:
+            fper["dispatch"] = [ev[1].elapsed_time(ev[2]) for ev in fev]
+        fper["combine"] = [ev[2].elapsed_time(ev[3]) for ev in fev]
+        flushed = {kname: round(float(np.mean(v)) * 1e3, 2) for kname, v in fper.items()}
+        del flush_buf
+
     # plain copy of the same size as combine's traffic: the practical ceiling
     copy_bytes = 1 << 30
     src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
@@ -428,6 +454,12 @@ def main() -> int:
             "algorithmic_bytes": nbytes["combine"]}
     else:
         result["config"]["step"] += " (HIP graph replay)"
+    if flushed is not None:
+        d_key = "layout_dispatch" if args.fused else "dispatch"
+        d_bytes_f = nbytes["dispatch"] + (nbytes["layout"] if args.fused else 0)
+        result["kernel_us_mean_after_flush"] = flushed
+        result["dispatch_plus_combine_gbps_after_flush"] = round(
+            (d_bytes_f + nbytes["combine"]) / ((flushed[d_key] + flushed["combine"]) * 1e-6) / 1e9, 1)
     if dedup is not None:
         result["dedup"] = dedup
     default_path = not (args.dedup or args.mx or args.f16 or args.pow2 or args.fp8_combine)
