@@ -10,10 +10,18 @@ deterministic, so its output is the same every step); it is not part of the
 path and not timed.
 
 Prints one JSON line.  `value` is the step's ideal (algorithmic) HBM bytes
-divided by the step's wall time; the per-kernel times come from HIP events
-recorded on the stream the kernels run on.  `--workload` times the other
-named workloads (tiny, skewed, lowlat, large) the same way; the default is the
-configuration the metric is quoted on.
+divided by the step's wall time over back-to-back steps (the steady state);
+the per-kernel times come from HIP events recorded on the stream the kernels
+run on.  The same line reports the per-kernel times of extra steps that each
+start with L2 and the MALL emptied (a 512 MiB read outside the events), and the
+roofline of the dominant kernel (combine) with its HBM traffic from the
+committed rocprofv3 counter summary.
+
+`--workload` times the other named workloads (tiny, skewed, lowlat, large) the
+same way; the default is the configuration the metric is quoted on.  Variant
+flags: --fused (one-call layout+dispatch), --pow2 / --mx (power-of-two or
+MXFP8 scales), --fp8-combine (FP8 expert outputs), --f16 (fp16 rows),
+--dedup (per-group dedup layout, dispatch and combine), --graph (HIP graph).
 """
 from __future__ import annotations
 

@@ -1,5 +1,5 @@
 // ep_api.hip -- the extern "C" entry points of libep.so (declared in ep.h):
-// host-side argument checks, then one enqueue of the HIP kernels on the
+// host-side argument checks, then the call's HIP kernels enqueued on the
 // caller's stream.  Nothing here allocates or synchronises.
 #include <stdint.h>
 
@@ -284,7 +284,7 @@ const char* ep_status_string(int status) {
     case EP_ERR_NULL: return "a required pointer is NULL";
     case EP_ERR_SHAPE: return "a size is out of range or sizes disagree";
     case EP_ERR_ALIGN: return "a buffer is not aligned as required";
-    case EP_ERR_WORKSPACE: return "workspace smaller than ep_layout_workspace_bytes()";
+    case EP_ERR_WORKSPACE: return "workspace smaller than its size query reports";
     case EP_ERR_LAUNCH: return "the HIP runtime reported a launch error";
     case EP_ERR_DTYPE: return "unknown receive dtype";
     default: return "unknown status";

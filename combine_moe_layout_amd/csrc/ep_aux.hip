@@ -1,6 +1,6 @@
-// ep_aux.hip -- helpers around the path: the identity-expert stand-in for FP8
-// receive buffers, the FP8 encoder exposed for verification, and a plain copy
-// kernel that serves as the bandwidth reference.
+// ep_aux.hip -- helpers around the path: the identity-expert stand-ins for
+// FP8 and MXFP8 receive buffers, the FP8 encoder exposed for verification, and
+// a streaming copy kernel that serves as the bandwidth reference.
 #include "ep_device.h"
 #include "ep_internal.h"
 

@@ -8,14 +8,21 @@
 // reduction; BF16 combine as in the DeepEP v2 release notes (donniechu.com),
 // section "Số liệu kỹ thuật").
 //
+// The same kernel, by template flags, also serves fp16 rows and output
+// (ep_combine_f16) and the unit-weight group combine of the per-group dedup
+// variant (ep_combine_groups); the second half of this file is the combine of
+// FP8 expert outputs (ep_combine_fp8).
+//
 // How: HBM-bound (k row reads and one row write per token, each read once).
-// One workgroup per token, one lane per 16-byte vector (8 channels) of the
-// row, so every wave instruction covers 1 KiB of one row and the rows can be
-// read with the non-temporal hint.  The k rows of a lane are loaded before any
-// arithmetic (the top-k is a template parameter for the common sizes, so all k
-// loads are in flight together), then accumulated with fp32 fma.  A pair
-// without a receive row is loaded from row 0 and discarded with a select,
-// never multiplied, so unwritten rows (padded mode) cannot leak NaNs.
+// One workgroup per token (rows shorter than a wave share a workgroup), one
+// lane per 16-byte vector (8 channels) of the row, so every wave instruction
+// covers 1 KiB of one row and the rows can be read with the non-temporal hint.
+// The k rows of a lane are loaded before any arithmetic (the top-k is a
+// template parameter for the common sizes, so all k loads are in flight
+// together), then accumulated with fp32 fma.  A pair without a receive row is
+// loaded from row 0 and discarded with a select, never multiplied, so
+// unwritten rows (padded mode) cannot leak NaNs; the group combine skips such
+// loads instead.
 #include "ep_device.h"
 #include "ep_internal.h"
 

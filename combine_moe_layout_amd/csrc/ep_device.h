@@ -1,5 +1,6 @@
-// ep_device.h -- device helpers shared by the gfx950 kernels of libep.so:
-// wave64 lane masks, bf16 and OCP FP8 E4M3 conversions, 16-byte vector types.
+// ep_device.h -- device helpers shared by the gfx950 kernels of libep.so: the
+// wave64 width, 16-byte vector types with non-temporal accesses, and bf16 and
+// OCP FP8 E4M3 conversions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,9 +19,10 @@ struct alignas(16) u32x4 {
 typedef uint32_t u32x4_vec __attribute__((ext_vector_type(4)));
 
 // 16-byte (and 8-byte) loads and stores with the non-temporal hint, for
-// streams touched once.  Each wave instruction using them must cover whole cache lines (64
-// lanes x 16 contiguous bytes): a non-temporal access does not keep the line,
-// so a second instruction reading the other half of a line fetches it again.
+// streams touched once.  Each wave instruction using them must cover whole
+// cache lines (64 lanes x 16 or 8 contiguous bytes: 1 KiB or 512 B): a
+// non-temporal access does not keep the line, so a second instruction reading
+// the other half of a line would fetch it again.
 __device__ __forceinline__ u32x4 load_nt(const u32x4* p) {
   const u32x4_vec v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_vec*>(p));
   return u32x4{v.x, v.y, v.z, v.w};
@@ -35,7 +37,9 @@ __device__ __forceinline__ void store_nt(u32x4* p, const u32x4& a) {
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) {
+  return __uint_as_float(packed & 0xFFFF0000u);
+}
 
 // fp32 -> bf16 bit pattern, round to nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -78,7 +82,7 @@ __device__ __forceinline__ uint32_t e4m3_encode_sw(float v) {
     code = (e8 << 3) | (m >> 20);
     uint32_t rem = m & 0xFFFFFu;
     code += (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u;
-    code = code > 0x7Eu ? 0x7Eu : code;  // only |v| == 448 rounding up could exceed
+    code = code > 0x7Eu ? 0x7Eu : code;  // a guard: |v| <= 448 never rounds past 0x7E
   } else {
     // subnormal codes are multiples of 2^-9: round |v| * 2^9 to an integer, ties to even
     code = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);

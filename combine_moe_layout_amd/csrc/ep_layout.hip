@@ -37,7 +37,8 @@ namespace ep {
 // flight at once); larger matrices are summed from memory.
 constexpr int kStageInts = 12288;
 static_assert(kStageInts % (4 * kLayoutThreads) == 0, "staging is done in whole 16-byte batches");
-static_assert(kStageInts >= kLayoutWaves * EP_MAX_EXPERTS, "phase-1 histograms alias the staging area");
+static_assert(kStageInts >= kLayoutWaves * EP_MAX_EXPERTS,
+              "phase-1 histograms alias the staging area");
 
 struct LayoutShared {
   int32_t counts[kStageInts];  // phase 2; phase 1 uses the front as kLayoutWaves histograms
@@ -324,8 +325,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(LayoutArg
     local[i] = v >= 0 ? (v >> kExpertBits) : 0;
   }
   finish_chunk<false>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, a.num_chunks,
-                      a.num_flags, blockIdx.x, a.chunk_count, a.chunk_flags, sh, eid, local, a.slot_idx,
-                      a.recv_src, a.num_tokens_per_expert, a.expert_offsets,
+                      a.num_flags, blockIdx.x, a.chunk_count, a.chunk_flags, sh, eid, local,
+                      a.slot_idx, a.recv_src, a.num_tokens_per_expert, a.expert_offsets,
                       a.num_tokens_per_group, a.error_flags, 0);
 }
 

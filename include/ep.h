@@ -55,8 +55,8 @@ enum ep_status {
     EP_OK = 0,
     EP_ERR_NULL = -1,      /* a required pointer is NULL */
     EP_ERR_SHAPE = -2,     /* a size is out of range or sizes disagree */
-    EP_ERR_ALIGN = -3,     /* a row buffer is not 16-byte aligned */
-    EP_ERR_WORKSPACE = -4, /* workspace smaller than ep_layout_workspace_bytes() */
+    EP_ERR_ALIGN = -3,     /* a buffer is not aligned as its call requires */
+    EP_ERR_WORKSPACE = -4, /* workspace smaller than its size query reports */
     EP_ERR_LAUNCH = -5,    /* the HIP runtime reported an error when launching */
     EP_ERR_DTYPE = -6      /* unknown receive dtype */
 };

@@ -512,7 +512,8 @@ EXPORT int ep_oracle_group_layout(const int64_t* topk_idx, const float* topk_wei
         num_tokens_per_group[g] = c;
     }
     group_offsets[0] = 0;
-    for (int32_t g = 0; g < G; ++g) group_offsets[g + 1] = group_offsets[g] + num_tokens_per_group[g];
+    for (int32_t g = 0; g < G; ++g)
+        group_offsets[g + 1] = group_offsets[g] + num_tokens_per_group[g];
 
     /* 4. rows: walk the tokens in order with one running cursor per group */
     int32_t* cursor = (int32_t*)calloc((size_t)G, sizeof(int32_t));
@@ -634,9 +635,10 @@ EXPORT void ep_oracle_dequant_mxfp8(const uint8_t* q, const uint8_t* scales, int
                                     uint16_t* y) {
     int32_t nb = H / 32;
     for (int64_t r = 0; r < R; ++r)
-        for (int32_t c = 0; c < H; ++c)
-            y[r * H + c] = ep_oracle_bf16_from_double(
-                ep_oracle_e4m3_decode(q[r * H + c]) * ldexp(1.0, (int)scales[r * nb + c / 32] - 127));
+        for (int32_t c = 0; c < H; ++c) {
+            double x = ldexp(1.0, (int)scales[r * nb + c / 32] - 127);   /* E8M0: 2^(byte-127) */
+            y[r * H + c] = ep_oracle_bf16_from_double(ep_oracle_e4m3_decode(q[r * H + c]) * x);
+        }
 }
 
 /* fp16 (IEEE 754 binary16: 1 sign bit, 5 exponent bits with bias 15, 10
@@ -703,5 +705,6 @@ EXPORT void ep_oracle_combine_f16(const uint16_t* y, const float* w, const int32
 EXPORT void ep_oracle_combine_f16_tokens(const uint16_t* y, const float* w, const int32_t* slot_idx,
                                          int32_t k, int32_t H, const int64_t* tokens, int64_t n,
                                          uint16_t* out_rows) {
-    for (int64_t i = 0; i < n; ++i) combine_f16_one(y, w, slot_idx, tokens[i], k, H, out_rows + i * H);
+    for (int64_t i = 0; i < n; ++i)
+        combine_f16_one(y, w, slot_idx, tokens[i], k, H, out_rows + i * H);
 }
