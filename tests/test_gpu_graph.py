@@ -81,3 +81,63 @@ def test_graph_replays_match_eager(name, T, H, fused):
         want = expected[r % 2]
         for a, b in zip(got, want):
             assert np.array_equal(a, b), "replay %d differs from the eager result" % r
+
+
+@pytest.mark.parametrize("name,T,H", [("dsv3", 1024, 1024), ("skewed", 600, 512)])
+def test_graph_replays_match_eager_dedup_mxfp8(name, T, H):
+    """The per-group dedup path with MXFP8 dispatch: group layout with the
+    receiving side's metadata, dispatch to the groups, the MXFP8 stand-in
+    expert, group combine."""
+    print("[gpu-graph] dedup+mxfp8 %s T=%s H=%s" % (name, T, H), flush=True)
+    wl = W.make(name, T=T, H=H)
+    wl2 = W.make(name, T=T, H=H, seed=7)
+    dev = torch.device("cuda")
+    idx = torch.from_numpy(wl.topk_idx).to(dev)
+    x = torch.from_numpy(wl.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    w = torch.from_numpy(wl.topk_weights).to(dev)
+    gl = B.EpGroupLayout(wl.T, wl.k, wl.E, wl.G, with_recv_src=True, device=dev)
+    R = gl.num_recv_rows
+    ridx = torch.zeros((R, wl.k), dtype=torch.int64, device=dev)
+    rw = torch.zeros((R, wl.k), dtype=torch.float32, device=dev)
+    q = torch.zeros((R, wl.H), dtype=torch.uint8, device=dev)
+    s = torch.zeros((R, wl.H // 32), dtype=torch.uint8, device=dev)
+    z = torch.zeros((R, wl.H), dtype=torch.bfloat16, device=dev)
+    out = torch.zeros((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+
+    def path():
+        B.ep_get_group_layout(idx, w, gl, ridx, rw)
+        B.ep_dispatch(x, gl, B.EP_MXFP8_E4M3, q, s)
+        B.ep_dequant_mxfp8(q, s, z)
+        B.ep_combine_groups(z, gl, out)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return tuple(t.cpu().numpy().copy() for t in (gl.slot_idx, gl.expert_offsets, gl.recv_src,
+                                                      gl.error_flags, ridx, rw, q, s)) + (_bits(out).copy(),)
+
+    def clear():
+        for t in (ridx, rw, q, s, z, out, gl.slot_idx, gl.expert_offsets, gl.recv_src, gl.error_flags):
+            t.zero_()
+
+    def load(ti, xi, wi):
+        idx.copy_(torch.from_numpy(ti))
+        x.copy_(torch.from_numpy(xi.view(np.int16)).view(torch.bfloat16))
+        w.copy_(torch.from_numpy(wi))
+
+    inputs = [(wl.topk_idx, wl.x_bits, wl.topk_weights), (wl2.topk_idx, wl2.x_bits, wl2.topk_weights)]
+    expected = []
+    for inp in inputs:
+        clear()
+        load(*inp)
+        path()
+        expected.append(snapshot())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path()
+    for r in range(6):
+        clear()
+        load(*inputs[r % 2])
+        torch.cuda.synchronize()
+        graph.replay()
+        for a, b in zip(snapshot(), expected[r % 2]):
+            assert np.array_equal(a, b), "replay %d differs from the eager result" % r

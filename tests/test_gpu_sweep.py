@@ -1,0 +1,81 @@
+"""GPU parity over seeded random configurations: layout, dispatch (bf16, FP8,
+power-of-two FP8, MXFP8) and combine against the oracle, on shapes the named
+workloads do not reach (odd token counts and top-k, many or few experts and
+groups, small capacities with drops, masked entries, narrow and wide rows).
+
+Same bar as the other parity tests: layout and dispatch bit-exact, combine
+within |gpu - ref| <= 8e-3 * max(|ref|, 1e-3).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_moe_layout_amd import binding as B
+from combine_moe_layout_amd import workloads as W
+from test_gpu_parity import (assert_close_bf16, assert_layout_equal, dev_bf16, gpu_layout, host_bits,
+                             layout_to_host, note)
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [B.EP_BF16, B.EP_FP8_E4M3, B.EP_FP8_E4M3_POW2, B.EP_MXFP8_E4M3]
+
+
+def _config(seed):
+    g = np.random.default_rng(1000 + seed)
+    k = int(g.integers(1, 11))
+    G = int(g.choice([1, 2, 4, 8, 16]))
+    E = G * int(g.integers(max(1, -(-k // G)), 65))          # at least k experts
+    dtype = DTYPES[seed % len(DTYPES)]
+    fp8 = dtype != B.EP_BF16
+    H = 128 * int(g.integers(1, 24)) if fp8 else 8 * int(g.integers(1, 400))
+    T = int(g.integers(1, max(2, 2_000_000 // (H * k))))
+    T = min(T, 3000)
+    cap = int(g.integers(1, 64)) if seed % 3 == 0 else 0
+    return T, H, E, G, k, cap, dtype
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_configuration(seed):
+    T, H, E, G, k, cap, dtype = _config(seed)
+    note("sweep seed %d: T=%d H=%d E=%d G=%d k=%d cap=%d dtype=%d" % (seed, T, H, E, G, k, cap, dtype))
+    wl = W.custom(T, H, E, k, G=G, cap=cap, fp8=dtype != B.EP_BF16, seed=seed)
+    idx = wl.topk_idx.copy()
+    g = np.random.default_rng(seed)
+    idx[g.random(idx.shape) < 0.05] = -1                     # masked entries
+    ol = oracle.layout(idx, E, G, cap)
+    lay = gpu_layout(idx, E, G, cap)
+    assert_layout_equal(layout_to_host(lay), ol, "sweep %d layout" % seed)
+
+    R = lay.num_recv_rows
+    x = dev_bf16(wl.x_bits)
+    used = np.zeros(R, bool)
+    used[ol["slot_idx"][ol["slot_idx"] >= 0]] = True
+    if dtype == B.EP_BF16:
+        recv = torch.zeros((R, H), dtype=torch.bfloat16, device="cuda")
+        B.ep_dispatch(x, lay, dtype, recv)
+        got = host_bits(recv)
+        assert (got[used] == oracle.dispatch_bf16(wl.x_bits, ol["slot_idx"], R)[used]).all()
+        y_bits = W.random_expert_outputs(R, H, seed=seed)
+    else:
+        mx = dtype == B.EP_MXFP8_E4M3
+        q = torch.zeros((R, H), dtype=torch.uint8, device="cuda")
+        s = (torch.zeros((R, H // 32), dtype=torch.uint8, device="cuda") if mx else
+             torch.zeros((R, H // 128), dtype=torch.float32, device="cuda"))
+        B.ep_dispatch(x, lay, dtype, q, s)
+        fn = (oracle.dispatch_mxfp8 if mx else
+              oracle.dispatch_fp8_pow2 if dtype == B.EP_FP8_E4M3_POW2 else oracle.dispatch_fp8)
+        oq, os_ = fn(wl.x_bits, ol["slot_idx"], R)
+        qh, sh = q.cpu().numpy(), s.cpu().numpy()
+        assert (qh[used] == oq[used]).all(), "codes"
+        if mx:
+            assert (sh[used] == os_[used]).all(), "E8M0 bytes"
+        else:
+            assert (sh[used].view(np.uint32) == os_[used].view(np.uint32)).all(), "scales"
+        y_bits = oracle.dequant_mxfp8(oq, os_) if mx else oracle.dequant_fp8(oq, os_)
+
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    B.ep_combine(dev_bf16(y_bits), torch.from_numpy(wl.topk_weights).cuda(), lay, out)
+    torch.cuda.synchronize()
+    assert_close_bf16(host_bits(out), oracle.combine(y_bits, wl.topk_weights, ol["slot_idx"]),
+                      "sweep %d combine" % seed)
