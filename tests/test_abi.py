@@ -1,8 +1,9 @@
 """The C ABI boundary on the host (CPU only, no kernel launches).
 
 libep.so loads, exports every function include/ep.h declares, the Python
-binding mirrors exactly that list, and the host-side checks reject bad
-arguments before anything is enqueued (fake device pointers below are never
+binding mirrors exactly that list, the header compiles as C11 and a C program
+links against the library, and the host-side checks reject bad arguments
+before anything is enqueued (fake device pointers below are never
 dereferenced: every call here fails validation first).
 """
 import ctypes
@@ -204,6 +205,25 @@ def test_group_layout_sizes_and_validation(L):
     assert L.ep_combine_fp8(fake, fake, fake, by(e), 200, fake, None) == -2   # H % 128
     assert L.ep_combine_fp8(fake, None, fake, by(e), 256, fake, None) == -1
     assert L.ep_combine_fp8(fake, fake + 2, fake, by(e), 256, fake, None) == -3
+
+
+def compile_c_roundtrip(out_path: str) -> subprocess.CompletedProcess:
+    """Builds tests/c/ep_roundtrip.c, a plain C program that uses include/ep.h
+    and links libep.so, with gcc (C11, warnings as errors)."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pkg = os.path.join(root, "combine_moe_layout_amd")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror",
+           os.path.join(root, "tests", "c", "ep_roundtrip.c"),
+           "-I", os.path.join(root, "include"), "-I", os.path.join(rocm, "include"),
+           "-L", pkg, "-lep", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath," + pkg, "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", out_path]
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    r = compile_c_roundtrip(str(tmp_path / "ep_roundtrip"))
+    assert r.returncode == 0, r.stderr
 
 
 def test_status_strings(L):
