@@ -10,12 +10,14 @@ deterministic, so its output is the same every step); it is not part of the
 path and not timed.
 
 Prints one JSON line.  `value` is the step's ideal (algorithmic) HBM bytes
-divided by the step's wall time over back-to-back steps (the steady state);
-the per-kernel times come from HIP events recorded on the stream the kernels
-run on.  The same line reports the per-kernel times of extra steps that each
-start with L2 and the MALL emptied (a 512 MiB read outside the events), and the
-roofline of the dominant kernel (combine) with its HBM traffic from the
-committed rocprofv3 counter summary.
+divided by the step's wall time over K back-to-back steps with nothing else
+enqueued (the steady state).  The per-kernel times come from a separate pass
+of K steps with HIP events recorded around every call on the stream the
+kernels run on; the events cost a few us each, so that pass's step time is
+reported apart (`ms_per_step_with_events`).  The same line reports the
+per-kernel times of extra steps that each start with L2 and the MALL emptied
+(a 512 MiB read outside the events), and the roofline of the dominant kernel
+(combine) with its HBM traffic from the committed rocprofv3 counter summary.
 
 `--workload` times the other named workloads (tiny, skewed, lowlat, large) the
 same way; the default is the configuration the metric is quoted on.  Variant
@@ -333,13 +335,17 @@ def main() -> int:
             graph.replay()
         torch.cuda.synchronize()
 
-    # timed region: exactly K steps, synchronised on both sides
+    # Per-kernel pass: K steps with HIP events recorded around every call on
+    # the stream the kernels run on.  The events measure each kernel's own
+    # duration (the per-kernel breakdown and the roofline come from here), but
+    # each costs a few us of its own on the GPU, so the step rate is taken
+    # from the timed loop below, which records none.
     if graph is not None:
         events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     else:
         events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    e0 = time.perf_counter()
     for i in range(args.steps):
         if graph is not None:
             events[i][0].record(stream)
@@ -348,8 +354,21 @@ def main() -> int:
         else:
             step(events[i], stream)
     torch.cuda.synchronize()
+    ms_with_events = (time.perf_counter() - e0) * 1e3 / args.steps
+
+    # timed region: exactly K steps, synchronised on both sides, nothing else
+    # enqueued between them
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step(None, stream)
+    torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
     if graph is not None:
         per = {"graph_step": [ev[0].elapsed_time(ev[1]) for ev in events]}
     elif args.fused:
@@ -442,6 +461,7 @@ def main() -> int:
                    if args.dedup else "layout_dispatch (fused call)+combine" if args.fused
                    else "layout+dispatch+combine"},
         "pct_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "ms_per_step_with_events": round(ms_with_events, 5),
         "ideal_bytes": nbytes,
         "kernel_us_mean": {kk: round(v, 2) for kk, v in us.items()},
         "kernel_us_p50": {kk: round(v, 2) for kk, v in p50.items()},
