@@ -381,6 +381,7 @@ def main() -> int:
     us = {kname: float(np.mean(v)) * 1e3 for kname, v in per.items()}
     p50 = {kname: float(np.percentile(v, 50)) * 1e3 for kname, v in per.items()}
     p95 = {kname: float(np.percentile(v, 95)) * 1e3 for kname, v in per.items()}
+    p99 = {kname: float(np.percentile(v, 99)) * 1e3 for kname, v in per.items()}
 
     # The same step with the caches emptied first: before each of these steps a
     # 512 MiB buffer (twice the 256 MB MALL) is read, outside the events, so
@@ -466,6 +467,9 @@ def main() -> int:
         "kernel_us_mean": {kk: round(v, 2) for kk, v in us.items()},
         "kernel_us_p50": {kk: round(v, 2) for kk, v in p50.items()},
         "kernel_us_p95": {kk: round(v, 2) for kk, v in p95.items()},
+        "kernel_us_p99": {kk: round(v, 2) for kk, v in p99.items()},
+        "caches": "warm: steps back to back (x stays in the MALL between steps); "
+                  "*_after_flush: each step after a 512 MiB read empties L2 and the MALL",
         "copy_kernel_gbps": round(copy_gbps, 1),
         "sources_digest": digest,
     }
