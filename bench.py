@@ -22,8 +22,10 @@ per-kernel times of extra steps that each start with L2 and the MALL emptied
 `--workload` times the other named workloads (tiny, skewed, lowlat, large) the
 same way; the default is the configuration the metric is quoted on.  Variant
 flags: --fused (one-call layout+dispatch), --pow2 / --mx (power-of-two or
-MXFP8 scales), --fp8-combine (FP8 expert outputs), --f16 (fp16 rows),
---dedup (per-group dedup layout, dispatch and combine), --graph (HIP graph).
+MXFP8 scales), --mn-scales (dispatch stores its scales transposed),
+--mn-convert (row-major dispatch, then the scale-layout conversion kernel),
+--fp8-combine (FP8 expert outputs), --f16 (fp16 rows), --dedup (per-group dedup layout, dispatch
+and combine), --graph (HIP graph).
 """
 from __future__ import annotations
 
@@ -171,6 +173,11 @@ def main() -> int:
                          "of at most 2048 pairs); the layout/dispatch split is then not reported")
     ap.add_argument("--mx", action="store_true",
                     help="MXFP8 dispatch (EP_MXFP8_E4M3: one E8M0 scale byte per 32 channels)")
+    ap.add_argument("--mn-scales", action="store_true",
+                    help="the timed dispatch stores its scales MN-major (EP_SCALES_MN_MAJOR)")
+    ap.add_argument("--mn-convert", action="store_true",
+                    help="row-major dispatch followed by ep_scales_to_mn_major inside the "
+                         "dispatch interval (the conversion's bytes join the dispatch's)")
     ap.add_argument("--f16", action="store_true",
                     help="fp16 path: EP_F16 dispatch and ep_combine_f16 (a bf16 workload's shapes)")
     ap.add_argument("--dedup", action="store_true",
@@ -180,6 +187,14 @@ def main() -> int:
     if args.dedup and (args.fused or args.fp8_combine or args.graph or args.f16):
         print("--dedup times its own three calls; it combines with --pow2 and --mx only",
               file=sys.stderr)
+        return 2
+    if args.mn_convert and (args.mn_scales or args.fused or args.dedup or args.graph):
+        print("--mn-convert times layout, dispatch, conversion and combine as separate calls",
+              file=sys.stderr)
+        return 2
+    if args.mn_scales and args.fp8_combine:
+        print("--mn-scales does not combine with --fp8-combine (ep_combine_fp8 reads row-major "
+              "scales)", file=sys.stderr)
         return 2
     if args.mx and (args.pow2 or args.fp8_combine):
         print("--mx is its own scale format; it does not combine with --pow2 or --fp8-combine",
@@ -208,8 +223,9 @@ def main() -> int:
         return 2
     wl = W.make(name, seed=args.seed)
     T, H, E, G, k, fp8 = wl.T, wl.H, wl.E, wl.G, wl.k, wl.fp8
-    if (args.fp8_combine or args.mx or args.pow2) and not fp8:
-        print("--fp8-combine, --mx and --pow2 need an FP8 workload (dsv3, lowlat, large)",
+    if (args.fp8_combine or args.mx or args.pow2 or args.mn_scales or args.mn_convert) and not fp8:
+        print("--fp8-combine, --mx, --pow2, --mn-scales and --mn-convert need an FP8 workload "
+              "(dsv3, lowlat, large)",
               file=sys.stderr)
         return 2
     if args.f16:
@@ -218,6 +234,9 @@ def main() -> int:
         dtype_enum = B.EP_MXFP8_E4M3 if args.mx else B.EP_FP8_E4M3_POW2 if args.pow2 else B.EP_FP8_E4M3
     else:
         dtype_enum = B.EP_F16 if args.f16 else B.EP_BF16
+    # the timed dispatch's dtype; the untimed set-up below writes row-major
+    # scales for the identity-expert stand-in
+    step_dtype = dtype_enum | (B.EP_SCALES_MN_MAJOR if args.mn_scales else 0)
     if args.f16:
         # fp16 activations of the same distribution (the bf16 values, converted)
         x = torch.from_numpy(wl.x_bits.view(np.int16)).to(dev).view(torch.bfloat16).to(torch.float16)
@@ -284,6 +303,11 @@ def main() -> int:
                  "dispatch_row_bytes": g_used * row_b, "dispatch_row_bytes_per_expert_path": used * row_b,
                  "combine_row_bytes": g_used * 2 * H, "combine_row_bytes_per_expert_path": used * 2 * H}
         nbytes = ideal_bytes_dedup(T, H, G, k, kg, g_used, fp8)
+    recv_s_mn = None
+    if args.mn_convert:
+        recv_s_mn = torch.empty(tuple(reversed(recv_s.shape)), dtype=recv_s.dtype, device=dev)
+        # every row's scales read once and written once
+        nbytes["scales_mn"] = 2 * R * (H // 128) * 4
     step_bytes = sum(nbytes.values())
 
     def step(ev=None, s=None):
@@ -295,7 +319,7 @@ def main() -> int:
             B.ep_get_group_layout(topk_idx, topk_w, glay, g_ridx, g_rw, s)
             if ev is not None:
                 ev[1].record(s)
-            B.ep_dispatch(x, glay, dtype_enum, g_q, g_s, s)
+            B.ep_dispatch(x, glay, step_dtype, g_q, g_s, s)
             if ev is not None:
                 ev[2].record(s)
             B.ep_combine_groups(g_z, glay, out, s)
@@ -303,14 +327,16 @@ def main() -> int:
                 ev[3].record(s)
             return
         if args.fused:
-            B.ep_layout_dispatch(topk_idx, lay, x, dtype_enum, recv_q, recv_s, s)
+            B.ep_layout_dispatch(topk_idx, lay, x, step_dtype, recv_q, recv_s, s)
             if ev is not None:
                 ev[1].record(s)
         else:
             B.ep_get_layout(topk_idx, lay, s)
             if ev is not None:
                 ev[1].record(s)
-            B.ep_dispatch(x, lay, dtype_enum, recv_q, recv_s, s)
+            B.ep_dispatch(x, lay, step_dtype, recv_q, recv_s, s)
+            if recv_s_mn is not None:
+                B.ep_scales_to_mn_major(recv_s, H, dtype_enum, recv_s_mn, s)
         if ev is not None:
             ev[2].record(s)
         if args.fp8_combine:
@@ -423,10 +449,22 @@ def main() -> int:
     copy_gbps = 2 * copy_bytes * reps / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
+    # the scale-layout conversion alone (its share of the dispatch interval)
+    convert = None
+    if recv_s_mn is not None:
+        c0.record(stream)
+        for _ in range(50):
+            B.ep_scales_to_mn_major(recv_s, H, dtype_enum, recv_s_mn, stream)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        conv_us = c0.elapsed_time(c1) * 1e3 / 50
+        convert = {"us": round(conv_us, 2), "bytes": nbytes["scales_mn"],
+                   "gbps": round(nbytes["scales_mn"] / (conv_us * 1e-6) / 1e9, 1)}
+
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     if graph is None:
         t_dispatch = us["layout_dispatch"] if args.fused else us["dispatch"]
-        d_bytes = nbytes["dispatch"] + (nbytes["layout"] if args.fused else 0)
+        d_bytes = nbytes["dispatch"] + (nbytes["layout"] if args.fused else 0) + nbytes.get("scales_mn", 0)
         dc_gbps = (d_bytes + nbytes["combine"]) / ((t_dispatch + us["combine"]) * 1e-6) / 1e9
         combine_gbps = nbytes["combine"] / (us["combine"] * 1e-6) / 1e9
         dispatch_gbps = d_bytes / (t_dispatch * 1e-6) / 1e9
@@ -454,7 +492,10 @@ def main() -> int:
                    "experts": E, "groups": G, "topk": k, "capacity": wl.cap,
                    "dispatch_dtype": ("mxfp8 (e4m3+e8m0 scale/32ch)" if args.mx else
                                       "fp8_e4m3+pow2 scale/128ch" if args.pow2 else
-                                      "fp8_e4m3+fp32 scale/128ch") if fp8 else
+                                      "fp8_e4m3+fp32 scale/128ch") +
+                                     (", scales MN-major" if args.mn_scales else
+                                      ", then scales converted to MN-major" if args.mn_convert
+                                      else "") if fp8 else
                                      "fp16" if args.f16 else "bf16",
                    "combine_dtype": "fp8_e4m3 in, bf16 out" if args.fp8_combine else
                                     "fp16" if args.f16 else "bf16",
@@ -488,13 +529,16 @@ def main() -> int:
         result["config"]["step"] += " (HIP graph replay)"
     if flushed is not None:
         d_key = "layout_dispatch" if args.fused else "dispatch"
-        d_bytes_f = nbytes["dispatch"] + (nbytes["layout"] if args.fused else 0)
+        d_bytes_f = nbytes["dispatch"] + (nbytes["layout"] if args.fused else 0) + nbytes.get("scales_mn", 0)
         result["kernel_us_mean_after_flush"] = flushed
         result["dispatch_plus_combine_gbps_after_flush"] = round(
             (d_bytes_f + nbytes["combine"]) / ((flushed[d_key] + flushed["combine"]) * 1e-6) / 1e9, 1)
     if dedup is not None:
         result["dedup"] = dedup
-    default_path = not (args.dedup or args.mx or args.f16 or args.pow2 or args.fp8_combine)
+    if convert is not None:
+        result["scales_mn_conversion"] = convert
+    default_path = not (args.dedup or args.mx or args.f16 or args.pow2 or args.fp8_combine
+                        or args.mn_scales or args.mn_convert)
     if not args.no_cpu_baseline and name == "dsv3" and default_path:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

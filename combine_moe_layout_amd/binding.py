@@ -20,6 +20,7 @@ EP_FP8_E4M3 = 1
 EP_FP8_E4M3_POW2 = 2
 EP_MXFP8_E4M3 = 3
 EP_F16 = 4
+EP_SCALES_MN_MAJOR = 0x100   # OR-ed into an FP8 dtype: scales stored transposed
 _FP8_DTYPES = (EP_FP8_E4M3, EP_FP8_E4M3_POW2, EP_MXFP8_E4M3)
 EP_FLAG_BAD_EXPERT = 1
 EP_FLAG_OVERFLOW = 2
@@ -61,6 +62,7 @@ SIGNATURES = {
     "ep_get_layout": (ctypes.c_int, [_vp, _LP, _vp, _sz, _vp]),
     "ep_dispatch": (ctypes.c_int, [_vp, _LP, _i32, _i32, _vp, _vp, _vp]),
     "ep_layout_dispatch": (ctypes.c_int, [_vp, _LP, _vp, _sz, _vp, _i32, _i32, _vp, _vp, _vp]),
+    "ep_scales_to_mn_major": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp]),
     "ep_combine": (ctypes.c_int, [_vp, _vp, _LP, _i32, _vp, _vp]),
     "ep_combine_fp8": (ctypes.c_int, [_vp, _vp, _vp, _LP, _i32, _vp, _vp]),
     "ep_combine_f16": (ctypes.c_int, [_vp, _vp, _LP, _i32, _vp, _vp]),
@@ -209,7 +211,9 @@ def ep_get_layout(topk_idx: torch.Tensor, layout: EpLayout, stream=None) -> EpLa
 
 
 def _dispatch_types(recv_dtype: int):
-    """(x dtype, recv_x dtype, recv_scales dtype) of a receive dtype."""
+    """(x dtype, recv_x dtype, recv_scales dtype) of a receive dtype (with or
+    without EP_SCALES_MN_MAJOR)."""
+    recv_dtype &= ~EP_SCALES_MN_MAJOR
     if recv_dtype == EP_F16:
         return torch.float16, torch.float16, None
     if recv_dtype == EP_MXFP8_E4M3:
@@ -219,14 +223,23 @@ def _dispatch_types(recv_dtype: int):
     return torch.bfloat16, torch.bfloat16, None
 
 
+def _check_scales(recv_dtype: int, recv_scales, R: int, H: int) -> None:
+    """Every FP8 scale layout holds H/128 four-byte words per receive row."""
+    if (recv_dtype & ~EP_SCALES_MN_MAJOR) in _FP8_DTYPES and recv_scales is not None:
+        if recv_scales.numel() * recv_scales.element_size() != R * (H // 128) * 4:
+            raise ValueError("recv_scales does not hold %d rows of %d channels' scales" % (R, H))
+
+
 def ep_dispatch(x: torch.Tensor, layout: EpLayout, recv_dtype: int, recv_x: torch.Tensor,
                 recv_scales: torch.Tensor | None = None, stream=None) -> None:
     """x bf16 [T, H] -> recv_x: bf16 [R, H]; uint8 [R, H] FP8 codes with
     recv_scales fp32 [R, H/128] (EP_FP8_E4M3, EP_FP8_E4M3_POW2) or uint8
-    [R, H/32] E8M0 bytes (EP_MXFP8_E4M3).  EP_F16: x and recv_x fp16."""
+    [R, H/32] E8M0 bytes (EP_MXFP8_E4M3), or their transposes [H/128, R] and
+    [H/32, R] with EP_SCALES_MN_MAJOR.  EP_F16: x and recv_x fp16."""
     T, H = layout.num_tokens, x.shape[-1]
     if tuple(x.shape) != (T, H) or recv_x.shape[0] != layout.num_recv_rows or recv_x.shape[-1] != H:
         raise ValueError("dispatch buffers do not match the layout")
+    _check_scales(recv_dtype, recv_scales, layout.num_recv_rows, H)
     xt, rt, st = _dispatch_types(recv_dtype)
     _check("ep_dispatch", lib().ep_dispatch(
         _ptr(x, "x", xt), ctypes.byref(layout.struct), H, recv_dtype,
@@ -243,6 +256,7 @@ def ep_layout_dispatch(topk_idx: torch.Tensor, layout: EpLayout, x: torch.Tensor
         raise ValueError("topk_idx shape %s does not match the layout" % (tuple(topk_idx.shape),))
     if tuple(x.shape) != (T, H) or recv_x.shape[0] != layout.num_recv_rows or recv_x.shape[-1] != H:
         raise ValueError("dispatch buffers do not match the layout")
+    _check_scales(recv_dtype, recv_scales, layout.num_recv_rows, H)
     xt, rt, st = _dispatch_types(recv_dtype)
     _check("ep_layout_dispatch", lib().ep_layout_dispatch(
         _ptr(topk_idx, "topk_idx", torch.int64) if topk_idx.numel() else None,
@@ -348,6 +362,23 @@ def ep_dequant_mxfp8(q: torch.Tensor, scales: torch.Tensor, y: torch.Tensor, str
     _check("ep_dequant_mxfp8", lib().ep_dequant_mxfp8(
         _ptr(q, "q", torch.uint8), _ptr(scales, "scales", torch.uint8), rows, H,
         _ptr(y, "y", torch.bfloat16), _stream(stream)))
+
+
+def ep_scales_to_mn_major(scales: torch.Tensor, hidden: int, recv_dtype: int, scales_mn: torch.Tensor,
+                          stream=None) -> None:
+    """Row-major scales of an FP8 dispatch (fp32 [R, H/128] or MXFP8 uint8
+    [R, H/32]) -> their MN-major layout ([H/128, R] or [H/32, R])."""
+    recv_dtype &= ~EP_SCALES_MN_MAJOR
+    if recv_dtype not in _FP8_DTYPES:
+        raise ValueError("recv_dtype %d has no scales" % recv_dtype)
+    per_row = hidden // 32 if recv_dtype == EP_MXFP8_E4M3 else hidden // 128
+    rows = scales.shape[0]
+    if tuple(scales.shape) != (rows, per_row) or tuple(scales_mn.shape) != (per_row, rows):
+        raise ValueError("scale buffers disagree: %s -> %s" % (tuple(scales.shape), tuple(scales_mn.shape)))
+    st = torch.uint8 if recv_dtype == EP_MXFP8_E4M3 else torch.float32
+    _check("ep_scales_to_mn_major", lib().ep_scales_to_mn_major(
+        _ptr(scales, "scales", st), rows, hidden, recv_dtype, _ptr(scales_mn, "scales_mn", st),
+        _stream(stream)))
 
 
 def ep_cast_e4m3_bits(first: int, n: int, method: int, out: torch.Tensor, stream=None) -> None:

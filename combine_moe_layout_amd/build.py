@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libep.so")
 SOURCES = ["ep_api.hip", "ep_layout.hip", "ep_dispatch.hip", "ep_fused.hip", "ep_combine.hip",
-           "ep_group.hip", "ep_aux.hip"]
+           "ep_group.hip", "ep_scales.hip", "ep_aux.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -55,9 +55,10 @@ int check_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* w
 // Checks shared by ep_dispatch and ep_layout_dispatch (after the layout's).
 int check_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,
                    void* recv_x, void* recv_scales) {
-  if (recv_dtype != EP_BF16 && recv_dtype != EP_F16 && !ep::dtype_is_fp8(recv_dtype))
-    return EP_ERR_DTYPE;
-  const bool fp8 = ep::dtype_is_fp8(recv_dtype);
+  const int32_t base = ep::dtype_base(recv_dtype);
+  const bool fp8 = ep::dtype_is_fp8(base);
+  if (base != EP_BF16 && base != EP_F16 && !fp8) return EP_ERR_DTYPE;
+  if (ep::dtype_scales_mn(recv_dtype) && !fp8) return EP_ERR_DTYPE;
   if (hidden < 8 || hidden > EP_MAX_HIDDEN || hidden % 8 != 0 || (fp8 && hidden % 128 != 0))
     return EP_ERR_SHAPE;
   if (layout->num_tokens == 0) return EP_OK;
@@ -260,6 +261,24 @@ int ep_dequant_mxfp8(const uint8_t* q, const uint8_t* scales, int64_t rows, int3
   if (!aligned16(q) || !aligned16(y)) return EP_ERR_ALIGN;
   return launch_status(
       ep::launch_dequant_mxfp8(q, scales, rows, hidden, y, static_cast<hipStream_t>(stream)));
+}
+
+int ep_scales_to_mn_major(const void* scales, int64_t rows, int32_t hidden, int32_t recv_dtype,
+                          void* scales_mn, void* stream) {
+  if (!ep::dtype_is_fp8(recv_dtype)) return EP_ERR_DTYPE;
+  if (rows < 0 || hidden < 128 || hidden > EP_MAX_HIDDEN || hidden % 128 != 0)
+    return EP_ERR_SHAPE;
+  if (rows == 0) return EP_OK;
+  if (scales == nullptr || scales_mn == nullptr) return EP_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(scales) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(scales_mn) & 3u) != 0)
+    return EP_ERR_ALIGN;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(scales);
+  const uintptr_t b = reinterpret_cast<uintptr_t>(scales_mn);
+  const uintptr_t bytes = (uintptr_t)rows * (uintptr_t)(hidden / 32);
+  if (a < b + bytes && b < a + bytes) return EP_ERR_SHAPE;  // the buffers overlap
+  return launch_status(ep::launch_scales_mn(scales, rows, hidden, recv_dtype, scales_mn,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int ep_cast_e4m3_bits(uint32_t first, int64_t n, int32_t method, uint8_t* out, void* stream) {

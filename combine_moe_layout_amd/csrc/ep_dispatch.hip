@@ -56,11 +56,12 @@ __global__ __launch_bounds__(1024) void dispatch_bf16_kernel(
 // Codes go to the receive rows with non-temporal stores.  The block scales are
 // staged in LDS and written afterwards row by row by consecutive lanes, so each
 // receive row's scales leave as one contiguous run instead of 4-byte pieces
-// from separate waves.
+// from separate waves; mn_rows > 0 selects the MN-major scale layout instead.
 template <bool kHw, int kMode>
 __global__ __launch_bounds__(1024) void dispatch_fp8_kernel(
     const u32x4* __restrict__ x, int64_t num_tokens, int32_t k, int32_t hidden, TokenMap m,
-    const int32_t* __restrict__ slot_idx, u32x4* __restrict__ recv, uint32_t* __restrict__ scales) {
+    const int32_t* __restrict__ slot_idx, u32x4* __restrict__ recv, uint32_t* __restrict__ scales,
+    int64_t mn_rows) {
   __shared__ uint32_t s_scale[kMaxScalesPerBlock];
   int64_t t;
   int32_t lt;
@@ -72,7 +73,8 @@ __global__ __launch_bounds__(1024) void dispatch_fp8_kernel(
                                 slot_idx + t * k, k, recv, my_scales);
   __syncthreads();
   if (t < num_tokens)
-    fp8_token_scales(hidden, lt, m.lanes_per_token, slot_idx + t * k, k, my_scales, scales);
+    fp8_token_scales_any<kMode>(hidden, lt, m.lanes_per_token, slot_idx + t * k, k, my_scales,
+                                mn_rows, scales);
 }
 
 // Lanes per token: one lane per vector when that fits a workgroup (rounded up
@@ -97,6 +99,8 @@ hipError_t launch_dispatch(const void* x, const ep_layout_t& L, int32_t hidden, 
                            void* recv_x, void* recv_scales, hipStream_t stream) {
   const int64_t T = L.num_tokens;
   if (T == 0) return hipSuccess;
+  const int64_t mn_rows = dtype_scales_mn(dtype) ? L.num_recv_rows : 0;
+  dtype = dtype_base(dtype);
   const bool fp8 = dtype_is_fp8(dtype);
   uint32_t* sw = static_cast<uint32_t*>(recv_scales);
   const TokenMap m = token_map(fp8 ? hidden / 16 : hidden / 8);
@@ -106,13 +110,13 @@ hipError_t launch_dispatch(const void* x, const ep_layout_t& L, int32_t hidden, 
   u32x4* rv = static_cast<u32x4*>(recv_x);
   if (dtype == EP_FP8_E4M3)
     hipLaunchKernelGGL((dispatch_fp8_kernel<kDispatchUsesHwCast, kScaleF32>), grid, block, 0,
-                       stream, xv, T, L.num_topk, hidden, m, L.slot_idx, rv, sw);
+                       stream, xv, T, L.num_topk, hidden, m, L.slot_idx, rv, sw, mn_rows);
   else if (dtype == EP_FP8_E4M3_POW2)
     hipLaunchKernelGGL((dispatch_fp8_kernel<kDispatchUsesHwCast, kScalePow2>), grid, block, 0,
-                       stream, xv, T, L.num_topk, hidden, m, L.slot_idx, rv, sw);
+                       stream, xv, T, L.num_topk, hidden, m, L.slot_idx, rv, sw, mn_rows);
   else if (dtype == EP_MXFP8_E4M3)
     hipLaunchKernelGGL((dispatch_fp8_kernel<kDispatchUsesHwCast, kScaleMx>), grid, block, 0,
-                       stream, xv, T, L.num_topk, hidden, m, L.slot_idx, rv, sw);
+                       stream, xv, T, L.num_topk, hidden, m, L.slot_idx, rv, sw, mn_rows);
   else  // EP_BF16 and EP_F16: a bit copy of 2-byte elements
     hipLaunchKernelGGL(dispatch_bf16_kernel, grid, block, 0, stream, xv, T, L.num_topk, hidden, m,
                        L.slot_idx, rv);

@@ -148,4 +148,42 @@ __device__ __forceinline__ void fp8_token_scales(int32_t hidden, int32_t lt, int
   }
 }
 
+// The MN-major (transposed) scale layout: entry c of receive row s goes to
+// c * rows + s, so one block column's entries for consecutive rows are
+// contiguous.  Entries are the 4-byte scale words (one per 128 channels) or,
+// with kBytes, the MXFP8 E8M0 bytes (one per 32 channels).  Ordinary stores:
+// the entries of neighbouring rows share cache lines and merge in the caches.
+template <bool kBytes>
+__device__ __forceinline__ void fp8_token_scales_mn(int32_t hidden, int32_t lt, int32_t lanes,
+                                                    const int32_t* slots, int32_t k,
+                                                    const uint32_t* my_scales, int64_t rows,
+                                                    void* __restrict__ scales) {
+  const int32_t per_row = kBytes ? hidden / 32 : hidden / kFp8Block;
+  const int32_t n = k * per_row;
+  for (int32_t i = lt; i < n; i += lanes) {
+    const int32_t j = i / per_row;
+    const int32_t c = i - j * per_row;
+    const int32_t s = slots[j];
+    if (s < 0) continue;
+    const int64_t at = (int64_t)c * rows + s;
+    if constexpr (kBytes)
+      static_cast<uint8_t*>(scales)[at] = reinterpret_cast<const uint8_t*>(my_scales)[c];
+    else
+      static_cast<uint32_t*>(scales)[at] = my_scales[c];
+  }
+}
+
+// Writes the staged scales of one token in the layout the caller chose:
+// row-major when mn_rows == 0, else MN-major over mn_rows receive rows.
+template <int kMode>
+__device__ __forceinline__ void fp8_token_scales_any(int32_t hidden, int32_t lt, int32_t lanes,
+                                                     const int32_t* slots, int32_t k,
+                                                     const uint32_t* my_scales, int64_t mn_rows,
+                                                     uint32_t* __restrict__ scales) {
+  if (mn_rows > 0)
+    fp8_token_scales_mn<kMode == kScaleMx>(hidden, lt, lanes, slots, k, my_scales, mn_rows, scales);
+  else
+    fp8_token_scales(hidden, lt, lanes, slots, k, my_scales, scales);
+}
+
 }  // namespace ep

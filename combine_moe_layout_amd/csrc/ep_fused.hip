@@ -31,6 +31,7 @@ struct FusedArgs {
   const u32x4* x;
   u32x4* recv;
   uint32_t* scales;
+  int64_t scales_mn_rows;  // 0: row-major scales; else MN-major over this many rows
   int32_t* slot_idx;
   int32_t* recv_src;
   int32_t* num_tokens_per_expert;
@@ -203,7 +204,8 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
   }
   if constexpr (kFp8) {
     __syncthreads();
-    fp8_token_scales(a.hidden, tid, blockDim.x, s_slot, k, s_scale, a.scales);
+    fp8_token_scales_any<kMode>(a.hidden, tid, blockDim.x, s_slot, k, s_scale, a.scales_mn_rows,
+                                a.scales);
   }
 }
 
@@ -215,6 +217,8 @@ bool fused_layout_dispatch_fits(const ep_layout_t& L) {
 hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout_t& L,
                                         const void* x, int32_t hidden, int32_t dtype,
                                         void* recv_x, void* recv_scales, hipStream_t stream) {
+  const int64_t mn_rows = dtype_scales_mn(dtype) ? L.num_recv_rows : 0;
+  dtype = dtype_base(dtype);
   const bool fp8 = dtype_is_fp8(dtype);
   FusedArgs a;
   a.topk_idx = topk_idx;
@@ -227,6 +231,7 @@ hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout
   a.x = static_cast<const u32x4*>(x);
   a.recv = static_cast<u32x4*>(recv_x);
   a.scales = static_cast<uint32_t*>(recv_scales);
+  a.scales_mn_rows = mn_rows;
   a.slot_idx = L.slot_idx;
   a.recv_src = L.recv_src;
   a.num_tokens_per_expert = L.num_tokens_per_expert;

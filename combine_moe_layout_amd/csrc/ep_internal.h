@@ -41,10 +41,20 @@ inline bool dtype_is_fp8(int32_t dtype) {
   return dtype == EP_FP8_E4M3 || dtype == EP_FP8_E4M3_POW2 || dtype == EP_MXFP8_E4M3;
 }
 
+// A dispatch dtype splits into its element type and the MN-major scale flag.
+inline int32_t dtype_base(int32_t dtype) { return dtype & ~EP_SCALES_MN_MAJOR; }
+inline bool dtype_scales_mn(int32_t dtype) { return (dtype & EP_SCALES_MN_MAJOR) != 0; }
+
 // recv_scales: fp32 [R, hidden/128] or, for EP_MXFP8_E4M3, E8M0 bytes
-// [R, hidden/32]: hidden/128 4-byte words per row either way.
+// [R, hidden/32]: hidden/128 4-byte words per row either way.  With
+// EP_SCALES_MN_MAJOR in dtype the same entries are stored transposed.
 hipError_t launch_dispatch(const void* x, const ep_layout_t& L, int32_t hidden, int32_t dtype,
                            void* recv_x, void* recv_scales, hipStream_t stream);
+
+// Row-major scales of `rows` rows (the layout an FP8 dispatch of dtype writes
+// without EP_SCALES_MN_MAJOR) -> the MN-major layout, every row.
+hipError_t launch_scales_mn(const void* scales, int64_t rows, int32_t hidden, int32_t dtype,
+                            void* scales_mn, hipStream_t stream);
 
 hipError_t launch_combine(const void* y, const float* w, const ep_layout_t& L, int32_t hidden,
                           void* out, hipStream_t stream);

@@ -70,6 +70,13 @@ enum ep_dtype {
     EP_F16 = 4            /* fp16 rows: x is fp16 and the rows are a bit copy of it */
 };
 
+/* Flag OR-ed into an FP8 receive dtype (EP_FP8_E4M3, EP_FP8_E4M3_POW2 or
+ * EP_MXFP8_E4M3) of ep_dispatch / ep_layout_dispatch: the scales are stored
+ * transposed (MN-major), see ep_dispatch. */
+enum ep_dtype_flag {
+    EP_SCALES_MN_MAJOR = 0x100
+};
+
 /* Bits of layout->error_flags, written by ep_get_layout. */
 enum ep_flag {
     EP_FLAG_BAD_EXPERT = 1, /* some topk_idx entry is outside [-1, num_experts) */
@@ -164,12 +171,39 @@ int ep_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* work
  *                an all-zero block), byte = se + 127, code = nearest E4M3 (ties
  *                to even) of clamp(x / 2^se, -448, 448); requires hidden % 128 == 0.
  *   EP_F16:      x is fp16 [T, hidden] and recv_x fp16 [R, hidden], a bit copy.
+ * FP8 dtype | EP_SCALES_MN_MAJOR: the same codes and scale values, with the
+ *                scales stored transposed: fp32 [hidden/128, R] (E8M0 bytes
+ *                [hidden/32, R] for MXFP8), entry c of receive row r at
+ *                c * R + r, so the scales of one block column over an expert's
+ *                consecutive rows are contiguous (the scale-layout conversion
+ *                that section "FP8與低精度通訊" of [yololab] lists among the
+ *                checks, for GEMMs that read a tile's row scales together).
+ *                R is layout->num_recv_rows.  The flag with a non-FP8 dtype,
+ *                or any other extra bit, is EP_ERR_DTYPE.
  * recv_scales (fp32 or E8M0 rows) must be 4-byte aligned.
  * Rows that no slot names are left untouched.  hidden % 8 == 0.
  * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN, EP_ERR_DTYPE or EP_ERR_LAUNCH.
  */
 int ep_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,
                 void* recv_x, void* recv_scales, void* stream);
+
+/*
+ * Scale-layout conversion (the layout conversion [yololab] "FP8與低精度通訊"
+ * lists among the checks of low-precision dispatch): copies the row-major
+ * scales an ep_dispatch with FP8 recv_dtype wrote -- fp32 [rows, hidden/128]
+ * for EP_FP8_E4M3 and EP_FP8_E4M3_POW2, E8M0 bytes [rows, hidden/32] for
+ * EP_MXFP8_E4M3 -- into the MN-major layout that EP_SCALES_MN_MAJOR writes:
+ * entry c of row r to scales_mn[c * rows + r].  Every row is converted,
+ * including rows that no slot named (they carry whatever the source held).
+ * For large batches this pass (each scale byte read once and written once) is
+ * cheaper than dispatch's own MN-major stores, which scatter one store per
+ * entry; for decode-sized batches the flag avoids a launch.
+ * scales and scales_mn: device memory, 4-byte aligned, not overlapping.
+ * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE (hidden not a multiple of 128, or
+ * the buffers overlap), EP_ERR_ALIGN, EP_ERR_DTYPE or EP_ERR_LAUNCH.
+ */
+int ep_scales_to_mn_major(const void* scales, int64_t rows, int32_t hidden, int32_t recv_dtype,
+                          void* scales_mn, void* stream);
 
 /*
  * Layout and dispatch in one call: the same results as ep_get_layout followed

@@ -49,6 +49,19 @@ def test_binding_mirrors_the_header():
     assert sorted(binding.SIGNATURES) == header_functions()
 
 
+def test_binding_constants_match_the_header():
+    """Every EP_* enumerator and limit the header defines has the same value
+    in the binding."""
+    text = open(HEADER).read()
+    found = dict(re.findall(r"\b(EP_[A-Z0-9_]+)\s*=\s*(-?(?:0x[0-9A-Fa-f]+|\d+))", text))
+    found.update(re.findall(r"#define\s+(EP_MAX_[A-Z]+)\s+(\d+)", text))
+    assert len(found) >= 18
+    for name, val in found.items():
+        if name.startswith("EP_ERR_"):
+            continue                       # status codes are read through ep_status_string
+        assert getattr(binding, name) == int(val, 0), name
+
+
 def test_library_has_no_oracle_code(L):
     nm = subprocess.run(["nm", "-D", binding.library_path()], capture_output=True, text=True,
                         check=True).stdout
@@ -145,9 +158,30 @@ def test_entry_points_reject_bad_arguments(L):
     assert L.ep_dispatch(fake, by(s), 256, 3, fake, fake + 1, None) == -3   # scale words aligned
     assert L.ep_dispatch(fake, by(s), 256, 5, fake, None, None) == -6       # no dtype 5
     assert L.ep_dispatch(fake + 2, by(s), 256, 4, fake, None, None) == -3   # fp16 x alignment
+    # the MN-major scale flag: only on FP8 dtypes, no other extra bits
+    mn = binding.EP_SCALES_MN_MAJOR
+    assert L.ep_dispatch(fake, by(s), 256, mn | 0, fake, None, None) == -6  # bf16 has no scales
+    assert L.ep_dispatch(fake, by(s), 256, mn | 4, fake, None, None) == -6  # nor fp16
+    assert L.ep_dispatch(fake, by(s), 256, 0x200 | 1, fake, fake, None) == -6
+    assert L.ep_dispatch(fake, by(s), 256, mn | 9, fake, fake, None) == -6
+    assert L.ep_dispatch(fake, by(s), 200, mn | 1, fake, fake, None) == -2  # H % 128 still
+    assert L.ep_dispatch(fake, by(s), 256, mn | 2, fake, None, None) == -1  # scales required
+    assert L.ep_dispatch(fake, by(s), 256, mn | 3, fake, fake + 1, None) == -3
+    assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake, 256, mn | 0, fake, None, None) == -6
+    assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake, 256, mn | 1, fake, None, None) == -1
     assert L.ep_combine_f16(None, fake, by(s), 256, fake, None) == -1
     assert L.ep_combine_f16(fake, fake, by(s), 252, fake, None) == -2
     assert L.ep_combine_f16(fake, fake, by(s), 256, fake + 8, None) == -3
+    # scale-layout conversion
+    assert L.ep_scales_to_mn_major(fake, 10, 256, 0, fake * 2, None) == -6      # bf16 has no scales
+    assert L.ep_scales_to_mn_major(fake, 10, 256, mn | 1, fake * 2, None) == -6 # a dtype, not a flag
+    assert L.ep_scales_to_mn_major(fake, 10, 200, 1, fake * 2, None) == -2      # H % 128
+    assert L.ep_scales_to_mn_major(fake, -1, 256, 1, fake * 2, None) == -2
+    assert L.ep_scales_to_mn_major(None, 10, 256, 3, fake * 2, None) == -1
+    assert L.ep_scales_to_mn_major(fake + 2, 10, 256, 1, fake * 2, None) == -3
+    assert L.ep_scales_to_mn_major(fake, 10, 256, 1, fake + 40, None) == -2     # overlap
+    assert L.ep_scales_to_mn_major(fake, 10, 256, 3, fake + 76, None) == -2     # 10 rows x 8 bytes
+    assert L.ep_scales_to_mn_major(None, 0, 256, 1, None, None) == 0            # nothing to do
     # auxiliaries
     assert L.ep_dequant_mxfp8(fake, fake, 4, 96, fake, None) == -2
     assert L.ep_dequant_mxfp8(fake, None, 4, 128, fake, None) == -1
