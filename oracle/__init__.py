@@ -6,7 +6,7 @@ never imports, loads or calls it, and it shares no code with the HIP library.
 
 This module is a thin numpy <-> ctypes wrapper around ``ep_oracle.c``: plain,
 single-threaded scalar loops written from the definitions on the pages (cited
-in that file's header, with the readings R1..R14 it takes where the pages are
+in that file's header, with the readings R1..R20 it takes where the pages are
 silent).  Every function here only marshals arrays; all arithmetic is in C.
 """
 from __future__ import annotations
@@ -58,6 +58,7 @@ def _load(path: str) -> ctypes.CDLL:
     L.ep_oracle_dispatch_bf16.argtypes = [vp, i64, i32, i32, vp, vp]
     L.ep_oracle_quantize_token_fp8.argtypes = [vp, i32, vp, vp]
     L.ep_oracle_dispatch_fp8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    L.ep_oracle_scales_mn_major.argtypes = [vp, i64, i32, i32, vp]
     L.ep_oracle_dequant_fp8.argtypes = [vp, vp, i64, i32, vp]
     L.ep_oracle_combine.argtypes = [vp, vp, vp, i64, i32, i32, vp]
     L.ep_oracle_combine_tokens.argtypes = [vp, vp, vp, i32, i32, vp, i64, vp]
@@ -436,4 +437,14 @@ def combine_f16_tokens(y_bits: np.ndarray, w: np.ndarray, slot_idx: np.ndarray, 
     out = np.empty((tokens.size, H), np.uint16)
     lib().ep_oracle_combine_f16_tokens(_p(y_bits), _p(w), _p(slot_idx), k, H, _p(tokens),
                                        tokens.size, _p(out))
+    return out
+
+
+def scales_mn_major(scales: np.ndarray) -> np.ndarray:
+    """R20: row-major scales [R, n] (fp32 or E8M0 bytes) -> MN-major [n, R],
+    entry c of row r at c * R + r."""
+    src = np.ascontiguousarray(scales)
+    rows, n = src.shape
+    out = np.empty((n, rows), dtype=src.dtype)
+    lib().ep_oracle_scales_mn_major(_p(src), rows, n, src.dtype.itemsize, _p(out))
     return out

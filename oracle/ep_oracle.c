@@ -78,6 +78,10 @@
  *   R19 FP16 I/O variant: fp16 rows are dispatched as a bit copy; the fp16
  *       combine rounds the exact weighted sum once to binary16, nearest-even,
  *       subnormals kept, overflow to infinity.
+ *   R20 MN-major scale layout (the layout conversion that the FP8 section of
+ *       the yololab page asks to check; two pages say the v2 buffer adopts a
+ *       GEMM layout): the same scale entries, stored transposed, entry c of
+ *       receive row r at c * R + r.
  */
 #include <math.h>
 #include <stdint.h>
@@ -707,4 +711,14 @@ EXPORT void ep_oracle_combine_f16_tokens(const uint16_t* y, const float* w, cons
                                          uint16_t* out_rows) {
     for (int64_t i = 0; i < n; ++i)
         combine_f16_one(y, w, slot_idx, tokens[i], k, H, out_rows + i * H);
+}
+
+/* R20: row-major scale entries [rows, entries] of entry_bytes bytes each
+ * (4 for fp32 scales, 1 for E8M0 bytes) -> MN-major [entries, rows]. */
+EXPORT void ep_oracle_scales_mn_major(const uint8_t* src, int64_t rows, int32_t entries,
+                                      int32_t entry_bytes, uint8_t* dst) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t c = 0; c < entries; ++c)
+            memcpy(dst + ((int64_t)c * rows + r) * entry_bytes,
+                   src + (r * entries + c) * entry_bytes, (size_t)entry_bytes);
 }

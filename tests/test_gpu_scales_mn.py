@@ -9,7 +9,8 @@ conversion entry point ep_scales_to_mn_major is checked against the transpose
 it defines and against the flag's output.
 
 The bar is that of every dispatch: codes and scale bits identical to the
-oracle's, and every entry of a row that no slot names left as it was.
+oracle's (its scales in the MN-major layout, oracle.scales_mn_major), and
+every entry of a row that no slot names left as it was.
 """
 import numpy as np
 import pytest
@@ -63,9 +64,10 @@ def _check(dtype, x_bits, slot_idx, q, s, what):
     assert (qh[used] == oq[used]).all(), "%s: codes" % what
     assert (qh[~used] == SENTINEL).all(), "%s: codes of unused rows" % what
     sb = _scale_bytes(s)                                          # [c, R, bytes]
-    ob = np.ascontiguousarray(os_).view(np.uint8).reshape(R, sb.shape[0], sb.shape[2])
-    assert (sb.transpose(1, 0, 2)[used] == ob[used]).all(), "%s: scales" % what
-    assert (sb.transpose(1, 0, 2)[~used] == SENTINEL).all(), "%s: scales of unused rows" % what
+    ob = oracle.scales_mn_major(os_)                              # the oracle's, MN-major
+    ob = ob.view(np.uint8).reshape(sb.shape)
+    assert (sb[:, used] == ob[:, used]).all(), "%s: scales" % what
+    assert (sb[:, ~used] == SENTINEL).all(), "%s: scales of unused rows" % what
     note("%s: %d rows used of %d" % (what, int(used.sum()), R))
 
 
@@ -195,7 +197,7 @@ def test_scales_to_mn_major_is_the_transpose(rows, H, offset, dtype):
     got = dbuf.cpu().numpy()
     assert (got[:offset] == SENTINEL).all() and (got[offset + n_bytes:] == SENTINEL).all()
     got = got[offset:offset + n_bytes].view(src.dtype).reshape(per_row, rows)
-    assert (got == src.T).all()
+    assert (got == oracle.scales_mn_major(src)).all()
 
 
 @pytest.mark.parametrize("dtype", FP8_KINDS)

@@ -27,6 +27,7 @@ import test_oracle_dispatch_combine as pins_dc
 import test_oracle_mx_f16 as pins_mx
 import test_oracle_formats as pins_fmt
 import test_oracle_layout as pins_lay
+import test_oracle_scales_mn as pins_mn
 import test_oracle_variants as pins_var
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ep_oracle.c")
@@ -100,6 +101,8 @@ MUTANTS = [
     ("fp16 decode exponent bias", "ldexp(1024.0 + m, e - 15 - 10)", "ldexp(1024.0 + m, e - 14 - 10)"),
     ("fp16 combine forgets the weight", "acc += (double)w[t * k + j] * ep_oracle_f16_to_double(",
      "acc += ep_oracle_f16_to_double("),
+    ("MN-major layout indexed row-major", "memcpy(dst + ((int64_t)c * rows + r) * entry_bytes,",
+     "memcpy(dst + (r * entries + c) * entry_bytes,"),
     ("group combine drops the last group",
      "for (int32_t i = 0; i < kg; ++i) {\n            int32_t r = group_slot[t * kg + i];",
      "for (int32_t i = 0; i < kg - 1; ++i) {\n            int32_t r = group_slot[t * kg + i];"),
@@ -151,6 +154,9 @@ def _battery():
                pins_mx.test_combine_f16_golden,
                pins_mx.test_combine_f16_one_hot_is_a_gather_and_round_trip_is_exact,
                pins_mx.test_combine_f16_is_the_rounded_exact_sum]
+    checks += [lambda: pins_mn.test_scales_mn_major_matches_index_loops(3, 5),
+               lambda: pins_mn.test_scales_mn_major_matches_index_loops(17, 56),
+               lambda: pins_mn.test_mn_major_columns_are_the_tokens_scales(False)]
     return checks
 
 
