@@ -7,13 +7,16 @@
 // batch of at most kFusedMaxPairs (token, k) pairs this kernel computes the
 // same layout as ep_get_layout and the same receive rows as ep_dispatch, with
 // one launch and no barrier between workgroups:
-//   - every workgroup loads the whole (small) top-k table into LDS;
+//   - every workgroup loads the whole (small) top-k table into LDS; a token's
+//     workgroup first issues the loads of its token's row, so that their
+//     latency overlaps the table's;
 //   - workgroup t < T finds its own token's receive rows directly: for each of
 //     its k pairs, the number of valid pairs routed to a lower expert (the
 //     expert's offset, contiguous mode) plus the number of earlier pairs
 //     routed to the same expert (its rank; padded mode keeps rank < capacity),
-//     counted over the table by all lanes and summed across the workgroup --
-//     exactly the stable counting-sort position ep_get_layout assigns;
+//     counted over the table with one ballot per wave and table slice and
+//     summed across the workgroup -- exactly the stable counting-sort position
+//     ep_get_layout assigns;
 //     it writes those slot_idx / recv_src entries and then dispatches the
 //     token like ep_dispatch;
 //   - workgroup T writes the per-expert counts, offsets, group totals and
@@ -39,12 +42,6 @@ struct FusedArgs {
   int32_t* num_tokens_per_group;
   int32_t* error_flags;
 };
-
-__device__ __forceinline__ int32_t wave_sum(int32_t v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 // Exclusive scan of n <= EP_MAX_EXPERTS values in LDS (in place into out),
 // returning the total; every thread of the block calls it.
@@ -94,6 +91,23 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
   const int E = a.num_experts, k = a.k;
   const int32_t P = (int32_t)(a.num_tokens * k);
 
+  // A token's workgroup loads its slice of the token first (when one pass of
+  // the lanes covers the row), so that this latency overlaps the table load
+  // and the table scan below.
+  const bool token_block = blockIdx.x < a.num_tokens;
+  const int32_t vecs = kFp8 ? a.hidden / 16 : a.hidden / 8;
+  const bool one_pass = vecs <= (int32_t)blockDim.x;
+  const u32x4* src = a.x + (int64_t)blockIdx.x * (a.hidden / 8);
+  u32x4 pre_lo = {0u, 0u, 0u, 0u}, pre_hi = {0u, 0u, 0u, 0u};
+  if (token_block && one_pass && tid < vecs) {
+    if constexpr (kFp8) {
+      pre_lo = src[2 * tid];
+      pre_hi = src[2 * tid + 1];
+    } else {
+      pre_lo = src[tid];
+    }
+  }
+
   bool bad = false;
   for (int32_t p = tid; p < P; p += blockDim.x) {
     const int64_t v = a.topk_idx[p];
@@ -132,22 +146,10 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
     return;
   }
 
-  // this token's receive rows
+  // this token's receive rows: per entry j, the valid pairs routed to a lower
+  // expert and the earlier pairs routed to the same expert, counted per wave
+  // with ballots (e[j] is the same for every lane) and summed over the waves
   const int64_t t = blockIdx.x;
-  // When one pass of the lanes covers the row, each lane's slice of the token
-  // is loaded now, so that its latency overlaps the table scan below.
-  const int32_t vecs = kFp8 ? a.hidden / 16 : a.hidden / 8;
-  const bool one_pass = vecs <= (int32_t)blockDim.x;
-  const u32x4* src = a.x + t * (a.hidden / 8);
-  u32x4 pre_lo = {0u, 0u, 0u, 0u}, pre_hi = {0u, 0u, 0u, 0u};
-  if (one_pass && tid < vecs) {
-    if constexpr (kFp8) {
-      pre_lo = src[2 * tid];
-      pre_hi = src[2 * tid + 1];
-    } else {
-      pre_lo = src[tid];
-    }
-  }
   const int32_t p0 = (int32_t)(t * k);
   int32_t e[kFusedMaxTopk], lower[kFusedMaxTopk], earlier[kFusedMaxTopk];
 #pragma unroll
@@ -156,21 +158,22 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
     lower[j] = 0;
     earlier[j] = 0;
   }
-  for (int32_t p = tid; p < P; p += blockDim.x) {
-    const int32_t ep = s_idx[p];
-    if (ep < 0) continue;
+  for (int32_t base = 0; base < P; base += blockDim.x) {  // the same trip count in every lane
+    const int32_t p = base + tid;
+    const int32_t ep = p < P ? s_idx[p] : -1;
 #pragma unroll
     for (int j = 0; j < kFusedMaxTopk; ++j) {
-      lower[j] += ep < e[j] ? 1 : 0;
-      earlier[j] += (ep == e[j] && p < p0 + j) ? 1 : 0;
+      lower[j] += __popcll(__ballot(ep >= 0 && ep < e[j]));
+      earlier[j] += __popcll(__ballot(ep >= 0 && ep == e[j] && p < p0 + j));
     }
   }
+  if (tid % kWave == 0) {
 #pragma unroll
-  for (int j = 0; j < kFusedMaxTopk; ++j) {
-    const int32_t l = wave_sum(lower[j]), r = wave_sum(earlier[j]);
-    if (tid % kWave == 0 && j < k) {
-      atomicAdd(&s_sum[j], l);
-      atomicAdd(&s_sum[kFusedMaxTopk + j], r);
+    for (int j = 0; j < kFusedMaxTopk; ++j) {
+      if (j < k) {
+        atomicAdd(&s_sum[j], lower[j]);
+        atomicAdd(&s_sum[kFusedMaxTopk + j], earlier[j]);
+      }
     }
   }
   __syncthreads();
