@@ -11,7 +11,7 @@
 // index p = t*k + j, so the layout is deterministic.
 //
 // The pairs are cut into chunks of kChunkPairs; one workgroup owns a chunk.
-//   phase 1 (count): each wave walks its 512 pairs in order, 64 at a time;
+//   phase 1 (count): each wave walks its kWavePairs pairs in order, 64 at a time;
 //      lanes that name the same expert find each other with one ballot per
 //      expert-id bit, the lowest such lane bumps the wave's private LDS
 //      histogram, and every lane's rank is the histogram value plus the
@@ -35,7 +35,7 @@ namespace ep {
 
 // Per-chunk counts up to this many ints are staged whole in LDS (all loads in
 // flight at once); larger matrices are summed from memory.
-constexpr int kStageInts = 12288;
+constexpr int kStageInts = 16384;
 static_assert(kStageInts % (4 * kLayoutThreads) == 0, "staging is done in whole 16-byte batches");
 static_assert(kStageInts >= kLayoutWaves * EP_MAX_EXPERTS,
               "phase-1 histograms alias the staging area");
@@ -195,19 +195,18 @@ __device__ __forceinline__ void chunk_totals(int32_t E, int32_t num_chunks, int6
 }
 
 // Phase 2 for chunk c, given every chunk's totals in memory.  kSingleChunk:
-// there is only this chunk, sh.tot and sh.pre are already set by the caller
-// and known_bad is its bad-id flag.  chunk_flags holds num_flags entries: one
-// per chunk, then any written by a kernel that prepared the ids.
+// there is only this chunk, and sh.tot and sh.pre are already set by the
+// caller.  For c == 0, flag_bits is the OR of this thread's share of the flag
+// entries (one per chunk, then any written by a kernel that prepared the ids),
+// which the caller loads at its start so that their latency is hidden.
 template <bool kSingleChunk>
 __device__ __forceinline__ void finish_chunk(
     int64_t num_pairs, int32_t E, int32_t num_groups, int32_t capacity, int32_t num_chunks,
-    int32_t num_flags,
-    int64_t c, const int32_t* __restrict__ chunk_count, const int32_t* __restrict__ chunk_flags,
-    LayoutShared& sh, const int32_t (&eid)[kLayoutItems], const int32_t (&local)[kLayoutItems],
+    int64_t c, const int32_t* __restrict__ chunk_count, LayoutShared& sh, const int32_t (&eid)[kLayoutItems], const int32_t (&local)[kLayoutItems],
     int32_t* __restrict__ slot_idx, int32_t* __restrict__ recv_src,
     int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ num_tokens_per_group, int32_t* __restrict__ error_flags,
-    int32_t known_bad) {
+    int32_t flag_bits) {
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
@@ -275,11 +274,7 @@ __device__ __forceinline__ void finish_chunk(
       for (int e = g * per_group; e < (g + 1) * per_group; ++e) s += sh.tot[e];
       num_tokens_per_group[g] = s;
     }
-    // the single chunk's own flag is known_bad; every other entry is read
-    int32_t bad = kSingleChunk ? known_bad : 0;
-    for (int cc = tid + (kSingleChunk ? 1 : 0); cc < num_flags; cc += kLayoutThreads)
-      bad |= chunk_flags[cc];
-    const int any_bad = __syncthreads_or(bad);
+    const int any_bad = __syncthreads_or(flag_bits);
     const int any_over = __syncthreads_or(over ? 1 : 0);
     if (tid == 0)
       error_flags[0] = (any_bad ? EP_FLAG_BAD_EXPERT : 0) | (any_over ? EP_FLAG_OVERFLOW : 0);
@@ -313,10 +308,21 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(LayoutArgs
   }
 }
 
+// OR of this thread's share of flag entries [first, num_flags).
+__device__ __forceinline__ int32_t load_flag_bits(const int32_t* __restrict__ chunk_flags,
+                                                  int32_t first, int32_t num_flags) {
+  int32_t bits = 0;
+  for (int32_t cc = first + threadIdx.x; cc < num_flags; cc += kLayoutThreads)
+    bits |= chunk_flags[cc];
+  return bits;
+}
+
 // Phase 2 (also the whole layout when there are no pairs).
 __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(LayoutArgs a) {
   __shared__ LayoutShared sh;
   int32_t eid[kLayoutItems], local[kLayoutItems];
+  // workgroup 0 reports the flags; their loads are issued first and used last
+  const int32_t flag_bits = blockIdx.x == 0 ? load_flag_bits(a.chunk_flags, 0, a.num_flags) : 0;
 #pragma unroll
   for (int i = 0; i < kLayoutItems; ++i) {
     const int64_t p = pair_of(blockIdx.x, i);
@@ -325,9 +331,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(LayoutArg
     local[i] = v >= 0 ? (v >> kExpertBits) : 0;
   }
   finish_chunk<false>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, a.num_chunks,
-                      a.num_flags, blockIdx.x, a.chunk_count, a.chunk_flags, sh, eid, local,
-                      a.slot_idx, a.recv_src, a.num_tokens_per_expert, a.expert_offsets,
-                      a.num_tokens_per_group, a.error_flags, 0);
+                      blockIdx.x, a.chunk_count, sh, eid, local, a.slot_idx, a.recv_src,
+                      a.num_tokens_per_expert, a.expert_offsets, a.num_tokens_per_group,
+                      a.error_flags, flag_bits);
 }
 
 // Inputs of at most one chunk (decode-sized batches): both phases in one
@@ -335,15 +341,15 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(LayoutArg
 __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(LayoutArgs a) {
   __shared__ LayoutShared sh;
   int32_t eid[kLayoutItems], local[kLayoutItems];
+  // entries after the chunk's own (written by a kernel that prepared the ids)
+  const int32_t extra_bits = load_flag_bits(a.chunk_flags, 1, a.num_flags);
   const int bad = count_chunk(a.topk_idx, a.num_pairs, a.num_experts, a.expert_bits, 0,
                               sh.counts, a.chunk_count, a.chunk_flags, sh.tot, eid, local);
   for (int e = threadIdx.x; e < a.num_experts; e += kLayoutThreads) sh.pre[e] = 0;
   __syncthreads();
-  finish_chunk<true>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, 1, a.num_flags, 0,
-                     a.chunk_count,
-                     a.chunk_flags, sh, eid, local, a.slot_idx, a.recv_src,
-                     a.num_tokens_per_expert, a.expert_offsets, a.num_tokens_per_group,
-                     a.error_flags, bad);
+  finish_chunk<true>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, 1, 0, a.chunk_count,
+                     sh, eid, local, a.slot_idx, a.recv_src, a.num_tokens_per_expert,
+                     a.expert_offsets, a.num_tokens_per_group, a.error_flags, bad | extra_bits);
 }
 
 hipError_t launch_layout(const int64_t* topk_idx, const ep_layout_t& L, void* workspace,
