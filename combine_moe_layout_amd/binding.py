@@ -69,7 +69,7 @@ SIGNATURES = {
     "ep_dequant_mxfp8": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp]),
     "ep_group_layout_init": (ctypes.c_int, [_LP, _i64, _i32, _i32]),
     "ep_group_layout_workspace_bytes": (_sz, [_i64, _i32, _i32]),
-    "ep_get_group_layout": (ctypes.c_int, [_vp, _vp, _i32, _i32, _LP, _vp, _vp, _vp, _sz, _vp]),
+    "ep_get_group_layout": (ctypes.c_int, [_vp, _vp, _i32, _i32, _LP, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ep_combine_groups": (ctypes.c_int, [_vp, _LP, _i32, _vp, _vp]),
     "ep_dequant_fp8": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp]),
     "ep_cast_e4m3_bits": (ctypes.c_int, [_u32, _i64, _i32, _vp, _vp]),
@@ -310,10 +310,12 @@ def ep_combine_fp8(expert_q: torch.Tensor, expert_scales: torch.Tensor, topk_wei
 
 def ep_get_group_layout(topk_idx: torch.Tensor, topk_weights: torch.Tensor | None,
                         layout: EpGroupLayout, recv_topk_idx: torch.Tensor | None = None,
-                        recv_topk_weights: torch.Tensor | None = None, stream=None) -> EpGroupLayout:
+                        recv_topk_weights: torch.Tensor | None = None, stream=None,
+                        is_token_in_group: torch.Tensor | None = None) -> EpGroupLayout:
     """topk_idx int64 [T, k] (and topk_weights fp32 [T, k] when
     recv_topk_weights is wanted) -> the group layout's arrays, plus optional
-    recv_topk_idx int64 [T*kg, k] / recv_topk_weights fp32 [T*kg, k]."""
+    recv_topk_idx int64 [T*kg, k] / recv_topk_weights fp32 [T*kg, k] and
+    is_token_in_group uint8 (or bool) [T, G]."""
     T, k = layout.num_tokens, layout.source_topk
     if tuple(topk_idx.shape) != (T, k):
         raise ValueError("topk_idx shape %s does not match the layout" % (tuple(topk_idx.shape),))
@@ -324,12 +326,18 @@ def ep_get_group_layout(topk_idx: torch.Tensor, topk_weights: torch.Tensor | Non
     for name, t in (("recv_topk_idx", recv_topk_idx), ("recv_topk_weights", recv_topk_weights)):
         if t is not None and tuple(t.shape) != rows:
             raise ValueError("%s must have shape %s" % (name, rows))
+    member = None
+    if is_token_in_group is not None:
+        if tuple(is_token_in_group.shape) != (T, layout.num_experts):
+            raise ValueError("is_token_in_group must have shape %s" % ((T, layout.num_experts),))
+        member = is_token_in_group.view(torch.uint8) if is_token_in_group.dtype == torch.bool else is_token_in_group
     _check("ep_get_group_layout", lib().ep_get_group_layout(
         _ptr(topk_idx, "topk_idx", torch.int64) if topk_idx.numel() else None,
         _ptr(topk_weights, "topk_weights", torch.float32) if topk_weights is not None and topk_weights.numel() else None,
         k, layout.source_experts, ctypes.byref(layout.struct),
         _ptr(recv_topk_idx, "recv_topk_idx", torch.int64) if recv_topk_idx is not None and recv_topk_idx.numel() else None,
         _ptr(recv_topk_weights, "recv_topk_weights", torch.float32) if recv_topk_weights is not None and recv_topk_weights.numel() else None,
+        _ptr(member, "is_token_in_group", torch.uint8) if member is not None and member.numel() else None,
         layout.workspace.data_ptr(), layout.workspace.numel(), _stream(stream)))
     return layout
 

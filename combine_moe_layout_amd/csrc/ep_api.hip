@@ -197,8 +197,9 @@ size_t ep_group_layout_workspace_bytes(int64_t num_tokens, int32_t num_topk, int
 
 int ep_get_group_layout(const int64_t* topk_idx, const float* topk_weights, int32_t num_topk,
                         int32_t num_experts, const ep_layout_t* group_layout,
-                        int64_t* recv_topk_idx, float* recv_topk_weights, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        int64_t* recv_topk_idx, float* recv_topk_weights,
+                        uint8_t* is_token_in_group, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   int rc = check_layout(group_layout);
   if (rc != EP_OK) return rc;
   const ep_layout_t& GL = *group_layout;
@@ -222,7 +223,8 @@ int ep_get_group_layout(const int64_t* topk_idx, const float* topk_weights, int3
   if (workspace_bytes < ep::group_layout_workspace_bytes(GL.num_tokens, num_topk, G))
     return EP_ERR_WORKSPACE;
   return launch_status(ep::launch_group_layout(topk_idx, topk_weights, num_topk, num_experts, GL,
-                                               recv_topk_idx, recv_topk_weights, workspace,
+                                               recv_topk_idx, recv_topk_weights,
+                                               is_token_in_group, workspace,
                                                static_cast<hipStream_t>(stream)));
 }
 

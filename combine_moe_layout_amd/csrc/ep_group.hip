@@ -29,6 +29,8 @@
 //   2. the layout kernels over that table (E := G, k := kg); they OR the
 //      table's flag entries into error_flags.
 //   3. group_meta_kernel: lane (t, j) writes column j of every row of token t.
+//   4. (optional) group_member_kernel: lane (t, g) writes is_token_in_group
+//      [t, g], 1 when g is one of the token's entries in the table.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -117,9 +119,30 @@ __global__ __launch_bounds__(kGroupThreads) void group_meta_kernel(
   }
 }
 
+// is_token_in_group[t, g] for the n = T * G (token, group) cells: a scan of
+// the token's kg table entries (its groups ascending, then -1).
+__global__ __launch_bounds__(kGroupThreads) void group_member_kernel(
+    const int64_t* __restrict__ table, int64_t n, int32_t kg, int32_t G,
+    uint8_t* __restrict__ member) {
+  for (int64_t c = (int64_t)blockIdx.x * kGroupThreads + threadIdx.x; c < n;
+       c += (int64_t)gridDim.x * kGroupThreads) {
+    const int64_t t = c / G;
+    const int64_t g = c - t * G;
+    const int64_t* row = table + t * kg;
+    uint8_t hit = 0;
+    for (int32_t i = 0; i < kg; ++i) {
+      const int64_t v = row[i];
+      if (v < 0) break;
+      hit |= v == g ? 1 : 0;
+    }
+    member[c] = hit;
+  }
+}
+
 hipError_t launch_group_layout(const int64_t* topk_idx, const float* topk_weights, int32_t k,
                                int32_t E, const ep_layout_t& GL, int64_t* recv_idx,
-                               float* recv_w, void* workspace, hipStream_t stream) {
+                               float* recv_w, uint8_t* member, void* workspace,
+                               hipStream_t stream) {
   const int64_t T = GL.num_tokens;
   const int32_t G = GL.num_experts;
   const int32_t kg = GL.num_topk;
@@ -137,6 +160,13 @@ hipError_t launch_group_layout(const int64_t* topk_idx, const float* topk_weight
     hipLaunchKernelGGL(group_meta_kernel, dim3((unsigned)blocks), dim3(kGroupThreads), 0, stream,
                        topk_idx, topk_weights, T, k, E, E / G, kg, sg, table, GL.slot_idx,
                        recv_idx, recv_w);
+  if (blocks > 0 && member != nullptr) {
+    const int64_t n = T * G;
+    const int64_t want = (n + kGroupThreads - 1) / kGroupThreads;
+    const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(group_member_kernel, dim3(grid), dim3(kGroupThreads), 0, stream, table, n,
+                       kg, G, member);
+  }
   return hipGetLastError();
 }
 

@@ -103,7 +103,8 @@ size_t group_layout_workspace_bytes(int64_t T, int32_t k, int32_t G);
 
 hipError_t launch_group_layout(const int64_t* topk_idx, const float* topk_weights, int32_t k,
                                int32_t E, const ep_layout_t& GL, int64_t* recv_idx,
-                               float* recv_w, void* workspace, hipStream_t stream);
+                               float* recv_w, uint8_t* member, void* workspace,
+                               hipStream_t stream);
 
 hipError_t launch_combine_groups(const void* z, const ep_layout_t& GL, int32_t hidden, void* out,
                                  hipStream_t stream);

@@ -299,15 +299,19 @@ size_t ep_group_layout_workspace_bytes(int64_t num_tokens, int32_t num_topk, int
  *                     valid and in group g, else -1
  *   recv_topk_weights fp32  [T*kg, num_topk]: topk_weights[t, j] for the same
  *                     entries, else 0
- * Rows past the used ones are left untouched.  workspace: at least
+ * Rows past the used ones are left untouched.  Optional (NULL to skip):
+ *   is_token_in_group uint8 [T, G]: 1 if token t has a valid expert in group g,
+ *                     else 0 (per-rank membership, [yololab] "Load
+ *                     Imbalance": what each rank receives).  workspace: at least
  * ep_group_layout_workspace_bytes(T, num_topk, G) bytes, 256-byte aligned,
  * scratch.  Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN,
  * EP_ERR_WORKSPACE or EP_ERR_LAUNCH.
  */
 int ep_get_group_layout(const int64_t* topk_idx, const float* topk_weights, int32_t num_topk,
                         int32_t num_experts, const ep_layout_t* group_layout,
-                        int64_t* recv_topk_idx, float* recv_topk_weights, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        int64_t* recv_topk_idx, float* recv_topk_weights,
+                        uint8_t* is_token_in_group, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * Group combine: the sending side's reduction of the rows that come back.

@@ -67,7 +67,7 @@ def _load(path: str) -> ctypes.CDLL:
     L.ep_oracle_combine_fp8.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp]
     L.ep_oracle_combine_fp8_tokens.argtypes = [vp, vp, vp, vp, i32, i32, vp, i64, vp]
     L.ep_oracle_group_layout.restype = ctypes.c_int
-    L.ep_oracle_group_layout.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.ep_oracle_group_layout.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.ep_oracle_combine_groups.argtypes = [vp, vp, i64, i32, i32, vp]
     L.ep_oracle_combine_groups_tokens.argtypes = [vp, vp, i32, i32, vp, i64, vp]
     L.ep_oracle_quantize_token_mxfp8.argtypes = [vp, i32, vp, vp]
@@ -322,7 +322,8 @@ def group_layout(topk_idx: np.ndarray, topk_weights: np.ndarray | None, E: int, 
     group_idx [T,kg], num_tokens_per_group [G], group_offsets [G+1],
     group_slot [T,kg], recv_token [T*kg] (-1 in unused rows),
     recv_topk_idx [T*kg,k] (-1 in unused rows), recv_topk_weights [T*kg,k]
-    (0 in unused rows, or None without weights), error_flags, kg, rows_used."""
+    (0 in unused rows, or None without weights), is_token_in_group [T,G]
+    (uint8, 1 where the token reaches the group), error_flags, kg, rows_used."""
     topk_idx = _c(topk_idx, np.int64)
     T, k = topk_idx.shape
     kg = min(k, G)
@@ -338,17 +339,18 @@ def group_layout(topk_idx: np.ndarray, topk_weights: np.ndarray | None, E: int, 
         topk_weights = _c(topk_weights, np.float32)
         rw = np.zeros((R, k), np.float32)
     flags = np.zeros(1, np.int32)
+    member = np.zeros((T, G), np.uint8)
     has = T > 0
     rc = lib().ep_oracle_group_layout(_p(topk_idx) if has else None,
                                       _p(topk_weights) if rw is not None and has else None,
                                       T, k, E, G, _p(gidx) if has else None, _p(cnt), _p(off),
                                       _p(slot) if has else None, _p(tok) if R else None,
                                       _p(ridx) if R else None, _p(rw) if rw is not None and R else None,
-                                      _p(flags))
+                                      _p(member) if has else None, _p(flags))
     if rc != 0:
         raise ValueError("oracle group layout rejected its arguments (status %d)" % rc)
     return dict(group_idx=gidx, num_tokens_per_group=cnt, group_offsets=off, group_slot=slot,
-                recv_token=tok, recv_topk_idx=ridx, recv_topk_weights=rw,
+                recv_token=tok, recv_topk_idx=ridx, recv_topk_weights=rw, is_token_in_group=member,
                 error_flags=int(flags[0]), kg=kg, rows_used=int(off[G]))
 
 

@@ -480,7 +480,7 @@ EXPORT int ep_oracle_group_layout(const int64_t* topk_idx, const float* topk_wei
                                   int32_t* num_tokens_per_group, int32_t* group_offsets,
                                   int32_t* group_slot, int32_t* recv_token,
                                   int64_t* recv_topk_idx, float* recv_topk_weights,
-                                  int32_t* error_flags) {
+                                  unsigned char* is_token_in_group, int32_t* error_flags) {
     if (T < 0 || k < 1 || E < 1 || G < 1 || E % G != 0) return ORACLE_ERR_SHAPE;
     if ((T > 0 && (!topk_idx || !group_idx || !group_slot)) || !num_tokens_per_group ||
         !group_offsets || !error_flags || (recv_topk_weights && !topk_weights))
@@ -541,6 +541,7 @@ EXPORT int ep_oracle_group_layout(const int64_t* topk_idx, const float* topk_wei
         }
     }
     free(cursor);
+    if (is_token_in_group && T > 0) memcpy(is_token_in_group, in_group, (size_t)T * (size_t)G);
     free(in_group);
     *error_flags = flags;
     return ORACLE_OK;

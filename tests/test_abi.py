@@ -221,14 +221,17 @@ def test_group_layout_sizes_and_validation(L):
     g.num_tokens_per_expert = g.expert_offsets = g.num_tokens_per_group = fake
     g.slot_idx = g.error_flags = fake
     need = L.ep_group_layout_workspace_bytes(64, 4, 8)
-    assert L.ep_get_group_layout(fake, fake, 4, 60, by(g), None, None, fake, need, None) == -2   # E % G
-    assert L.ep_get_group_layout(fake, fake, 3, 64, by(g), None, None, fake, need, None) == -2   # kg != min(k, G)
-    assert L.ep_get_group_layout(None, None, 4, 64, by(g), None, None, fake, need, None) == -1   # topk_idx
-    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, fake, fake, need, None) == -1   # weights needed
-    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, None, None, need, None) == -1   # workspace
-    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, None, fake + 64, need, None) == -3
-    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), fake + 4, None, fake, need, None) == -3
-    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, None, fake, need - 1, None) == -4
+    # arguments: topk_idx, topk_weights, k, E, layout, recv_topk_idx, recv_topk_weights,
+    # is_token_in_group, workspace, bytes, stream
+    assert L.ep_get_group_layout(fake, fake, 4, 60, by(g), None, None, None, fake, need, None) == -2   # E % G
+    assert L.ep_get_group_layout(fake, fake, 3, 64, by(g), None, None, None, fake, need, None) == -2   # kg != min(k, G)
+    assert L.ep_get_group_layout(None, None, 4, 64, by(g), None, None, None, fake, need, None) == -1   # topk_idx
+    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, fake, None, fake, need, None) == -1   # weights needed
+    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, None, None, None, need, None) == -1   # workspace
+    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, None, None, fake + 64, need, None) == -3
+    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), fake + 4, None, None, fake, need, None) == -3
+    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, None, None, fake, need - 1, None) == -4
+    assert L.ep_get_group_layout(fake, None, 4, 64, by(g), None, None, fake + 1, fake, need - 1, None) == -4
     e = binding.ep_layout_t()
     assert L.ep_layout_init(by(e), 64, 4, 16, 4, 0) == 0             # an expert layout is not a group layout
     e.num_tokens_per_expert = e.expert_offsets = e.num_tokens_per_group = e.slot_idx = e.error_flags = fake

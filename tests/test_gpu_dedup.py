@@ -28,9 +28,11 @@ def gpu_group_layout(idx: np.ndarray, w, E: int, G: int, meta: bool = True):
     ridx = torch.full((R, k), SENTINEL, dtype=torch.int64, device="cuda") if meta else None
     rw = torch.full((R, k), float(SENTINEL), dtype=torch.float32, device="cuda") if meta else None
     tw = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda() if w is not None else None
+    member = torch.full((T, G), 0x77, dtype=torch.uint8, device="cuda")
     B.ep_get_group_layout(torch.from_numpy(np.ascontiguousarray(idx, np.int64)).cuda(), tw, gl,
-                          ridx, rw if w is not None else None)
+                          ridx, rw if w is not None else None, is_token_in_group=member)
     torch.cuda.synchronize()
+    gl.is_token_in_group = member
     return gl, ridx, (rw if w is not None else None)
 
 
@@ -47,6 +49,7 @@ def compare_group_layout(idx, w, E, G, what, meta=True):
     t_of, i_of = np.nonzero(o["group_slot"] >= 0)
     src[o["group_slot"][t_of, i_of]] = t_of * kg + i_of
     eq(gl.recv_src.cpu().numpy(), src, "recv_src (and untouched unused rows)")
+    eq(gl.is_token_in_group.cpu().numpy(), o["is_token_in_group"], "is_token_in_group")
     assert int(gl.error_flags.cpu()[0]) == o["error_flags"], what
     if meta:
         gi = ridx.cpu().numpy()

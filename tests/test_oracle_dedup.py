@@ -104,6 +104,8 @@ def test_group_layout_brute_force_tiny(seed):
     assert out["group_offsets"].tolist() == offs
     assert out["group_slot"].tolist() == (slot if T else [])
     assert out["error_flags"] == flags
+    member = [[1 if gg in gidx[t] else 0 for gg in range(G)] for t in range(T)]
+    assert out["is_token_in_group"].tolist() == member
     for r in range(out["rows_used"]):
         assert out["recv_token"][r] == tok[r]
         assert out["recv_topk_idx"][r].tolist() == ridx[r]
@@ -127,6 +129,7 @@ def test_group_layout_matches_a_stable_sort(name):
     present = _entries(wl.topk_idx, wl.E, wl.G)
     t_of, g_of = np.nonzero(present)              # token-major, groups ascending per token
     assert (out["num_tokens_per_group"] == present.sum(0)).all()
+    assert (out["is_token_in_group"] == present).all()
     assert (out["group_offsets"] == np.concatenate([[0], np.cumsum(present.sum(0))])).all()
     order = np.argsort(g_of, kind="stable")       # group-major, token order kept
     rows = np.empty_like(order)

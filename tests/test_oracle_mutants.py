@@ -101,6 +101,8 @@ MUTANTS = [
     ("fp16 decode exponent bias", "ldexp(1024.0 + m, e - 15 - 10)", "ldexp(1024.0 + m, e - 14 - 10)"),
     ("fp16 combine forgets the weight", "acc += (double)w[t * k + j] * ep_oracle_f16_to_double(",
      "acc += ep_oracle_f16_to_double("),
+    ("token-in-group matrix copied short", "memcpy(is_token_in_group, in_group, (size_t)T * (size_t)G);",
+     "memcpy(is_token_in_group, in_group, (size_t)T);"),
     ("MN-major layout indexed row-major", "memcpy(dst + ((int64_t)c * rows + r) * entry_bytes,",
      "memcpy(dst + (r * entries + c) * entry_bytes,"),
     ("group combine drops the last group",
