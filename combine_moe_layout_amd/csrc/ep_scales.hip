@@ -12,8 +12,9 @@
 // stride (reading one column across lanes then touches distinct banks).  The
 // tile leaves column by column, consecutive lanes on consecutive rows, so each
 // column of the tile is one contiguous run: 64 fp32 words or 128 E8M0 bytes,
-// 256 or 128 bytes, stored 16 bytes per lane where alignment allows.  Each
-// byte is read once and written once.
+// 256 or 128 bytes, stored 16 bytes per lane where alignment allows (for E8M0
+// bytes a lane transposes 16 rows x 4 columns in registers).  Each byte is read
+// once and written once.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -67,6 +68,31 @@ __global__ __launch_bounds__(kScaleThreads) void scales_mn_kernel(
     return kEntryBytes == 4 ? word : (word >> (8 * (c % kPerWord))) & 0xFFu;
   };
   constexpr int kGroups = kTileRows / kRowsPerStore;  // stores per column of a tile
+  if constexpr (kVec && kEntryBytes == 1) {
+    // E8M0 bytes: a lane takes one tile word (4 columns) of 16 consecutive
+    // rows, reads those 16 words once, transposes the 16 x 4 bytes in
+    // registers and stores the 4 columns' 16-byte runs
+    for (int32_t i = threadIdx.x; i < ncols * kGroups; i += kScaleThreads) {
+      const int32_t u = i / kGroups;                        // tile word
+      const int32_t r = (i - u * kGroups) * kRowsPerStore;  // first of 16 rows
+      if (r >= nrows) continue;
+      uint32_t rw[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) rw[q] = tile[(r + q) * kStride + u];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {  // column 4u + b
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = ((rw[4 * q] >> (8 * b)) & 0xFFu) | (((rw[4 * q + 1] >> (8 * b)) & 0xFFu) << 8) |
+                 (((rw[4 * q + 2] >> (8 * b)) & 0xFFu) << 16) |
+                 (((rw[4 * q + 3] >> (8 * b)) & 0xFFu) << 24);
+        const int64_t at = (int64_t)(4 * (w0 + u) + b) * rows + r0 + r;
+        *reinterpret_cast<u32x4*>(dst + at) = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    }
+    return;
+  }
   const int32_t entries = ncols * kPerWord;
   for (int32_t i = threadIdx.x; i < entries * kGroups; i += kScaleThreads) {
     const int32_t c = i / kGroups;
