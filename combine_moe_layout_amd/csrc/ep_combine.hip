@@ -90,14 +90,15 @@ __device__ __forceinline__ bool combine_token(const CombineMap& m, int64_t num_t
 // K > 0: compile-time top-k.  K == 0: any top-k, one row at a time.
 // kUnit: every weight is 1 and w is not read (the group combine of the dedup
 // variant, whose rows arrive already weighted).  kF16: fp16 rows and output.
-template <int K, bool kUnit, bool kF16 = false>
+// kWhole: one token per workgroup, its slots and weights through scalar loads.
+template <int K, bool kUnit, bool kF16 = false, bool kWhole = false>
 __global__ __launch_bounds__(1024) void combine_kernel(
     const u32x4* __restrict__ y, const float* __restrict__ w,
     const int32_t* __restrict__ slot_idx, int64_t num_tokens, int32_t k, int32_t hidden,
     CombineMap m, u32x4* __restrict__ out) {
   int64_t t;
   int32_t lt;
-  if (!combine_token<false>(m, num_tokens, t, lt)) return;
+  if (!combine_token<kWhole>(m, num_tokens, t, lt)) return;
   const int32_t vec_per_row = hidden / 8;
   const int32_t kk = K > 0 ? K : k;
   const int32_t* slots = slot_idx + t * kk;
@@ -163,16 +164,25 @@ static CombineMap combine_map(int32_t vecs_per_row) {
   return m;
 }
 
-// The bf16 kernel always takes the general token mapping (which also covers one
-// token per workgroup): its slots and weights then arrive as per-lane vector
-// loads, which measured about 4% faster here than the scalar loads of the
-// uniform-token form (179 vs 187 us at 8192 tokens x 7168, top-8).
+// Large batches take the general token mapping (which also covers one token
+// per workgroup): slots and weights then arrive as per-lane vector loads,
+// about 3% faster there than the scalar loads of the uniform-token form (179
+// vs 185 us at 8192 tokens x 7168, top-8).  Decode-sized batches (at most
+// kFusedMaxPairs pairs, one token per workgroup) are latency-bound, and there
+// the scalar loads win (6.7 vs 7.2 us per call at 128 tokens, top-8).
 template <int K, bool kUnit, bool kF16>
 static void launch_k(dim3 grid, dim3 block, hipStream_t stream, const void* y, const float* w,
                      const ep_layout_t& L, int32_t hidden, CombineMap m, void* out) {
-  hipLaunchKernelGGL((combine_kernel<K, kUnit, kF16>), grid, block, 0, stream,
-                     static_cast<const u32x4*>(y), w, L.slot_idx, L.num_tokens, L.num_topk,
-                     hidden, m, static_cast<u32x4*>(out));
+  const bool whole = m.tokens_per_block == 1 &&
+                     L.num_tokens * (int64_t)L.num_topk <= (int64_t)kFusedMaxPairs;
+  if (whole)
+    hipLaunchKernelGGL((combine_kernel<K, kUnit, kF16, true>), grid, block, 0, stream,
+                       static_cast<const u32x4*>(y), w, L.slot_idx, L.num_tokens, L.num_topk,
+                       hidden, m, static_cast<u32x4*>(out));
+  else
+    hipLaunchKernelGGL((combine_kernel<K, kUnit, kF16>), grid, block, 0, stream,
+                       static_cast<const u32x4*>(y), w, L.slot_idx, L.num_tokens, L.num_topk,
+                       hidden, m, static_cast<u32x4*>(out));
 }
 
 template <bool kUnit, bool kF16 = false>
