@@ -6,7 +6,7 @@ never imports, loads or calls it, and it shares no code with the HIP library.
 
 This module is a thin numpy <-> ctypes wrapper around ``ep_oracle.c``: plain,
 single-threaded scalar loops written from the definitions on the pages (cited
-in that file's header, with the readings R1..R20 it takes where the pages are
+in that file's header, with the readings R1..R21 it takes where the pages are
 silent).  Every function here only marshals arrays; all arithmetic is in C.
 """
 from __future__ import annotations
@@ -59,6 +59,8 @@ def _load(path: str) -> ctypes.CDLL:
     L.ep_oracle_quantize_token_fp8.argtypes = [vp, i32, vp, vp]
     L.ep_oracle_dispatch_fp8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
     L.ep_oracle_scales_mn_major.argtypes = [vp, i64, i32, i32, vp]
+    L.ep_oracle_combine_mxfp8.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp]
+    L.ep_oracle_combine_mxfp8_tokens.argtypes = [vp, vp, vp, vp, i32, i32, vp, i64, vp]
     L.ep_oracle_dequant_fp8.argtypes = [vp, vp, i64, i32, vp]
     L.ep_oracle_combine.argtypes = [vp, vp, vp, i64, i32, i32, vp]
     L.ep_oracle_combine_tokens.argtypes = [vp, vp, vp, i32, i32, vp, i64, vp]
@@ -449,4 +451,31 @@ def scales_mn_major(scales: np.ndarray) -> np.ndarray:
     rows, n = src.shape
     out = np.empty((n, rows), dtype=src.dtype)
     lib().ep_oracle_scales_mn_major(_p(src), rows, n, src.dtype.itemsize, _p(out))
+    return out
+
+
+def combine_mxfp8(q: np.ndarray, scales: np.ndarray, w: np.ndarray, slot_idx: np.ndarray) -> np.ndarray:
+    """Combine of MXFP8 expert outputs (reading R21): codes [R, H], E8M0 bytes [R, H/32]."""
+    q = _c(q, np.uint8)
+    scales = _c(scales, np.uint8)
+    w = _c(w, np.float32)
+    slot_idx = _c(slot_idx, np.int32)
+    T, k = slot_idx.shape
+    H = q.shape[1]
+    out = np.empty((T, H), np.uint16)
+    lib().ep_oracle_combine_mxfp8(_p(q), _p(scales), _p(w), _p(slot_idx), T, k, H, _p(out))
+    return out
+
+
+def combine_mxfp8_tokens(q, scales, w, slot_idx, tokens) -> np.ndarray:
+    q = _c(q, np.uint8)
+    scales = _c(scales, np.uint8)
+    w = _c(w, np.float32)
+    slot_idx = _c(slot_idx, np.int32)
+    tokens = _c(tokens, np.int64).reshape(-1)
+    k = slot_idx.shape[1]
+    H = q.shape[1]
+    out = np.empty((tokens.size, H), np.uint16)
+    lib().ep_oracle_combine_mxfp8_tokens(_p(q), _p(scales), _p(w), _p(slot_idx), k, H, _p(tokens),
+                                         tokens.size, _p(out))
     return out

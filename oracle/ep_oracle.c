@@ -82,6 +82,9 @@
  *       the yololab page asks to check; two pages say the v2 buffer adopts a
  *       GEMM layout): the same scale entries, stored transposed, entry c of
  *       receive row r at c * R + r.
+ *   R21 MXFP8 combine variant: expert outputs as E4M3 codes + one E8M0 byte
+ *       per (row, 32-channel block) with value 2^(byte - 127) (byte 255 is
+ *       NaN), decoded exactly inside the weighted sum.
  */
 #include <math.h>
 #include <stdint.h>
@@ -722,4 +725,40 @@ EXPORT void ep_oracle_scales_mn_major(const uint8_t* src, int64_t rows, int32_t 
         for (int32_t c = 0; c < entries; ++c)
             memcpy(dst + ((int64_t)c * rows + r) * entry_bytes,
                    src + (r * entries + c) * entry_bytes, (size_t)entry_bytes);
+}
+
+/* R21: an E8M0 scale byte's value, 2^(byte - 127); 255 encodes NaN (OCP MX). */
+static double e8m0_value(uint8_t b) { return b == 255 ? NAN : ldexp(1.0, (int)b - 127); }
+
+/* R21 MXFP8 combine: out[t] = bf16(sum_j w[t,j] * decode(q) * 2^(byte - 127))
+ * over valid pairs, with one scale byte per (row, 32-channel block), summed in
+ * fp64 (each product is exact there) and rounded once, nearest-even; +0 for a
+ * token with no valid pair. */
+static void combine_mxfp8_one(const uint8_t* q, const uint8_t* scales, const float* w,
+                              const int32_t* slot_idx, int64_t t, int32_t k, int32_t H,
+                              uint16_t* out_row) {
+    int32_t nb = H / 32;
+    for (int32_t c = 0; c < H; ++c) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t s = slot_idx[t * k + j];
+            if (s < 0) continue;
+            acc += (double)w[t * k + j] * ep_oracle_e4m3_decode(q[(int64_t)s * H + c]) *
+                   e8m0_value(scales[(int64_t)s * nb + c / 32]);
+        }
+        out_row[c] = ep_oracle_bf16_from_double(acc);
+    }
+}
+
+EXPORT void ep_oracle_combine_mxfp8(const uint8_t* q, const uint8_t* scales, const float* w,
+                                    const int32_t* slot_idx, int64_t T, int32_t k, int32_t H,
+                                    uint16_t* out) {
+    for (int64_t t = 0; t < T; ++t) combine_mxfp8_one(q, scales, w, slot_idx, t, k, H, out + t * H);
+}
+
+EXPORT void ep_oracle_combine_mxfp8_tokens(const uint8_t* q, const uint8_t* scales, const float* w,
+                                           const int32_t* slot_idx, int32_t k, int32_t H,
+                                           const int64_t* tokens, int64_t n, uint16_t* out_rows) {
+    for (int64_t i = 0; i < n; ++i)
+        combine_mxfp8_one(q, scales, w, slot_idx, tokens[i], k, H, out_rows + i * H);
 }

@@ -103,6 +103,10 @@ MUTANTS = [
      "acc += ep_oracle_f16_to_double("),
     ("token-in-group matrix copied short", "memcpy(is_token_in_group, in_group, (size_t)T * (size_t)G);",
      "memcpy(is_token_in_group, in_group, (size_t)T);"),
+    ("MX combine scale bias off by one", "return b == 255 ? NAN : ldexp(1.0, (int)b - 127);",
+     "return b == 255 ? NAN : ldexp(1.0, (int)b - 128);"),
+    ("MX combine reads the 128-channel block's scale", "e8m0_value(scales[(int64_t)s * nb + c / 32]);",
+     "e8m0_value(scales[(int64_t)s * nb + c / 128]);"),
     ("MN-major layout indexed row-major", "memcpy(dst + ((int64_t)c * rows + r) * entry_bytes,",
      "memcpy(dst + (r * entries + c) * entry_bytes,"),
     ("group combine drops the last group",
@@ -155,7 +159,9 @@ def _battery():
                pins_mx.test_f16_golden_values, pins_mx.test_f16_rounding_against_numpy,
                pins_mx.test_combine_f16_golden,
                pins_mx.test_combine_f16_one_hot_is_a_gather_and_round_trip_is_exact,
-               pins_mx.test_combine_f16_is_the_rounded_exact_sum]
+               pins_mx.test_combine_f16_is_the_rounded_exact_sum,
+               pins_mx.test_combine_mxfp8_golden, pins_mx.test_combine_mxfp8_one_hot_is_the_dequantisation,
+               pins_mx.test_combine_mxfp8_vs_float64_sum]
     checks += [lambda: pins_mn.test_scales_mn_major_matches_index_loops(3, 5),
                lambda: pins_mn.test_scales_mn_major_matches_index_loops(17, 56),
                lambda: pins_mn.test_mn_major_columns_are_the_tokens_scales(False)]

@@ -8,6 +8,9 @@ exponent's defining bracket and the error bound.
 FP16 (reading R19): binary16 rounding and the fp16 combine.  Pinned by
 hand-worked values, numpy's float16 (decoded exhaustively, rounding on random
 values and constructed ties), and exact sums.
+
+MXFP8 combine (reading R21): a hand-worked case, the one-hot reduction to the
+MXFP8 dequantisation, and a float64 sum built on torch's E4M3 and E8M0 decodes.
 """
 import json
 import os
@@ -204,3 +207,76 @@ def test_combine_f16_is_the_rounded_exact_sum():
             exact = float(acc)
             assert Fraction(exact) == acc
             assert out[t, c] == np.float16(exact).view(np.uint16) or (exact == 0 and out[t, c] == 0)
+
+
+# --------------------------------------------------------------------------- MXFP8 combine
+def test_combine_mxfp8_golden():
+    """Hand-worked, H = 64 (two 32-channel blocks), k = 2.
+    Row 0: codes 0x38 (1.0) except column 31, 0xB8 (-1.0); scale bytes 128, 129
+    (2 and 4).  Row 1: codes 0x40 (2.0); bytes 126, 127 (0.5 and 1).
+    Token 0 = 0.5 * row 0 + 0.25 * row 1:
+      columns 0..30  0.5*1*2 + 0.25*2*0.5 = 1.25   (bf16 0x3FA0)
+      column 31      0.5*-1*2 + 0.25*2*0.5 = -0.75 (0xBF40)
+      columns 32..63 0.5*1*4 + 0.25*2*1 = 2.5      (0x4020)
+    Token 1 = 1.0 * row 1, its second pair dropped: 1.0 (0x3F80), then 2.0 (0x4000).
+    Token 2 has no valid pair: +0."""
+    q = np.full((2, 64), 0x38, np.uint8)
+    q[0, 31] = 0xB8
+    q[1, :] = 0x40
+    sc = np.array([[128, 129], [126, 127]], np.uint8)
+    slot = np.array([[0, 1], [1, -1], [-1, -1]], np.int32)
+    w = np.array([[0.5, 0.25], [1.0, 0.7], [0.3, 0.3]], np.float32)
+    out = oracle.combine_mxfp8(q, sc, w, slot)
+    want = np.zeros((3, 64), np.uint16)
+    want[0, :31], want[0, 31], want[0, 32:] = 0x3FA0, 0xBF40, 0x4020
+    want[1, :32], want[1, 32:] = 0x3F80, 0x4000
+    assert (out == want).all(), [(r, c, hex(out[r, c]), hex(want[r, c])) for r, c in np.argwhere(out != want)[:4]]
+
+
+def _mx_operands(g, R, H, lo=100, hi=155):
+    q = g.integers(0, 256, (R, H)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x31          # no NaN codes
+    sc = g.integers(lo, hi, (R, H // 32)).astype(np.uint8)
+    return q, sc
+
+
+def test_combine_mxfp8_one_hot_is_the_dequantisation():
+    g = np.random.default_rng(12)
+    R, H, k = 40, 256, 4
+    q, sc = _mx_operands(g, R, H)
+    slot = np.full((R, k), -1, np.int32)
+    slot[:, 2] = np.arange(R)
+    w = g.random((R, k)).astype(np.float32)
+    w[:, 2] = 1.0
+    # equal up to the sign of zero: the sum starts at +0, so a -0 term (code 0x80) gives +0
+    nz = lambda b: np.where(b == 0x8000, 0, b)
+    assert (nz(oracle.combine_mxfp8(q, sc, w, slot)) == nz(oracle.dequant_mxfp8(q, sc))).all()
+
+
+def test_combine_mxfp8_vs_float64_sum():
+    """Within half a bf16 ulp of a float64 sum whose operands come from torch's
+    float8_e4m3fn and float8_e8m0fnu decodes (independent of the oracle)."""
+    g = np.random.default_rng(13)
+    R, H, T, k = 300, 256, 64, 8
+    q, sc = _mx_operands(g, R, H)
+    slot = g.integers(-1, R, (T, k)).astype(np.int32)
+    w = g.random((T, k)).astype(np.float32)
+    out = unbf(oracle.combine_mxfp8(q, sc, w, slot)).astype(np.float64)
+    vals = _e4m3_values(q) * np.repeat(_e8m0_values(sc), 32, 1)
+    ref = np.zeros((T, H))
+    for j in range(k):
+        m = slot[:, j] >= 0
+        ref[m] += w[m, j:j + 1].astype(np.float64) * vals[slot[m, j]]
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    assert (np.abs(out - ref) <= 0.5 * ulp * (1 + 1e-9)).all()
+
+
+def test_combine_mxfp8_nan_scale_and_codes():
+    """E8M0 byte 255 and E4M3 codes 0x7F / 0xFF are NaN; a NaN term makes its
+    column NaN, and other columns are unaffected."""
+    q = np.full((1, 64), 0x38, np.uint8)
+    q[0, 40] = 0x7F
+    sc = np.array([[255, 127]], np.uint8)
+    out = unbf(oracle.combine_mxfp8(q, sc, np.ones((1, 1), np.float32), np.zeros((1, 1), np.int32)))
+    assert np.isnan(out[0, :32]).all() and np.isnan(out[0, 40])
+    assert (np.delete(out[0, 32:], 8) == 1.0).all()
