@@ -167,7 +167,7 @@ def main() -> int:
                     help="FP8 dispatch with power-of-two scales (EP_FP8_E4M3_POW2)")
     ap.add_argument("--fp8-combine", action="store_true",
                     help="expert outputs stay FP8 (the dispatched codes and scales) and combine "
-                         "reads them with ep_combine_fp8")
+                         "reads them with ep_combine_fp8 (ep_combine_mxfp8 with --mx)")
     ap.add_argument("--fused", action="store_true",
                     help="layout and dispatch through ep_layout_dispatch (one launch for batches "
                          "of at most 2048 pairs); the layout/dispatch split is then not reported")
@@ -196,9 +196,8 @@ def main() -> int:
         print("--mn-scales does not combine with --fp8-combine (ep_combine_fp8 reads row-major "
               "scales)", file=sys.stderr)
         return 2
-    if args.mx and (args.pow2 or args.fp8_combine):
-        print("--mx is its own scale format; it does not combine with --pow2 or --fp8-combine",
-              file=sys.stderr)
+    if args.mx and args.pow2:
+        print("--mx is its own scale format; it does not combine with --pow2", file=sys.stderr)
         return 2
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -339,7 +338,9 @@ def main() -> int:
                 B.ep_scales_to_mn_major(recv_s, H, dtype_enum, recv_s_mn, s)
         if ev is not None:
             ev[2].record(s)
-        if args.fp8_combine:
+        if args.fp8_combine and args.mx:
+            B.ep_combine_mxfp8(recv_q, recv_s, topk_w, lay, out, s)
+        elif args.fp8_combine:
             B.ep_combine_fp8(recv_q, recv_s, topk_w, lay, out, s)
         elif args.f16:
             B.ep_combine_f16(y, topk_w, lay, out, s)
@@ -497,7 +498,8 @@ def main() -> int:
                                       ", then scales converted to MN-major" if args.mn_convert
                                       else "") if fp8 else
                                      "fp16" if args.f16 else "bf16",
-                   "combine_dtype": "fp8_e4m3 in, bf16 out" if args.fp8_combine else
+                   "combine_dtype": ("mxfp8 in, bf16 out" if args.mx else "fp8_e4m3 in, bf16 out")
+                   if args.fp8_combine else
                                     "fp16" if args.f16 else "bf16",
                    "step": "group_layout+dispatch_to_groups+combine_groups (per-group dedup)"
                    if args.dedup else "layout_dispatch (fused call)+combine" if args.fused
@@ -519,7 +521,8 @@ def main() -> int:
         result["dispatch_plus_combine_pct_peak"] = round(100 * dc_gbps / HBM_PEAK_GBPS, 2)
         result["dispatch_gbps"] = round(dispatch_gbps, 1)
         result["roofline"] = {
-            "kernel": "combine_groups" if args.dedup else "combine_fp8" if args.fp8_combine
+            "kernel": "combine_groups" if args.dedup else
+            ("combine_mxfp8" if args.mx else "combine_fp8") if args.fp8_combine
             else "combine_f16" if args.f16 else "combine", "bound": "hbm",
             "achieved": round(combine_gbps, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(combine_gbps / HBM_PEAK_GBPS, 4),

@@ -66,6 +66,7 @@ SIGNATURES = {
     "ep_combine": (ctypes.c_int, [_vp, _vp, _LP, _i32, _vp, _vp]),
     "ep_combine_fp8": (ctypes.c_int, [_vp, _vp, _vp, _LP, _i32, _vp, _vp]),
     "ep_combine_f16": (ctypes.c_int, [_vp, _vp, _LP, _i32, _vp, _vp]),
+    "ep_combine_mxfp8": (ctypes.c_int, [_vp, _vp, _vp, _LP, _i32, _vp, _vp]),
     "ep_dequant_mxfp8": (ctypes.c_int, [_vp, _vp, _i64, _i32, _vp, _vp]),
     "ep_group_layout_init": (ctypes.c_int, [_LP, _i64, _i32, _i32]),
     "ep_group_layout_workspace_bytes": (_sz, [_i64, _i32, _i32]),
@@ -304,6 +305,22 @@ def ep_combine_fp8(expert_q: torch.Tensor, expert_scales: torch.Tensor, topk_wei
         raise ValueError("combine buffers do not match the layout")
     _check("ep_combine_fp8", lib().ep_combine_fp8(
         _ptr(expert_q, "expert_q", torch.uint8), _ptr(expert_scales, "expert_scales", torch.float32),
+        _ptr(topk_weights, "topk_weights", torch.float32), ctypes.byref(layout.struct), H,
+        _ptr(out, "out", torch.bfloat16), _stream(stream)))
+
+
+def ep_combine_mxfp8(expert_q: torch.Tensor, expert_scales: torch.Tensor, topk_weights: torch.Tensor,
+                     layout: EpLayout, out: torch.Tensor, stream=None) -> None:
+    """expert_q uint8 [R, H] E4M3 codes, expert_scales uint8 [R, H/32] E8M0 bytes,
+    topk_weights fp32 [T, k] -> out bf16 [T, H]."""
+    H = expert_q.shape[-1]
+    if (expert_q.shape[0] != layout.num_recv_rows
+            or tuple(expert_scales.shape) != (layout.num_recv_rows, H // 32)
+            or tuple(topk_weights.shape) != (layout.num_tokens, layout.num_topk)
+            or tuple(out.shape) != (layout.num_tokens, H)):
+        raise ValueError("combine buffers do not match the layout")
+    _check("ep_combine_mxfp8", lib().ep_combine_mxfp8(
+        _ptr(expert_q, "expert_q", torch.uint8), _ptr(expert_scales, "expert_scales", torch.uint8),
         _ptr(topk_weights, "topk_weights", torch.float32), ctypes.byref(layout.struct), H,
         _ptr(out, "out", torch.bfloat16), _stream(stream)))
 

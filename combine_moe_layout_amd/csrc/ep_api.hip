@@ -179,6 +179,22 @@ int ep_combine_fp8(const uint8_t* expert_q, const float* expert_scales,
                                               hidden, out, static_cast<hipStream_t>(stream)));
 }
 
+int ep_combine_mxfp8(const uint8_t* expert_q, const uint8_t* expert_scales,
+                     const float* topk_weights, const ep_layout_t* layout, int32_t hidden,
+                     void* out, void* stream) {
+  int rc = check_layout(layout);
+  if (rc != EP_OK) return rc;
+  if (hidden < 128 || hidden > EP_MAX_HIDDEN || hidden % 128 != 0) return EP_ERR_SHAPE;
+  if (layout->num_tokens == 0) return EP_OK;
+  if (expert_q == nullptr || expert_scales == nullptr || topk_weights == nullptr || out == nullptr)
+    return EP_ERR_NULL;
+  if (!aligned16(expert_q) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(topk_weights) & 3u) != 0)
+    return EP_ERR_ALIGN;
+  return launch_status(ep::launch_combine_mxfp8(expert_q, expert_scales, topk_weights, *layout,
+                                                hidden, out, static_cast<hipStream_t>(stream)));
+}
+
 int ep_group_layout_init(ep_layout_t* group_layout, int64_t num_tokens, int32_t num_topk,
                          int32_t num_groups) {
   if (group_layout == nullptr) return EP_ERR_NULL;

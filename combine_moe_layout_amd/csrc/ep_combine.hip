@@ -248,12 +248,30 @@ __device__ __forceinline__ void accumulate8_fp8(float* acc, const u32x2_vec& c, 
   for (int i = 0; i < 8; ++i) acc[i] = valid ? fmaf(ws, f[i], acc[i]) : acc[i];
 }
 
+// E8M0 byte -> fp32 2^(b - 127): the exponent field itself for b >= 1, the
+// subnormal 2^-127 for b = 0; 255 is NaN.
+__device__ __forceinline__ float e8m0_to_float(uint32_t b) {
+  if (b == 255u) return __uint_as_float(0x7FC00000u);
+  return __uint_as_float(b == 0u ? 0x00400000u : (b << 23));
+}
+
+// Scale of row `row` for 8-channel slice v: kMx = E8M0 bytes, one per 32
+// channels ([R, hidden/32]); else fp32, one per 128 channels ([R, hidden/128]).
+template <bool kMx>
+__device__ __forceinline__ float fp8_row_scale(const void* __restrict__ scales, int64_t row,
+                                               int32_t hidden, int32_t v) {
+  if constexpr (kMx)
+    return e8m0_to_float(static_cast<const uint8_t*>(scales)[row * (hidden / 32) + v / 4]);
+  else
+    return static_cast<const float*>(scales)[row * (hidden / kFp8Block) + v / 16];
+}
+
 // One 8-channel slice v of token t: all K code and scale loads first, then the sum.
-template <int K>
+template <int K, bool kMx>
 __device__ __forceinline__ void combine_fp8_slice(const uint8_t* __restrict__ q,
-                                                  const float* __restrict__ scales,
+                                                  const void* __restrict__ scales,
                                                   const int32_t* s, const float* wt, int32_t k,
-                                                  int32_t hidden, int32_t blocks, int32_t v,
+                                                  int32_t hidden, int32_t v,
                                                   u32x4* __restrict__ dst) {
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if constexpr (K > 0) {
@@ -263,7 +281,7 @@ __device__ __forceinline__ void combine_fp8_slice(const uint8_t* __restrict__ q,
     for (int j = 0; j < K; ++j) {
       const int64_t row = s[j] >= 0 ? s[j] : 0;
       c[j] = load_nt8(q + row * hidden + 8 * v);
-      sc[j] = scales[row * blocks + v / 16];
+      sc[j] = fp8_row_scale<kMx>(scales, row, hidden, v);
     }
 #pragma unroll
     for (int j = 0; j < K; ++j) accumulate8_fp8(acc, c[j], wt[j] * sc[j], s[j] >= 0);
@@ -272,22 +290,21 @@ __device__ __forceinline__ void combine_fp8_slice(const uint8_t* __restrict__ q,
       const int32_t sj = s[j];
       if (sj < 0) continue;
       accumulate8_fp8(acc, load_nt8(q + (int64_t)sj * hidden + 8 * v),
-                      wt[j] * scales[(int64_t)sj * blocks + v / 16], true);
+                      wt[j] * fp8_row_scale<kMx>(scales, sj, hidden, v), true);
     }
   }
   store_nt(dst + v, pack8(acc));
 }
 
-template <int K, bool kWhole>
+template <int K, bool kWhole, bool kMx>
 __global__ __launch_bounds__(1024) void combine_fp8_kernel(
-    const uint8_t* __restrict__ q, const float* __restrict__ scales, const float* __restrict__ w,
+    const uint8_t* __restrict__ q, const void* __restrict__ scales, const float* __restrict__ w,
     const int32_t* __restrict__ slot_idx, int64_t num_tokens, int32_t k, int32_t hidden,
     CombineMap m, u32x4* __restrict__ out) {
   int64_t t;
   int32_t lt;
   if (!combine_token<kWhole>(m, num_tokens, t, lt)) return;
   const int32_t vecs = hidden / 8;  // 8-channel slices per row
-  const int32_t blocks = hidden / kFp8Block;
   const int32_t kk = K > 0 ? K : k;
   u32x4* dst = out + t * vecs;
   int32_t s[K > 0 ? K : 1];
@@ -303,42 +320,55 @@ __global__ __launch_bounds__(1024) void combine_fp8_kernel(
   const float* wp = K > 0 ? ww : w + t * kk;
   if (vecs <= m.lanes_per_token) {
     // one pass covers the row: straight-line code, every load issued up front
-    if (lt < vecs) combine_fp8_slice<K>(q, scales, sp, wp, k, hidden, blocks, lt, dst);
+    if (lt < vecs) combine_fp8_slice<K, kMx>(q, scales, sp, wp, k, hidden, lt, dst);
   } else {
     for (int32_t v = lt; v < vecs; v += m.lanes_per_token)
-      combine_fp8_slice<K>(q, scales, sp, wp, k, hidden, blocks, v, dst);
+      combine_fp8_slice<K, kMx>(q, scales, sp, wp, k, hidden, v, dst);
   }
 }
 
-template <int K>
+template <int K, bool kMx>
 static void launch_fp8_k(dim3 grid, dim3 block, hipStream_t stream, const uint8_t* q,
-                         const float* scales, const float* w, const ep_layout_t& L,
+                         const void* scales, const float* w, const ep_layout_t& L,
                          int32_t hidden, CombineMap m, void* out) {
   if (m.tokens_per_block == 1)
-    hipLaunchKernelGGL((combine_fp8_kernel<K, true>), grid, block, 0, stream, q, scales, w,
+    hipLaunchKernelGGL((combine_fp8_kernel<K, true, kMx>), grid, block, 0, stream, q, scales, w,
                        L.slot_idx, L.num_tokens, L.num_topk, hidden, m, static_cast<u32x4*>(out));
   else
-    hipLaunchKernelGGL((combine_fp8_kernel<K, false>), grid, block, 0, stream, q, scales, w,
+    hipLaunchKernelGGL((combine_fp8_kernel<K, false, kMx>), grid, block, 0, stream, q, scales, w,
                        L.slot_idx, L.num_tokens, L.num_topk, hidden, m, static_cast<u32x4*>(out));
 }
 
-hipError_t launch_combine_fp8(const uint8_t* q, const float* scales, const float* w,
-                              const ep_layout_t& L, int32_t hidden, void* out,
-                              hipStream_t stream) {
+template <bool kMx>
+static hipError_t launch_combine_codes(const uint8_t* q, const void* scales, const float* w,
+                                       const ep_layout_t& L, int32_t hidden, void* out,
+                                       hipStream_t stream) {
   const int64_t T = L.num_tokens;
   if (T == 0) return hipSuccess;
   const CombineMap m = combine_map(hidden / 8);
   const dim3 grid((unsigned)((T + m.tokens_per_block - 1) / m.tokens_per_block));
   const dim3 block(m.lanes_per_token * m.tokens_per_block);
   switch (L.num_topk) {
-    case 1: launch_fp8_k<1>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
-    case 2: launch_fp8_k<2>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
-    case 4: launch_fp8_k<4>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
-    case 6: launch_fp8_k<6>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
-    case 8: launch_fp8_k<8>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
-    default: launch_fp8_k<0>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
+    case 1: launch_fp8_k<1, kMx>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
+    case 2: launch_fp8_k<2, kMx>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
+    case 4: launch_fp8_k<4, kMx>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
+    case 6: launch_fp8_k<6, kMx>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
+    case 8: launch_fp8_k<8, kMx>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
+    default: launch_fp8_k<0, kMx>(grid, block, stream, q, scales, w, L, hidden, m, out); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_combine_fp8(const uint8_t* q, const float* scales, const float* w,
+                              const ep_layout_t& L, int32_t hidden, void* out,
+                              hipStream_t stream) {
+  return launch_combine_codes<false>(q, scales, w, L, hidden, out, stream);
+}
+
+hipError_t launch_combine_mxfp8(const uint8_t* q, const uint8_t* scales, const float* w,
+                                const ep_layout_t& L, int32_t hidden, void* out,
+                                hipStream_t stream) {
+  return launch_combine_codes<true>(q, scales, w, L, hidden, out, stream);
 }
 
 }  // namespace ep

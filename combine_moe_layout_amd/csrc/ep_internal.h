@@ -97,6 +97,12 @@ hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout
 hipError_t launch_combine_fp8(const uint8_t* q, const float* scales, const float* w,
                               const ep_layout_t& L, int32_t hidden, void* out, hipStream_t stream);
 
+// Combine of MXFP8 expert outputs: E4M3 codes [R, hidden] with one E8M0 byte
+// per 32 channels [R, hidden/32].
+hipError_t launch_combine_mxfp8(const uint8_t* q, const uint8_t* scales, const float* w,
+                                const ep_layout_t& L, int32_t hidden, void* out,
+                                hipStream_t stream);
+
 // Per-group dedup variant: the group layout (a layout whose experts are the
 // G groups, with kg = min(k, G) entries per token) and its unit-weight combine.
 size_t group_layout_workspace_bytes(int64_t T, int32_t k, int32_t G);

@@ -256,6 +256,20 @@ int ep_combine_fp8(const uint8_t* expert_q, const float* expert_scales,
                    void* stream);
 
 /*
+ * Combine of MXFP8 expert outputs (the FP8 combine of [yololab] "FP8與低精度
+ * 通訊" in the format EP_MXFP8_E4M3 dispatch produces).  expert_q: device uint8
+ * [R, hidden] E4M3 codes; expert_scales: device uint8 [R, hidden/32], one E8M0
+ * byte per row and 32-channel block, value 2^(byte - 127) (255 is NaN).
+ * out[t] = bf16(sum over valid j of topk_weights[t,j] * decode(code) *
+ * 2^(byte - 127)), accumulated in fp32, rounded to nearest-even; +0 for a token
+ * with no valid pair.  hidden % 128 == 0.
+ * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN or EP_ERR_LAUNCH.
+ */
+int ep_combine_mxfp8(const uint8_t* expert_q, const uint8_t* expert_scales,
+                     const float* topk_weights, const ep_layout_t* layout, int32_t hidden,
+                     void* out, void* stream);
+
+/*
  * Per-group dedup variant.  A token goes once to every group of experts that
  * holds at least one of its top-k experts (a group is what one EP rank would
  * own), instead of once per expert: the pages count each rank's send and

@@ -169,6 +169,10 @@ def test_entry_points_reject_bad_arguments(L):
     assert L.ep_dispatch(fake, by(s), 256, mn | 3, fake, fake + 1, None) == -3
     assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake, 256, mn | 0, fake, None, None) == -6
     assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake, 256, mn | 1, fake, None, None) == -1
+    assert L.ep_combine_mxfp8(None, fake, fake, by(s), 256, fake, None) == -1
+    assert L.ep_combine_mxfp8(fake, fake, fake, by(s), 200, fake, None) == -2   # hidden % 128
+    assert L.ep_combine_mxfp8(fake + 8, fake, fake, by(s), 256, fake, None) == -3
+    assert L.ep_combine_mxfp8(fake, fake + 1, fake + 2, by(s), 256, fake, None) == -3  # weights
     assert L.ep_combine_f16(None, fake, by(s), 256, fake, None) == -1
     assert L.ep_combine_f16(fake, fake, by(s), 252, fake, None) == -2
     assert L.ep_combine_f16(fake, fake, by(s), 256, fake + 8, None) == -3

@@ -35,8 +35,8 @@ def test_more_than_one_gpu_exits_with_a_message(args, env):
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
-@pytest.mark.parametrize("flags", [["--mx", "--pow2"], ["--mx", "--fp8-combine"],
-                                   ["--dedup", "--fused"], ["--dedup", "--graph"],
+@pytest.mark.parametrize("flags", [["--mx", "--pow2"],
+                                   ["--dedup", "--fused"], ["--dedup", "--graph"], ["--mx", "--pow2", "--fp8-combine"],
                                    ["--mn-scales", "--fp8-combine"], ["--mn-convert", "--mn-scales"],
                                    ["--mn-convert", "--dedup"]])
 def test_flag_combinations_it_does_not_time_are_rejected(flags):
