@@ -81,6 +81,22 @@ def test_missing_library_is_an_error(monkeypatch):
         binding.lib()
 
 
+def test_binding_rejects_host_tensors_before_any_launch(L):
+    """Every step runs on the GPU: host tensors are refused with an error,
+    never computed on the CPU."""
+    import torch
+    lay = binding.EpLayout(16, 2, 8, 2, device=torch.device("cpu"))
+    idx = torch.zeros((16, 2), dtype=torch.int64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding.ep_get_layout(idx, lay)
+    x = torch.zeros((16, 256), dtype=torch.bfloat16)
+    recv = torch.zeros((lay.num_recv_rows, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding.ep_dispatch(x, lay, binding.EP_BF16, recv)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding.ep_combine(recv, torch.zeros((16, 2)), lay, x)
+
+
 def test_layout_init_validation(L):
     s = binding.ep_layout_t()
     ok = L.ep_layout_init(ctypes.byref(s), 8192, 8, 256, 8, 0)
