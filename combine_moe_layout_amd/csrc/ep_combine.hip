@@ -29,9 +29,11 @@
 namespace ep {
 
 struct CombineMap {
-  int32_t lanes_per_token;
+  int32_t lanes_per_token;   // lanes of one workgroup given to a token
   int32_t tokens_per_block;
+  int32_t slices;            // workgroups per token (1 unless one token per workgroup)
 };
+
 
 // Rows hold 2-byte elements: bf16, or IEEE fp16 when kF16 (decoded exactly
 // by the conversion instruction; results rounded to nearest-even by it, with
@@ -72,14 +74,16 @@ __device__ __forceinline__ u32x4 pack8(const float* acc) {
                pack_elem2<kF16>(acc[4], acc[5]), pack_elem2<kF16>(acc[6], acc[7])};
 }
 
-// Token and lane of this thread.  kWhole: one token per workgroup, so the token
-// index is uniform and its slots and weights come in through scalar loads.
+// Token and lane of this thread.  kWhole: one token per workgroup (or per
+// m.slices consecutive workgroups, each taking every slices-th run of
+// lanes_per_token vectors), so the token index is uniform and its slots and
+// weights come in through scalar loads.
 template <bool kWhole>
 __device__ __forceinline__ bool combine_token(const CombineMap& m, int64_t num_tokens, int64_t& t,
                                               int32_t& lt) {
   if constexpr (kWhole) {
-    t = blockIdx.x;
-    lt = threadIdx.x;
+    t = blockIdx.x / m.slices;
+    lt = (int32_t)(blockIdx.x % m.slices) * m.lanes_per_token + threadIdx.x;
   } else {
     t = (int64_t)blockIdx.x * m.tokens_per_block + threadIdx.x / m.lanes_per_token;
     lt = threadIdx.x % m.lanes_per_token;
@@ -100,6 +104,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(
   int32_t lt;
   if (!combine_token<kWhole>(m, num_tokens, t, lt)) return;
   const int32_t vec_per_row = hidden / 8;
+  const int32_t stride = m.lanes_per_token * m.slices;
   const int32_t kk = K > 0 ? K : k;
   const int32_t* slots = slot_idx + t * kk;
   const float* wt = kUnit ? nullptr : w + t * kk;
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(
       s[j] = slots[j];
       ww[j] = kUnit ? 1.0f : wt[j];
     }
-    for (int32_t v = lt; v < vec_per_row; v += m.lanes_per_token) {
+    for (int32_t v = lt; v < vec_per_row; v += stride) {
       u32x4 d[K];
 #pragma unroll
       for (int j = 0; j < K; ++j) {
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(
       store_nt(dst + v, pack8<kF16>(acc));
     }
   } else {
-    for (int32_t v = lt; v < vec_per_row; v += m.lanes_per_token) {
+    for (int32_t v = lt; v < vec_per_row; v += stride) {
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       for (int32_t j = 0; j < k; ++j) {
         const int32_t sj = slots[j];
@@ -152,6 +157,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(
 // share a 256-lane workgroup with other tokens.
 static CombineMap combine_map(int32_t vecs_per_row) {
   CombineMap m;
+  m.slices = 1;
   if (vecs_per_row >= 64) {
     m.lanes_per_token = vecs_per_row <= 1024 ? ((vecs_per_row + 63) / 64) * 64 : 1024;
     m.tokens_per_block = 1;
@@ -162,6 +168,26 @@ static CombineMap combine_map(int32_t vecs_per_row) {
     m.tokens_per_block = 256 / l;
   }
   return m;
+}
+
+// Decode-sized batches (one token per workgroup, at most kFusedMaxPairs pairs)
+// leave most of the chip idle: each token is spread over up to 8 workgroups,
+// each taking at least one wave of vectors, so that about one workgroup runs
+// per CU and all CUs share the row traffic.  Measured at hidden 7168, top-8,
+// with the calls replayed from a HIP graph: bf16 5.0 -> 4.2 us at 128 tokens
+// and 4.1 -> 3.0 us at 32; FP8 4.6 -> 3.8 and 3.9 -> 3.0 us.  At 256 tokens
+// (already one per CU) splitting gains nothing.
+static void split_tokens(int32_t vecs, int64_t T, CombineMap& m, dim3& grid, dim3& block) {
+  int64_t S = kChipCUs / T;
+  if (S > 8) S = 8;
+  if (S > vecs / 64) S = vecs / 64;
+  if (S <= 1) return;
+  int32_t lanes = (((vecs + S - 1) / S + 63) / 64) * 64;
+  if (lanes > 1024) lanes = 1024;
+  m.lanes_per_token = lanes;
+  m.slices = (int32_t)S;
+  grid = dim3((unsigned)(T * S));
+  block = dim3((unsigned)lanes);
 }
 
 // Large batches take the general token mapping (which also covers one token
@@ -175,11 +201,12 @@ static void launch_k(dim3 grid, dim3 block, hipStream_t stream, const void* y, c
                      const ep_layout_t& L, int32_t hidden, CombineMap m, void* out) {
   const bool whole = m.tokens_per_block == 1 &&
                      L.num_tokens * (int64_t)L.num_topk <= (int64_t)kFusedMaxPairs;
-  if (whole)
+  if (whole) {
+    split_tokens(hidden / 8, L.num_tokens, m, grid, block);
     hipLaunchKernelGGL((combine_kernel<K, kUnit, kF16, true>), grid, block, 0, stream,
                        static_cast<const u32x4*>(y), w, L.slot_idx, L.num_tokens, L.num_topk,
                        hidden, m, static_cast<u32x4*>(out));
-  else
+  } else
     hipLaunchKernelGGL((combine_kernel<K, kUnit, kF16>), grid, block, 0, stream,
                        static_cast<const u32x4*>(y), w, L.slot_idx, L.num_tokens, L.num_topk,
                        hidden, m, static_cast<u32x4*>(out));
@@ -305,6 +332,7 @@ __global__ __launch_bounds__(1024) void combine_fp8_kernel(
   int32_t lt;
   if (!combine_token<kWhole>(m, num_tokens, t, lt)) return;
   const int32_t vecs = hidden / 8;  // 8-channel slices per row
+  const int32_t stride = m.lanes_per_token * m.slices;
   const int32_t kk = K > 0 ? K : k;
   u32x4* dst = out + t * vecs;
   int32_t s[K > 0 ? K : 1];
@@ -318,11 +346,11 @@ __global__ __launch_bounds__(1024) void combine_fp8_kernel(
   }
   const int32_t* sp = K > 0 ? s : slot_idx + t * kk;
   const float* wp = K > 0 ? ww : w + t * kk;
-  if (vecs <= m.lanes_per_token) {
+  if (vecs <= stride) {
     // one pass covers the row: straight-line code, every load issued up front
     if (lt < vecs) combine_fp8_slice<K, kMx>(q, scales, sp, wp, k, hidden, lt, dst);
   } else {
-    for (int32_t v = lt; v < vecs; v += m.lanes_per_token)
+    for (int32_t v = lt; v < vecs; v += stride)
       combine_fp8_slice<K, kMx>(q, scales, sp, wp, k, hidden, v, dst);
   }
 }
@@ -331,6 +359,8 @@ template <int K, bool kMx>
 static void launch_fp8_k(dim3 grid, dim3 block, hipStream_t stream, const uint8_t* q,
                          const void* scales, const float* w, const ep_layout_t& L,
                          int32_t hidden, CombineMap m, void* out) {
+  if (m.tokens_per_block == 1 && L.num_tokens * (int64_t)L.num_topk <= (int64_t)kFusedMaxPairs)
+    split_tokens(hidden / 8, L.num_tokens, m, grid, block);
   if (m.tokens_per_block == 1)
     hipLaunchKernelGGL((combine_fp8_kernel<K, true, kMx>), grid, block, 0, stream, q, scales, w,
                        L.slot_idx, L.num_tokens, L.num_topk, hidden, m, static_cast<u32x4*>(out));

@@ -87,6 +87,8 @@ constexpr bool kDispatchUsesHwCast = true;
 // kFusedMaxTopk, take the one-launch layout+dispatch path.
 constexpr int kFusedMaxPairs = kChunkPairs;
 constexpr int kFusedMaxTopk = 8;
+// Compute units of the MI355X (gfx950) this library is built for.
+constexpr int kChipCUs = 256;
 
 bool fused_layout_dispatch_fits(const ep_layout_t& L);
 
