@@ -78,6 +78,11 @@ __device__ int32_t block_exclusive_scan(const int32_t* in, int32_t* out, int n, 
   return total;
 }
 
+// Workgroups have at least kFusedMinLanes lanes, so a lane loads at most
+// kTableTrips entries of the top-k table.
+constexpr int kFusedMinLanes = 256;
+constexpr int kTableTrips = kFusedMaxPairs / kFusedMinLanes;
+
 template <bool kFp8, bool kHw, int kMode>
 __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a) {
   __shared__ int32_t s_idx[kFusedMaxPairs];  // expert of every pair, -1 if none
@@ -108,12 +113,24 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
     }
   }
 
+  // The table in at most kTableTrips loads per lane, all issued before the
+  // first is used: a loop that stores each entry to LDS before loading the
+  // next would wait one memory latency per trip.
+  int64_t tv[kTableTrips];
+#pragma unroll
+  for (int i = 0; i < kTableTrips; ++i) {
+    const int32_t p = tid + i * (int32_t)blockDim.x;
+    tv[i] = p < P ? a.topk_idx[p] : -1;
+  }
   bool bad = false;
-  for (int32_t p = tid; p < P; p += blockDim.x) {
-    const int64_t v = a.topk_idx[p];
-    const bool ok = v >= 0 && v < E;
-    bad |= !ok && v != -1;
-    s_idx[p] = ok ? (int32_t)v : -1;
+#pragma unroll
+  for (int i = 0; i < kTableTrips; ++i) {
+    const int32_t p = tid + i * (int32_t)blockDim.x;
+    if (p < P) {
+      const bool ok = tv[i] >= 0 && tv[i] < E;
+      bad |= !ok && tv[i] != -1;
+      s_idx[p] = ok ? (int32_t)tv[i] : -1;
+    }
   }
   if (tid < 2 * kFusedMaxTopk) s_sum[tid] = 0;
   __syncthreads();
@@ -245,7 +262,7 @@ hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout
   // at least 256 lanes for the table scan, at most 1024 (longer rows loop)
   const int32_t vecs = fp8 ? hidden / 16 : hidden / 8;
   int32_t lanes = ((vecs + 63) / 64) * 64;
-  lanes = lanes < 256 ? 256 : (lanes > 1024 ? 1024 : lanes);
+  lanes = lanes < kFusedMinLanes ? kFusedMinLanes : (lanes > 1024 ? 1024 : lanes);
   const dim3 grid((unsigned)(L.num_tokens + 1));
   if (dtype == EP_FP8_E4M3)
     hipLaunchKernelGGL((layout_dispatch_small_kernel<true, kDispatchUsesHwCast, kScaleF32>), grid,
