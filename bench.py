@@ -161,8 +161,11 @@ def main() -> int:
     ap.add_argument("--workload", default="dsv3",
                     help="dsv3 (default: the metric's configuration), tiny, skewed, lowlat or large")
     ap.add_argument("--graph", action="store_true",
-                    help="capture one step in a HIP graph and time its replays (launch-bound "
-                         "workloads); per-kernel times are then not reported")
+                    help="record consecutive steps in a HIP graph and time its replays "
+                         "(launch-bound workloads); per-kernel times are then not reported")
+    ap.add_argument("--graph-steps", type=int, default=10,
+                    help="steps recorded in the graph, back to back, as a decode loop's "
+                         "layers would be (must divide --steps)")
     ap.add_argument("--pow2", action="store_true",
                     help="FP8 dispatch with power-of-two scales (EP_FP8_E4M3_POW2)")
     ap.add_argument("--fp8-combine", action="store_true",
@@ -191,6 +194,9 @@ def main() -> int:
     if args.mn_convert and (args.mn_scales or args.fused or args.dedup or args.graph):
         print("--mn-convert times layout, dispatch, conversion and combine as separate calls",
               file=sys.stderr)
+        return 2
+    if args.graph and (args.graph_steps < 1 or args.steps % args.graph_steps != 0):
+        print("--graph-steps must be positive and divide --steps", file=sys.stderr)
         return 2
     if args.mn_scales and args.fp8_combine:
         print("--mn-scales does not combine with --fp8-combine (ep_combine_fp8 reads row-major "
@@ -354,11 +360,13 @@ def main() -> int:
     torch.cuda.synchronize()
 
     graph = None
+    gs = args.graph_steps if args.graph else 1   # steps per replay
     if args.graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
-        for _ in range(args.warmup):
+            for _ in range(gs):
+                step()
+        for _ in range(max(1, args.warmup // gs)):
             graph.replay()
         torch.cuda.synchronize()
 
@@ -368,12 +376,13 @@ def main() -> int:
     # each costs a few us of its own on the GPU, so the step rate is taken
     # from the timed loop below, which records none.
     if graph is not None:
-        events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                  for _ in range(args.steps // gs)]
     else:
         events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     e0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(len(events)):
         if graph is not None:
             events[i][0].record(stream)
             graph.replay()
@@ -387,17 +396,18 @@ def main() -> int:
     # enqueued between them
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        if graph is not None:
+    if graph is not None:
+        for _ in range(args.steps // gs):
             graph.replay()
-        else:
+    else:
+        for _ in range(args.steps):
             step(None, stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     if graph is not None:
-        per = {"graph_step": [ev[0].elapsed_time(ev[1]) for ev in events]}
+        per = {"graph_step": [ev[0].elapsed_time(ev[1]) / gs for ev in events]}
     elif args.fused:
         per = {"layout_dispatch": [ev[0].elapsed_time(ev[2]) for ev in events]}
     else:
@@ -529,7 +539,8 @@ def main() -> int:
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
             "algorithmic_bytes": nbytes["combine"]}
     else:
-        result["config"]["step"] += " (HIP graph replay)"
+        result["config"]["step"] += " (HIP graph replay, %d steps per graph)" % gs
+        result["graph_steps"] = gs
     if flushed is not None:
         d_key = "layout_dispatch" if args.fused else "dispatch"
         d_bytes_f = nbytes["dispatch"] + (nbytes["layout"] if args.fused else 0) + nbytes.get("scales_mn", 0)

@@ -38,7 +38,8 @@ def test_more_than_one_gpu_exits_with_a_message(args, env):
 @pytest.mark.parametrize("flags", [["--mx", "--pow2"],
                                    ["--dedup", "--fused"], ["--dedup", "--graph"], ["--mx", "--pow2", "--fp8-combine"],
                                    ["--mn-scales", "--fp8-combine"], ["--mn-convert", "--mn-scales"],
-                                   ["--mn-convert", "--dedup"]])
+                                   ["--mn-convert", "--dedup"], ["--graph", "--graph-steps", "3"],
+                                   ["--graph", "--graph-steps", "0"]])
 def test_flag_combinations_it_does_not_time_are_rejected(flags):
     r = _run(*flags)
     assert r.returncode == 2 and r.stdout == "", (flags, r.stderr)
