@@ -7,15 +7,14 @@
 // batch of at most kFusedMaxPairs (token, k) pairs this kernel computes the
 // same layout as ep_get_layout and the same receive rows as ep_dispatch, with
 // one launch and no barrier between workgroups:
-//   - every workgroup loads the whole (small) top-k table into LDS; a token's
+//   - every workgroup reads the whole (small) top-k table; a token's
 //     workgroup first issues the loads of its token's row, so that their
 //     latency overlaps the table's;
-//   - workgroup t < T finds its own token's receive rows directly: for each of
-//     its k pairs, the number of valid pairs routed to a lower expert (the
-//     expert's offset, contiguous mode) plus the number of earlier pairs
-//     routed to the same expert (its rank; padded mode keeps rank < capacity),
-//     counted over the table with one ballot per wave and table slice and
-//     summed across the workgroup -- exactly the stable counting-sort position
+//   - workgroup t < T finds its own token's receive rows directly: an LDS
+//     histogram of the pairs before its token gives each of its k pairs the
+//     rank within its expert (padded mode keeps rank < capacity), and in
+//     contiguous mode an exclusive scan of the whole table's histogram gives
+//     the expert's first row -- exactly the stable counting-sort position
 //     ep_get_layout assigns;
 //     it writes those slot_idx / recv_src entries and then dispatches the
 //     token like ep_dispatch;
@@ -85,10 +84,10 @@ constexpr int kTableTrips = kFusedMaxPairs / kFusedMinLanes;
 
 template <bool kFp8, bool kHw, int kMode>
 __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a) {
-  __shared__ int32_t s_idx[kFusedMaxPairs];  // expert of every pair, -1 if none
-  __shared__ int32_t s_sum[2 * kFusedMaxTopk];
+  __shared__ int32_t s_tok[kFusedMaxTopk];  // this token's experts, -1 if none
   __shared__ int32_t s_slot[kFusedMaxTopk];
   __shared__ int32_t s_hist[EP_MAX_EXPERTS];
+  __shared__ int32_t s_pre[EP_MAX_EXPERTS];
   __shared__ int32_t s_off[EP_MAX_EXPERTS];
   __shared__ int32_t s_wave[1024 / kWave];
   __shared__ uint32_t s_scale[kMaxScalesPerBlock];
@@ -122,6 +121,18 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
     const int32_t p = tid + i * (int32_t)blockDim.x;
     tv[i] = p < P ? a.topk_idx[p] : -1;
   }
+  // Histograms of the valid pairs: of the whole table (s_hist; the
+  // metadata workgroup's counts, and each expert's first row in contiguous
+  // mode after a scan) and of the pairs before this token (s_pre; the rank of
+  // the token's pairs within their experts).  Padded mode places rows at
+  // e * capacity, so its token workgroups need only s_pre.
+  const bool need_hist = !token_block || a.capacity == 0;
+  const int32_t p0 = token_block ? (int32_t)blockIdx.x * k : 0;
+  for (int e = tid; e < E; e += blockDim.x) {
+    s_hist[e] = 0;
+    s_pre[e] = 0;
+  }
+  __syncthreads();
   bool bad = false;
 #pragma unroll
   for (int i = 0; i < kTableTrips; ++i) {
@@ -129,19 +140,18 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
     if (p < P) {
       const bool ok = tv[i] >= 0 && tv[i] < E;
       bad |= !ok && tv[i] != -1;
-      s_idx[p] = ok ? (int32_t)tv[i] : -1;
+      const int32_t e = ok ? (int32_t)tv[i] : -1;
+      if (e >= 0) {
+        if (need_hist) atomicAdd(&s_hist[e], 1);
+        if (p < p0) atomicAdd(&s_pre[e], 1);
+      }
+      if (token_block && p >= p0 && p < p0 + k) s_tok[p - p0] = e;
     }
   }
-  if (tid < 2 * kFusedMaxTopk) s_sum[tid] = 0;
   __syncthreads();
 
-  if (blockIdx.x == a.num_tokens) {
-    // metadata: histogram, offsets, group totals, flags
-    for (int e = tid; e < E; e += blockDim.x) s_hist[e] = 0;
-    __syncthreads();
-    for (int32_t p = tid; p < P; p += blockDim.x)
-      if (s_idx[p] >= 0) atomicAdd(&s_hist[s_idx[p]], 1);
-    __syncthreads();
+  if (!token_block) {
+    // metadata: counts, offsets, group totals, flags
     const int32_t total = block_exclusive_scan(s_hist, s_off, E, s_wave);
     bool over = false;
     for (int e = tid; e < E; e += blockDim.x) {
@@ -163,44 +173,19 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
     return;
   }
 
-  // this token's receive rows: per entry j, the valid pairs routed to a lower
-  // expert and the earlier pairs routed to the same expert, counted per wave
-  // with ballots (e[j] is the same for every lane) and summed over the waves
-  const int64_t t = blockIdx.x;
-  const int32_t p0 = (int32_t)(t * k);
-  int32_t e[kFusedMaxTopk], lower[kFusedMaxTopk], earlier[kFusedMaxTopk];
-#pragma unroll
-  for (int j = 0; j < kFusedMaxTopk; ++j) {
-    e[j] = j < k ? s_idx[p0 + j] : -1;
-    lower[j] = 0;
-    earlier[j] = 0;
-  }
-  for (int32_t base = 0; base < P; base += blockDim.x) {  // the same trip count in every lane
-    const int32_t p = base + tid;
-    const int32_t ep = p < P ? s_idx[p] : -1;
-#pragma unroll
-    for (int j = 0; j < kFusedMaxTopk; ++j) {
-      lower[j] += __popcll(__ballot(ep >= 0 && ep < e[j]));
-      earlier[j] += __popcll(__ballot(ep >= 0 && ep == e[j] && p < p0 + j));
-    }
-  }
-  if (tid % kWave == 0) {
-#pragma unroll
-    for (int j = 0; j < kFusedMaxTopk; ++j) {
-      if (j < k) {
-        atomicAdd(&s_sum[j], lower[j]);
-        atomicAdd(&s_sum[kFusedMaxTopk + j], earlier[j]);
-      }
-    }
-  }
-  __syncthreads();
+  // this token's receive rows: pair j of expert e takes rank s_pre[e] plus
+  // the token's earlier pairs of e -- its stable counting-sort position, as
+  // ep_get_layout assigns it
+  if (a.capacity == 0) block_exclusive_scan(s_hist, s_off, E, s_wave);
   if (tid < k) {
     const int j = tid;
+    const int32_t e = s_tok[j];
     int32_t s = -1;
-    if (e[j] >= 0) {
-      const int32_t rank = s_sum[kFusedMaxTopk + j];
-      if (a.capacity == 0) s = s_sum[j] + rank;
-      else if (rank < a.capacity) s = e[j] * a.capacity + rank;
+    if (e >= 0) {
+      int32_t rank = s_pre[e];
+      for (int i = 0; i < j; ++i) rank += s_tok[i] == e ? 1 : 0;
+      if (a.capacity == 0) s = s_off[e] + rank;
+      else if (rank < a.capacity) s = e * a.capacity + rank;
     }
     s_slot[j] = s;
     a.slot_idx[p0 + j] = s;
