@@ -40,6 +40,8 @@ struct FusedArgs {
   int32_t* expert_offsets;
   int32_t* num_tokens_per_group;
   int32_t* error_flags;
+  const int32_t* extra_flags;  // flag entries a kernel that prepared the ids wrote (or null)
+  int32_t num_extra_flags;
 };
 
 // Exclusive scan of n <= EP_MAX_EXPERTS values in LDS (in place into out),
@@ -82,7 +84,9 @@ __device__ int32_t block_exclusive_scan(const int32_t* in, int32_t* out, int n, 
 constexpr int kFusedMinLanes = 256;
 constexpr int kTableTrips = kFusedMaxPairs / kFusedMinLanes;
 
-template <bool kFp8, bool kHw, int kMode>
+// kDispatch = false: the layout alone (ep_get_layout for batches of one
+// layout chunk); x, recv and scales are not touched.
+template <bool kFp8, bool kHw, int kMode, bool kDispatch = true>
 __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a) {
   __shared__ int32_t s_tok[kFusedMaxTopk];  // this token's experts, -1 if none
   __shared__ int32_t s_slot[kFusedMaxTopk];
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
   const bool one_pass = vecs <= (int32_t)blockDim.x;
   const u32x4* src = a.x + (int64_t)blockIdx.x * (a.hidden / 8);
   u32x4 pre_lo = {0u, 0u, 0u, 0u}, pre_hi = {0u, 0u, 0u, 0u};
-  if (token_block && one_pass && tid < vecs) {
+  if (kDispatch && token_block && one_pass && tid < vecs) {
     if constexpr (kFp8) {
       pre_lo = src[2 * tid];
       pre_hi = src[2 * tid + 1];
@@ -121,6 +125,11 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
     const int32_t p = tid + i * (int32_t)blockDim.x;
     tv[i] = p < P ? a.topk_idx[p] : -1;
   }
+  // the metadata workgroup ORs in the flag entries of a prepared table
+  int32_t extra_bits = 0;
+  if (!token_block && a.extra_flags != nullptr)
+    for (int32_t i = tid; i < a.num_extra_flags; i += blockDim.x) extra_bits |= a.extra_flags[i];
+
   // Histograms of the valid pairs: of the whole table (s_hist; the
   // metadata workgroup's counts, and each expert's first row in contiguous
   // mode after a scan) and of the pairs before this token (s_pre; the rank of
@@ -166,6 +175,8 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
       for (int e = g * per_group; e < (g + 1) * per_group; ++e) s += s_hist[e];
       a.num_tokens_per_group[g] = s;
     }
+    bad |= (extra_bits & EP_FLAG_BAD_EXPERT) != 0;
+    over |= (extra_bits & EP_FLAG_OVERFLOW) != 0;
     const int any_bad = __syncthreads_or(bad ? 1 : 0);
     const int any_over = __syncthreads_or(over ? 1 : 0);
     if (tid == 0)
@@ -192,6 +203,8 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
     if (a.recv_src != nullptr && s >= 0) a.recv_src[s] = p0 + j;
   }
   __syncthreads();
+
+  if constexpr (!kDispatch) return;
 
   // dispatch the token (one token per workgroup, all lanes on its row)
   if (one_pass) {
@@ -225,7 +238,9 @@ hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout
   const int64_t mn_rows = dtype_scales_mn(dtype) ? L.num_recv_rows : 0;
   dtype = dtype_base(dtype);
   const bool fp8 = dtype_is_fp8(dtype);
-  FusedArgs a;
+  FusedArgs a = {};
+  a.extra_flags = nullptr;  // the top-k table comes from the caller: no prepared flags
+  a.num_extra_flags = 0;
   a.topk_idx = topk_idx;
   a.num_tokens = L.num_tokens;
   a.k = L.num_topk;
@@ -261,6 +276,33 @@ hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout
   else  // EP_BF16 and EP_F16: a bit copy
     hipLaunchKernelGGL((layout_dispatch_small_kernel<false, kDispatchUsesHwCast, kScaleF32>), grid,
                        dim3(lanes), 0, stream, a);
+  return hipGetLastError();
+}
+
+// The layout alone for a batch that fits the fused kernel: one workgroup of
+// kFusedMinLanes lanes per token plus the metadata workgroup, one launch.
+// extra_flags: num_extra flag entries written by the kernel that prepared the
+// ids (the group layout's table), ORed into error_flags.
+hipError_t launch_layout_small(const int64_t* topk_idx, const ep_layout_t& L,
+                               const int32_t* extra_flags, int32_t num_extra,
+                               hipStream_t stream) {
+  FusedArgs a = {};
+  a.extra_flags = extra_flags;
+  a.num_extra_flags = num_extra;
+  a.topk_idx = topk_idx;
+  a.num_tokens = L.num_tokens;
+  a.k = L.num_topk;
+  a.num_experts = L.num_experts;
+  a.num_groups = L.num_groups;
+  a.capacity = L.capacity;
+  a.slot_idx = L.slot_idx;
+  a.recv_src = L.recv_src;
+  a.num_tokens_per_expert = L.num_tokens_per_expert;
+  a.expert_offsets = L.expert_offsets;
+  a.num_tokens_per_group = L.num_tokens_per_group;
+  a.error_flags = L.error_flags;
+  hipLaunchKernelGGL((layout_dispatch_small_kernel<false, kDispatchUsesHwCast, kScaleF32, false>),
+                     dim3((unsigned)(L.num_tokens + 1)), dim3(kFusedMinLanes), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -91,6 +91,9 @@ constexpr int kFusedMaxTopk = 8;
 constexpr int kChipCUs = 256;
 
 bool fused_layout_dispatch_fits(const ep_layout_t& L);
+hipError_t launch_layout_small(const int64_t* topk_idx, const ep_layout_t& L,
+                               const int32_t* extra_flags, int32_t num_extra,
+                               hipStream_t stream);
 
 hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout_t& L,
                                         const void* x, int32_t hidden, int32_t dtype,

@@ -385,6 +385,10 @@ hipError_t launch_layout_ids(const int64_t* topk_idx, const ep_layout_t& L, void
   a.num_tokens_per_group = L.num_tokens_per_group;
   a.error_flags = L.error_flags;
 
+  // Batches the fused decode kernel takes: its layout-only form, one workgroup
+  // per token.
+  if (chunks == 1 && fused_layout_dispatch_fits(L))
+    return launch_layout_small(topk_idx, L, a.chunk_flags + chunks, extra_flags, stream);
   if (chunks == 1) {
     hipLaunchKernelGGL(layout_single_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, a);
     return hipGetLastError();
