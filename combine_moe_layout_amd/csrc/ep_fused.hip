@@ -101,7 +101,7 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
 
   // A token's workgroup loads its slice of the token first (when one pass of
   // the lanes covers the row), so that this latency overlaps the table load
-  // and the table scan below.
+  // and the histograms below.
   const bool token_block = blockIdx.x < a.num_tokens;
   const int32_t vecs = kFp8 ? a.hidden / 16 : a.hidden / 8;
   const bool one_pass = vecs <= (int32_t)blockDim.x;
@@ -117,8 +117,8 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
   }
 
   // The table in at most kTableTrips loads per lane, all issued before the
-  // first is used: a loop that stores each entry to LDS before loading the
-  // next would wait one memory latency per trip.
+  // first is used: a loop that handled each entry before loading the next
+  // would wait one memory latency per trip.
   int64_t tv[kTableTrips];
 #pragma unroll
   for (int i = 0; i < kTableTrips; ++i) {
