@@ -91,6 +91,12 @@ def _edge_cases():
     idx[20, 2] = E + 3                           # out of range: flag, skipped
     idx[30, 0] = -9                              # negative and not -1: flag
     cases.append(("masks+dups+bad", idx, E, G))
+    # the same in one layout chunk (the one-launch layout, whose metadata
+    # workgroup ORs in the table kernel's flag entries)
+    small = idx[:100].copy()
+    cases.append(("one chunk: masks+dups+bad", small, E, G))
+    ok_small = np.where((small >= -1) & (small < E), small, -1)
+    cases.append(("one chunk: masks+dups", ok_small, E, G))
     idx2 = np.full((50, 4), -1, np.int64)        # nothing routed at all
     cases.append(("all unrouted", idx2, 32, 4))
     idx3 = np.zeros((0, 8), np.int64)

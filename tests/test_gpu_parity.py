@@ -152,6 +152,14 @@ def _edge_layouts():
         # more chunks than workgroups resident at once: the two-launch path
         ("1.1M pairs, 547 chunks", g.integers(0, 64, (140000, 8)), 64, 8, 0),
         ("1.1M pairs padded", g.integers(-1, 64, (140000, 8)), 64, 8, 20000),
+        # one layout chunk, top-k <= 8: one workgroup per token
+        ("one chunk: masked and bad ids", g.integers(-3, 40, (200, 6)), 32, 4, 0),
+        ("one chunk: padded overflow cap=3", g.integers(-1, 16, (300, 4)), 16, 4, 3),
+        ("one chunk: 2048 pairs exactly", g.integers(0, 256, (256, 8)), 256, 8, 0),
+        ("one chunk: E=1024", g.integers(0, 1024, (100, 8)), 1024, 8, 0),
+        ("one chunk: all to one expert, padded", np.full((200, 8), 7, np.int64), 16, 2, 100),
+        # one layout chunk with top-k 9: the single-workgroup layout
+        ("one chunk: k=9", g.integers(0, 64, (200, 9)), 64, 8, 0),
     ]
     return cases
 
