@@ -20,6 +20,7 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("name,T,H,fused", [("lowlat", None, None, True),
+                                             ("lowlat", None, None, False),   # one-chunk layout
                                              ("dsv3", 1024, 1024, False)])
 def test_graph_replays_match_eager(name, T, H, fused):
     print("[gpu-graph] %s T=%s H=%s fused=%s" % (name, T, H, fused), flush=True)
@@ -83,7 +84,8 @@ def test_graph_replays_match_eager(name, T, H, fused):
             assert np.array_equal(a, b), "replay %d differs from the eager result" % r
 
 
-@pytest.mark.parametrize("name,T,H", [("dsv3", 1024, 1024), ("skewed", 600, 512)])
+@pytest.mark.parametrize("name,T,H", [("dsv3", 1024, 1024), ("skewed", 600, 512),
+                                       ("dsv3", 200, 1024)])   # one-chunk group layout
 def test_graph_replays_match_eager_dedup_mxfp8(name, T, H):
     """The per-group dedup path with MXFP8 dispatch: group layout with the
     receiving side's metadata, dispatch to the groups, the MXFP8 stand-in
