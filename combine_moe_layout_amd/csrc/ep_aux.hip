@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256) void dequant_mxfp8_kernel(const u32x4* __restr
        u += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = u / units_per_row;
     const int32_t c16 = (int32_t)(u % units_per_row);
-    const int32_t e = (int32_t)scales[r * blocks_per_row + c16 / 2] - 127;
+    const uint32_t byte = scales[r * blocks_per_row + c16 / 2];
+    const int32_t e = (int32_t)byte - 127;
     const u32x4 codes = q[u];
     const uint32_t words[4] = {codes.x, codes.y, codes.z, codes.w};
     uint32_t outw[8];
@@ -110,7 +111,8 @@ __global__ __launch_bounds__(256) void dequant_mxfp8_kernel(const u32x4* __restr
       const int sh = (i % 2) * 16;
       const float a = ldexpf(e4m3_decode((word >> sh) & 0xFFu), e);
       const float b = ldexpf(e4m3_decode((word >> (sh + 8)) & 0xFFu), e);
-      outw[i] = bf16_rne(a) | (bf16_rne(b) << 16);
+      // E8M0 byte 255 is NaN: the whole block becomes the quiet NaN 0x7FC0
+      outw[i] = byte == 255u ? 0x7FC07FC0u : (bf16_rne(a) | (bf16_rne(b) << 16));
     }
     y[2 * u] = u32x4{outw[0], outw[1], outw[2], outw[3]};
     y[2 * u + 1] = u32x4{outw[4], outw[5], outw[6], outw[7]};

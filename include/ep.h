@@ -352,9 +352,10 @@ int ep_dequant_fp8(const uint8_t* q, const float* scales, int64_t rows, int32_t 
 
 /* Identity-expert stand-in for MXFP8 receive buffers (not part of the path):
  * y[r, c] = the bf16 nearest (ties to even) to decode(q[r, c]) *
- * 2^(scales[r, c/32] - 127), an exact product rounded once.  q uint8
- * [rows, hidden], scales uint8 [rows, hidden/32], y bf16 [rows, hidden];
- * hidden % 128 == 0. */
+ * 2^(scales[r, c/32] - 127), an exact product rounded once; a scale byte of
+ * 255 (NaN in E8M0; dispatch never writes it) makes its 32 outputs the quiet
+ * NaN 0x7FC0.  q uint8 [rows, hidden], scales uint8 [rows, hidden/32], y bf16
+ * [rows, hidden]; hidden % 128 == 0. */
 int ep_dequant_mxfp8(const uint8_t* q, const uint8_t* scales, int64_t rows, int32_t hidden,
                      void* y, void* stream);
 

@@ -638,13 +638,17 @@ EXPORT void ep_oracle_dispatch_mxfp8(const uint16_t* x, int64_t T, int32_t k, in
 }
 
 /* Identity expert stand-in for MXFP8 rows (harness only): the bf16 nearest to
- * decode(q) * 2^(byte - 127), rounded once from the exact product. */
+ * decode(q) * 2^(byte - 127), rounded once from the exact product; scale byte
+ * 255 (which dispatch never writes) is NaN in E8M0 and gives the quiet NaN
+ * 0x7FC0 for its whole block. */
 EXPORT void ep_oracle_dequant_mxfp8(const uint8_t* q, const uint8_t* scales, int64_t R, int32_t H,
                                     uint16_t* y) {
     int32_t nb = H / 32;
     for (int64_t r = 0; r < R; ++r)
         for (int32_t c = 0; c < H; ++c) {
-            double x = ldexp(1.0, (int)scales[r * nb + c / 32] - 127);   /* E8M0: 2^(byte-127) */
+            uint8_t b = scales[r * nb + c / 32];
+            if (b == 255) { y[r * H + c] = 0x7FC0u; continue; }
+            double x = ldexp(1.0, (int)b - 127);                         /* E8M0: 2^(byte-127) */
             y[r * H + c] = ep_oracle_bf16_from_double(ep_oracle_e4m3_decode(q[r * H + c]) * x);
         }
 }

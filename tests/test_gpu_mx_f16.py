@@ -129,11 +129,18 @@ def test_layout_dispatch_fused_mxfp8(T, H):
 
 
 def test_dequant_mxfp8_matches_oracle():
+    """Dispatch's own rows, plus rows at the ends of the E8M0 range (bytes 0,
+    1, 254 and 255, the NaN byte that makes its block 0x7FC0)."""
     H = 1024
     x = _mx_special_rows(H)
     qs = [oracle.quantize_token_mxfp8(r) for r in x]
     q = np.stack([a for a, _ in qs])
     s = np.stack([b for _, b in qs])
+    g = np.random.default_rng(9)
+    q_ext = g.integers(0, 256, (4, H)).astype(np.uint8)
+    q_ext[(q_ext & 0x7F) == 0x7F] = 0x38
+    s_ext = np.resize(np.array([0, 1, 254, 255, 127], np.uint8), (4, H // 32)).astype(np.uint8)
+    q, s = np.concatenate([q, q_ext]), np.concatenate([s, s_ext])
     y = torch.empty((q.shape[0], H), dtype=torch.bfloat16, device="cuda")
     B.ep_dequant_mxfp8(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(), y)
     torch.cuda.synchronize()

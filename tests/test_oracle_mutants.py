@@ -92,7 +92,7 @@ MUTANTS = [
      "if (se > 127)"),
     ("MX amax of signed values", "double m = fabs(ep_oracle_bf16_to_double(x_row[c]));",
      "double m = ep_oracle_bf16_to_double(x_row[c]);"),
-    ("MX dequant scale bias off by one", "(int)scales[r * nb + c / 32] - 127", "(int)scales[r * nb + c / 32] - 128"),
+    ("MX dequant scale bias off by one", "double x = ldexp(1.0, (int)b - 127);", "double x = ldexp(1.0, (int)b - 128);"),
     ("fp16 ties away from zero", "double r = nearbyint(a / quantum) * quantum;",
      "double r = floor(a / quantum + 0.5) * quantum;"),
     ("fp16 overflows at the largest finite value", "if (r > 65504.0)", "if (r >= 65504.0)"),
@@ -105,6 +105,9 @@ MUTANTS = [
      "memcpy(is_token_in_group, in_group, (size_t)T);"),
     ("MX combine scale bias off by one", "return b == 255 ? NAN : ldexp(1.0, (int)b - 127);",
      "return b == 255 ? NAN : ldexp(1.0, (int)b - 128);"),
+    ("MX combine decodes scale byte 0 as zero", "return b == 255 ? NAN : ldexp(1.0, (int)b - 127);",
+     "return b == 255 ? NAN : (b == 0 ? 0.0 : ldexp(1.0, (int)b - 127));"),
+    ("MX dequant decodes the NaN byte as 2^128", "if (b == 255) { y[r * H + c] = 0x7FC0u; continue; }", ""),
     ("MX combine reads the 128-channel block's scale", "e8m0_value(scales[(int64_t)s * nb + c / 32]);",
      "e8m0_value(scales[(int64_t)s * nb + c / 128]);"),
     ("MN-major layout indexed row-major", "memcpy(dst + ((int64_t)c * rows + r) * entry_bytes,",
@@ -161,7 +164,8 @@ def _battery():
                pins_mx.test_combine_f16_one_hot_is_a_gather_and_round_trip_is_exact,
                pins_mx.test_combine_f16_is_the_rounded_exact_sum,
                pins_mx.test_combine_mxfp8_golden, pins_mx.test_combine_mxfp8_one_hot_is_the_dequantisation,
-               pins_mx.test_combine_mxfp8_vs_float64_sum]
+               pins_mx.test_combine_mxfp8_vs_float64_sum, pins_mx.test_combine_mxfp8_extreme_scale_bytes,
+               pins_mx.test_combine_mxfp8_nan_scale_and_codes, pins_mx.test_dequant_mxfp8_extreme_scale_bytes]
     checks += [lambda: pins_mn.test_scales_mn_major_matches_index_loops(3, 5),
                lambda: pins_mn.test_scales_mn_major_matches_index_loops(17, 56),
                lambda: pins_mn.test_mn_major_columns_are_the_tokens_scales(False)]

@@ -240,6 +240,27 @@ def _mx_operands(g, R, H, lo=100, hi=155):
     return q, sc
 
 
+def test_dequant_mxfp8_extreme_scale_bytes():
+    """The stand-in at the ends of the E8M0 range: bytes 0 and 1 (bf16
+    subnormal products), 254 (overflow to infinity for codes of magnitude >= 2)
+    and 255, NaN in E8M0, which turns its whole block into 0x7FC0 while the
+    other blocks keep their values.  Reference: torch's float8_e4m3fn and
+    float8_e8m0fnu decodes; every product here is exact in fp32."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) >= 0x38 and (c & 0x7F) != 0x7F], np.uint8)
+    bytes_ = np.array([0, 1, 127, 254, 255], np.uint8)
+    R, H = 2, 32 * bytes_.size
+    q = np.resize(codes, (R, H)).astype(np.uint8)
+    sc = np.tile(bytes_, (R, 1))
+    y = oracle.dequant_mxfp8(q, sc)
+    nan_block = np.repeat(sc == 255, 32, axis=1)
+    assert (y[nan_block] == 0x7FC0).all()
+    with np.errstate(over="ignore", invalid="ignore"):
+        prod = _e4m3_values(q) * np.repeat(_e8m0_values(sc), 32, axis=1)
+        prod = np.where(np.abs(prod) > 3.3895313892515355e38, np.copysign(np.inf, prod), prod)
+        ref = (prod.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert (y[~nan_block] == ref[~nan_block]).all()
+
+
 def test_combine_mxfp8_one_hot_is_the_dequantisation():
     g = np.random.default_rng(12)
     R, H, k = 40, 256, 4
@@ -269,6 +290,29 @@ def test_combine_mxfp8_vs_float64_sum():
         ref[m] += w[m, j:j + 1].astype(np.float64) * vals[slot[m, j]]
     ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
     assert (np.abs(out - ref) <= 0.5 * ulp * (1 + 1e-9)).all()
+
+
+def test_combine_mxfp8_extreme_scale_bytes():
+    """One-hot weights over every E4M3 code of magnitude >= 1 and scale bytes
+    from 0 (2^-127, whose products are bf16 subnormals) to 254 (2^127, whose
+    products of magnitude >= 2 overflow to infinity): each output is the single
+    product, exactly representable or infinite, compared with torch's
+    float8_e4m3fn and float8_e8m0fnu decodes."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) >= 0x38 and (c & 0x7F) != 0x7F], np.uint8)
+    bytes_ = np.array([0, 1, 2, 100, 127, 200, 253, 254], np.uint8)
+    R, H = bytes_.size, 32 * ((codes.size + 31) // 32)
+    q = np.resize(codes, (R, H)).astype(np.uint8)
+    sc = np.repeat(bytes_[:, None], H // 32, 1)
+    slot = np.arange(R, dtype=np.int32).reshape(R, 1)
+    out = oracle.combine_mxfp8(q, sc, np.ones((R, 1), np.float32), slot)
+    exact = _e4m3_values(q) * np.repeat(_e8m0_values(sc), 32, 1)
+    with np.errstate(over="ignore"):
+        want = np.where(np.abs(exact) > 3.3895313892515355e38, np.copysign(np.inf, exact), exact)
+        want_bits = (want.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    finite = np.isfinite(want)
+    assert (want.astype(np.float32)[finite].astype(np.float64) == want[finite]).all()
+    assert (out == want_bits).all(), [(r, c, hex(out[r, c]), hex(want_bits[r, c]))
+                                       for r, c in np.argwhere(out != want_bits)[:4]]
 
 
 def test_combine_mxfp8_nan_scale_and_codes():
