@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 # (tokens, hidden, top-k): workgroups per token = min(8, 256 // T, hidden / 512)
 CASES = [(1, 7168, 8), (2, 1024, 8), (5, 16512, 8), (31, 7168, 8), (32, 1664, 8), (33, 7168, 6),
          (64, 2048, 8), (100, 7168, 8), (128, 7168, 8), (129, 7168, 8), (16, 65536, 8),
-         (3, 65536, 9), (256, 7168, 8), (7, 1152, 3)]
+         (3, 65536, 9), (256, 7168, 8), (7, 1152, 3),
+         (64, 4096, 1), (100, 2048, 2), (200, 7168, 4), (40, 640, 5)]
 
 NAN_BF16, NAN_F16 = 0x7FC0, 0x7E00
 
