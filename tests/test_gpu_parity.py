@@ -422,6 +422,11 @@ def _fused_cases():
                   8, 2, 3, True))
     cases.append(("rows longer than a workgroup", g.integers(0, 64, (16, 8)).astype(np.int64),
                   W.draw_x(16, 16512), 64, 8, 0, True))
+    # top-k above 8 in one layout chunk: the two calls' kernels instead
+    cases.append(("top-k 9, one chunk", g.integers(-1, 32, (50, 9)).astype(np.int64),
+                  W.draw_x(50, 256), 32, 4, 0, True))
+    cases.append(("top-k 12 padded, one chunk", g.integers(0, 16, (40, 12)).astype(np.int64),
+                  W.draw_x(40, 512), 16, 4, 20, True))
     return cases
 
 
