@@ -33,6 +33,7 @@
 //      [t, g], 1 when g is one of the token's entries in the table.
 #include "ep_device.h"
 #include "ep_internal.h"
+#include "ep_scan.h"
 
 namespace ep {
 
@@ -139,6 +140,171 @@ __global__ __launch_bounds__(kGroupThreads) void group_member_kernel(
   }
 }
 
+// Decode-sized batches (at most kFusedMaxPairs pairs, top-k at most
+// kFusedMaxTopk): the whole group layout in one launch, one workgroup per token
+// plus a metadata workgroup, the way the fused decode kernel computes the
+// expert layout.  Every workgroup reads the whole top-k table and marks, for
+// each pair, whether its group is the first occurrence in its token; the LDS
+// histogram of those marks over all tokens gives the groups' totals (scanned
+// into offsets), and over the tokens before this one the token's row inside
+// each of its groups.  The token's workgroup then writes its entries (groups
+// ascending, then -1), the receiving side's masked ids and weights for its
+// rows, and its is_token_in_group row; the metadata workgroup writes the
+// counts, offsets and flags.  Same results as the table, layout and metadata
+// kernels.
+constexpr int kGroupSmallLanes = 256;
+constexpr int kGroupSmallTrips = kFusedMaxPairs / kGroupSmallLanes;
+
+struct GroupSmallArgs {
+  const int64_t* topk_idx;
+  const float* topk_weights;
+  int32_t T, k, E, per_group, G, kg;
+  int32_t* slot_idx;
+  int32_t* recv_src;
+  int32_t* num_tokens_per_expert;
+  int32_t* expert_offsets;
+  int32_t* num_tokens_per_group;
+  int32_t* error_flags;
+  int64_t* recv_idx;
+  float* recv_w;
+  uint8_t* member;
+};
+
+__global__ __launch_bounds__(kGroupSmallLanes) void group_layout_small_kernel(GroupSmallArgs a) {
+  __shared__ int32_t s_g[kFusedMaxPairs];  // group of every pair, -1 if none
+  __shared__ int32_t s_hist[EP_MAX_EXPERTS];
+  __shared__ int32_t s_pre[EP_MAX_EXPERTS];
+  __shared__ int32_t s_off[EP_MAX_EXPERTS];
+  __shared__ int32_t s_wave[kGroupSmallLanes / kWave];
+  __shared__ int32_t s_ent[kFusedMaxTopk];   // this token's entries: groups ascending, then -1
+  __shared__ int32_t s_row[kFusedMaxTopk];   // their receive rows
+  const int tid = threadIdx.x;
+  const int32_t k = a.k, G = a.G, kg = a.kg;
+  const int32_t P = a.T * k;
+  const bool token_block = (int32_t)blockIdx.x < a.T;
+  const int32_t t = blockIdx.x;
+  const int32_t p0 = token_block ? t * k : 0;
+
+  int64_t tv[kGroupSmallTrips];
+#pragma unroll
+  for (int i = 0; i < kGroupSmallTrips; ++i) {
+    const int32_t p = tid + i * kGroupSmallLanes;
+    tv[i] = p < P ? a.topk_idx[p] : -1;
+  }
+  for (int g = tid; g < G; g += kGroupSmallLanes) {
+    s_hist[g] = 0;
+    s_pre[g] = 0;
+  }
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < kGroupSmallTrips; ++i) {
+    const int32_t p = tid + i * kGroupSmallLanes;
+    if (p < P) {
+      const bool ok = tv[i] >= 0 && tv[i] < a.E;
+      bad |= !ok && tv[i] != -1;
+      s_g[p] = ok ? (int32_t)(tv[i] / a.per_group) : -1;
+    }
+  }
+  __syncthreads();
+
+  // a pair counts once for its group if no earlier pair of its token names it
+  // (a fixed trip count over the at most kFusedMaxTopk - 1 earlier pairs, so
+  // their LDS reads are all in flight together)
+#pragma unroll
+  for (int i = 0; i < kGroupSmallTrips; ++i) {
+    const int32_t p = tid + i * kGroupSmallLanes;
+    if (p < P) {
+      const int32_t g = s_g[p];
+      const int32_t j = p % k;
+      bool first = g >= 0;
+#pragma unroll
+      for (int d = 1; d < kFusedMaxTopk; ++d)
+        if (d <= j) first = first && s_g[p - d] != g;
+      if (first) {
+        atomicAdd(&s_hist[g], 1);
+        if (p < p0) atomicAdd(&s_pre[g], 1);
+      }
+    }
+  }
+  __syncthreads();
+  const int32_t total = block_exclusive_scan(s_hist, s_off, G, s_wave);
+
+  if (!token_block) {
+    for (int g = tid; g < G; g += kGroupSmallLanes) {
+      a.num_tokens_per_expert[g] = s_hist[g];
+      a.expert_offsets[g] = s_off[g];
+      a.num_tokens_per_group[g] = s_hist[g];  // the group layout's groups are its experts
+    }
+    if (tid == 0) a.expert_offsets[G] = total;
+    const int any_bad = __syncthreads_or(bad ? 1 : 0);
+    if (tid == 0) a.error_flags[0] = any_bad ? EP_FLAG_BAD_EXPERT : 0;
+    return;
+  }
+
+  // this token's entries: pair j's group, if first in the token, goes to entry
+  // (number of the token's distinct groups below it); the rest are -1
+  if (tid < k) {
+    const int32_t j = tid;
+    // the token's groups in registers (fixed trip counts, all reads in flight)
+    int32_t gt[kFusedMaxTopk];
+    bool fq[kFusedMaxTopk];
+#pragma unroll
+    for (int q = 0; q < kFusedMaxTopk; ++q) gt[q] = q < k ? s_g[p0 + q] : -1;
+    int32_t g = -1, rank = 0, ndist = 0;
+    bool first = false;
+#pragma unroll
+    for (int q = 0; q < kFusedMaxTopk; ++q) {
+      fq[q] = gt[q] >= 0;
+#pragma unroll
+      for (int r = 0; r < q; ++r) fq[q] = fq[q] && gt[r] != gt[q];
+      g = q == j ? gt[q] : g;
+      first = q == j ? fq[q] : first;
+    }
+#pragma unroll
+    for (int q = 0; q < kFusedMaxTopk; ++q) {
+      ndist += fq[q] ? 1 : 0;
+      rank += (fq[q] && gt[q] < g) ? 1 : 0;
+    }
+    if (first) {
+      const int32_t row = s_off[g] + s_pre[g];
+      s_ent[rank] = g;
+      s_row[rank] = row;
+      a.slot_idx[t * kg + rank] = row;
+      if (a.recv_src != nullptr) a.recv_src[row] = t * kg + rank;
+    }
+    if (j >= ndist && j < kg) {
+      s_ent[j] = -1;
+      s_row[j] = -1;
+      a.slot_idx[t * kg + j] = -1;
+    }
+  }
+  __syncthreads();
+
+  // the receiving side's metadata: column j of each of the token's rows
+  if (a.recv_idx != nullptr || a.recv_w != nullptr) {
+    for (int32_t l = tid; l < kg * k; l += kGroupSmallLanes) {
+      const int32_t i = l / k, j = l - i * k;
+      const int32_t row = s_row[i];
+      if (row < 0) continue;
+      const int32_t g = s_g[p0 + j];
+      const bool mine = g >= 0 && g == s_ent[i];
+      if (a.recv_idx != nullptr) a.recv_idx[(int64_t)row * k + j] = mine ? a.topk_idx[p0 + j] : -1;
+      if (a.recv_w != nullptr) a.recv_w[(int64_t)row * k + j] = mine ? a.topk_weights[p0 + j] : 0.0f;
+    }
+  }
+  if (a.member != nullptr) {
+    int32_t ent[kFusedMaxTopk];
+#pragma unroll
+    for (int i = 0; i < kFusedMaxTopk; ++i) ent[i] = i < kg ? s_ent[i] : -1;
+    for (int32_t g = tid; g < G; g += kGroupSmallLanes) {
+      uint8_t hit = 0;
+#pragma unroll
+      for (int i = 0; i < kFusedMaxTopk; ++i) hit |= ent[i] == g ? 1 : 0;
+      a.member[(int64_t)t * G + g] = hit;
+    }
+  }
+}
+
 hipError_t launch_group_layout(const int64_t* topk_idx, const float* topk_weights, int32_t k,
                                int32_t E, const ep_layout_t& GL, int64_t* recv_idx,
                                float* recv_w, uint8_t* member, void* workspace,
@@ -146,6 +312,29 @@ hipError_t launch_group_layout(const int64_t* topk_idx, const float* topk_weight
   const int64_t T = GL.num_tokens;
   const int32_t G = GL.num_experts;
   const int32_t kg = GL.num_topk;
+  if (T > 0 && T * k <= kFusedMaxPairs && k <= kFusedMaxTopk) {
+    GroupSmallArgs a;
+    a.topk_idx = topk_idx;
+    a.topk_weights = topk_weights;
+    a.T = (int32_t)T;
+    a.k = k;
+    a.E = E;
+    a.per_group = E / G;
+    a.G = G;
+    a.kg = kg;
+    a.slot_idx = GL.slot_idx;
+    a.recv_src = GL.recv_src;
+    a.num_tokens_per_expert = GL.num_tokens_per_expert;
+    a.expert_offsets = GL.expert_offsets;
+    a.num_tokens_per_group = GL.num_tokens_per_group;
+    a.error_flags = GL.error_flags;
+    a.recv_idx = recv_idx;
+    a.recv_w = recv_w;
+    a.member = member;
+    hipLaunchKernelGGL(group_layout_small_kernel, dim3((unsigned)(T + 1)), dim3(kGroupSmallLanes),
+                       0, stream, a);
+    return hipGetLastError();
+  }
   const GroupSeg sg = group_seg(k);
   const int64_t blocks = group_table_blocks(T, k);
   int64_t* table = static_cast<int64_t*>(workspace);
