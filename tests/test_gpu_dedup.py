@@ -117,6 +117,20 @@ def test_group_layout_without_metadata_or_weights():
     compare_group_layout(wl.topk_idx, wl.topk_weights, wl.E, wl.G, "no metadata", meta=False)
 
 
+def test_decode_group_layout_without_metadata_or_weights():
+    """The one-launch form (at most 2048 pairs) with each optional output left
+    out in turn, and with none of them: the slots and counts still match."""
+    wl = W.make("dsv3", T=200)
+    compare_group_layout(wl.topk_idx, None, wl.E, wl.G, "decode, no weights", meta=True)
+    compare_group_layout(wl.topk_idx, wl.topk_weights, wl.E, wl.G, "decode, no metadata", meta=False)
+    o = oracle.group_layout(wl.topk_idx, None, wl.E, wl.G)
+    gl = B.EpGroupLayout(wl.T, wl.k, wl.E, wl.G)
+    B.ep_get_group_layout(torch.from_numpy(wl.topk_idx).cuda(), None, gl)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gl.slot_idx.cpu().numpy(), o["group_slot"])
+    np.testing.assert_array_equal(gl.num_tokens_per_expert.cpu().numpy(), o["num_tokens_per_group"])
+
+
 def test_group_layout_is_deterministic_and_repeatable():
     wl = W.make("skewed")
     a, _, _ = gpu_group_layout(wl.topk_idx, wl.topk_weights, wl.E, wl.G)
