@@ -170,7 +170,7 @@ static CombineMap combine_map(int32_t vecs_per_row) {
   return m;
 }
 
-// Decode-sized batches (one token per workgroup, at most kFusedMaxPairs pairs)
+// Decode-sized batches (one token per workgroup, at most kDecodeCombinePairs pairs)
 // leave most of the chip idle: each token is spread over up to 8 workgroups,
 // each taking at least one wave of vectors, so that about one workgroup runs
 // per CU and all CUs share the row traffic.  Measured at hidden 7168, top-8,
@@ -194,13 +194,13 @@ static void split_tokens(int32_t vecs, int64_t T, CombineMap& m, dim3& grid, dim
 // per workgroup): slots and weights then arrive as per-lane vector loads,
 // about 3% faster there than the scalar loads of the uniform-token form (179
 // vs 185 us at 8192 tokens x 7168, top-8).  Decode-sized batches (at most
-// kFusedMaxPairs pairs, one token per workgroup) are latency-bound, and there
+// kDecodeCombinePairs pairs, one token per workgroup) are latency-bound, and there
 // the scalar loads win (6.7 vs 7.2 us per call at 128 tokens, top-8).
 template <int K, bool kUnit, bool kF16>
 static void launch_k(dim3 grid, dim3 block, hipStream_t stream, const void* y, const float* w,
                      const ep_layout_t& L, int32_t hidden, CombineMap m, void* out) {
   const bool whole = m.tokens_per_block == 1 &&
-                     L.num_tokens * (int64_t)L.num_topk <= (int64_t)kFusedMaxPairs;
+                     L.num_tokens * (int64_t)L.num_topk <= (int64_t)kDecodeCombinePairs;
   if (whole) {
     split_tokens(hidden / 8, L.num_tokens, m, grid, block);
     hipLaunchKernelGGL((combine_kernel<K, kUnit, kF16, true>), grid, block, 0, stream,
@@ -359,7 +359,8 @@ template <int K, bool kMx>
 static void launch_fp8_k(dim3 grid, dim3 block, hipStream_t stream, const uint8_t* q,
                          const void* scales, const float* w, const ep_layout_t& L,
                          int32_t hidden, CombineMap m, void* out) {
-  if (m.tokens_per_block == 1 && L.num_tokens * (int64_t)L.num_topk <= (int64_t)kFusedMaxPairs)
+  if (m.tokens_per_block == 1 &&
+      L.num_tokens * (int64_t)L.num_topk <= (int64_t)kDecodeCombinePairs)
     split_tokens(hidden / 8, L.num_tokens, m, grid, block);
   if (m.tokens_per_block == 1)
     hipLaunchKernelGGL((combine_fp8_kernel<K, true, kMx>), grid, block, 0, stream, q, scales, w,

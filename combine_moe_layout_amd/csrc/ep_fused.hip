@@ -47,7 +47,7 @@ struct FusedArgs {
 
 // Workgroups have at least kFusedMinLanes lanes, so a lane loads at most
 // kTableTrips entries of the top-k table.
-constexpr int kFusedMinLanes = 256;
+constexpr int kFusedMinLanes = 512;
 constexpr int kTableTrips = kFusedMaxPairs / kFusedMinLanes;
 
 // kDispatch = false: the layout alone (ep_get_layout for batches of one
@@ -225,7 +225,7 @@ hipError_t launch_layout_dispatch_small(const int64_t* topk_idx, const ep_layout
   a.num_tokens_per_group = L.num_tokens_per_group;
   a.error_flags = L.error_flags;
   // one token per workgroup: one lane per 16-byte output vector, whole waves,
-  // at least 256 lanes for the table scan, at most 1024 (longer rows loop)
+  // at least kFusedMinLanes lanes for the table, at most 1024 (longer rows loop)
   const int32_t vecs = fp8 ? hidden / 16 : hidden / 8;
   int32_t lanes = ((vecs + 63) / 64) * 64;
   lanes = lanes < kFusedMinLanes ? kFusedMinLanes : (lanes > 1024 ? 1024 : lanes);

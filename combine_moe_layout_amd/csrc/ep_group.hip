@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_member_kernel(
 // rows, and its is_token_in_group row; the metadata workgroup writes the
 // counts, offsets and flags.  Same results as the table, layout and metadata
 // kernels.
-constexpr int kGroupSmallLanes = 256;
+constexpr int kGroupSmallLanes = 512;
 constexpr int kGroupSmallTrips = kFusedMaxPairs / kGroupSmallLanes;
 
 struct GroupSmallArgs {
@@ -289,7 +289,8 @@ __global__ __launch_bounds__(kGroupSmallLanes) void group_layout_small_kernel(Gr
       const int32_t g = s_g[p0 + j];
       const bool mine = g >= 0 && g == s_ent[i];
       if (a.recv_idx != nullptr) a.recv_idx[(int64_t)row * k + j] = mine ? a.topk_idx[p0 + j] : -1;
-      if (a.recv_w != nullptr) a.recv_w[(int64_t)row * k + j] = mine ? a.topk_weights[p0 + j] : 0.0f;
+      if (a.recv_w != nullptr)
+        a.recv_w[(int64_t)row * k + j] = mine ? a.topk_weights[p0 + j] : 0.0f;
     }
   }
   if (a.member != nullptr) {

@@ -84,8 +84,12 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t str
 constexpr bool kDispatchUsesHwCast = true;
 
 // Batches of at most this many (token, k) pairs, with top-k at most
-// kFusedMaxTopk, take the one-launch layout+dispatch path.
-constexpr int kFusedMaxPairs = kChunkPairs;
+// kFusedMaxTopk, take the one-launch layout (+ dispatch) kernels.
+constexpr int kFusedMaxPairs = 2 * kChunkPairs;
+// Combines of at most this many pairs are decode-sized: one token per
+// workgroup, slots and weights through scalar loads, tokens split over
+// several workgroups when there are fewer tokens than CUs.
+constexpr int kDecodeCombinePairs = kChunkPairs;
 constexpr int kFusedMaxTopk = 8;
 // Compute units of the MI355X (gfx950) this library is built for.
 constexpr int kChipCUs = 256;

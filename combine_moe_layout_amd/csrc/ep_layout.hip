@@ -202,7 +202,8 @@ __device__ __forceinline__ void chunk_totals(int32_t E, int32_t num_chunks, int6
 template <bool kSingleChunk>
 __device__ __forceinline__ void finish_chunk(
     int64_t num_pairs, int32_t E, int32_t num_groups, int32_t capacity, int32_t num_chunks,
-    int64_t c, const int32_t* __restrict__ chunk_count, LayoutShared& sh, const int32_t (&eid)[kLayoutItems], const int32_t (&local)[kLayoutItems],
+    int64_t c, const int32_t* __restrict__ chunk_count, LayoutShared& sh,
+    const int32_t (&eid)[kLayoutItems], const int32_t (&local)[kLayoutItems],
     int32_t* __restrict__ slot_idx, int32_t* __restrict__ recv_src,
     int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ num_tokens_per_group, int32_t* __restrict__ error_flags,
@@ -387,7 +388,7 @@ hipError_t launch_layout_ids(const int64_t* topk_idx, const ep_layout_t& L, void
 
   // Batches the fused decode kernel takes: its layout-only form, one workgroup
   // per token.
-  if (chunks == 1 && fused_layout_dispatch_fits(L))
+  if (fused_layout_dispatch_fits(L))
     return launch_layout_small(topk_idx, L, a.chunk_flags + chunks, extra_flags, stream);
   if (chunks == 1) {
     hipLaunchKernelGGL(layout_single_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, a);

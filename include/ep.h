@@ -208,7 +208,7 @@ int ep_scales_to_mn_major(const void* scales, int64_t rows, int32_t hidden, int3
 /*
  * Layout and dispatch in one call: the same results as ep_get_layout followed
  * by ep_dispatch with the same arguments.  For decode-sized batches -- at most
- * 2048 (token, k) pairs and top-k at most 8 -- both run in a single launch
+ * 4096 (token, k) pairs and top-k at most 8 -- both run in a single launch
  * (the pages' low-latency mode: "DeepEP是什麼？…" (yololab.net), section
  * "高吞吐與低延遲工作負載"); larger batches run the two calls' kernels in turn.
  * Arguments, layouts and status codes are those of ep_get_layout and

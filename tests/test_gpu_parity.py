@@ -413,7 +413,7 @@ def _fused_cases():
     wl = W.make("tiny")
     cases.append(("tiny (bf16)", wl.topk_idx, wl.x_bits, wl.E, wl.G, wl.cap, False))
     wl = W.make("dsv3", T=256)
-    cases.append(("2048 pairs, the largest fused batch", wl.topk_idx, wl.x_bits, wl.E, wl.G, 0, True))
+    cases.append(("2048 pairs", wl.topk_idx, wl.x_bits, wl.E, wl.G, 0, True))
     cases.append(("one token, one expert", np.array([[0]], np.int64), W.draw_x(1, 256), 1, 1, 0, True))
     idx = g.integers(-3, 24, (37, 3)).astype(np.int64)
     idx[5] = [4, 4, 4]  # the same expert three times in one token
@@ -427,6 +427,12 @@ def _fused_cases():
                   W.draw_x(50, 256), 32, 4, 0, True))
     cases.append(("top-k 12 padded, one chunk", g.integers(0, 16, (40, 12)).astype(np.int64),
                   W.draw_x(40, 512), 16, 4, 20, True))
+    # the largest one-launch batch (4096 pairs, two layout chunks), and one pair more
+    wl = W.make("dsv3", T=512, H=1024)
+    cases.append(("4096 pairs, the largest fused batch", wl.topk_idx, wl.x_bits, wl.E, wl.G, 0, True))
+    cases.append(("4096 pairs padded with drops", wl.topk_idx, wl.x_bits, wl.E, wl.G, 12, True))
+    cases.append(("4104 pairs, top-k 8: the two-call kernels", g.integers(-1, 64, (513, 8)).astype(np.int64),
+                  W.draw_x(513, 512), 64, 8, 0, True))
     return cases
 
 
