@@ -187,8 +187,8 @@ def main() -> int:
                     help="per-group dedup variant: ep_get_group_layout (with the receiving "
                          "side's metadata), dispatch to the groups, ep_combine_groups")
     args = ap.parse_args()
-    if args.dedup and (args.fused or args.fp8_combine or args.graph or args.f16):
-        print("--dedup times its own three calls; it combines with --pow2 and --mx only",
+    if args.dedup and (args.fused or args.fp8_combine or args.f16):
+        print("--dedup times its own three calls; it combines with --pow2, --mx and --graph only",
               file=sys.stderr)
         return 2
     if args.mn_convert and (args.mn_scales or args.fused or args.dedup or args.graph):

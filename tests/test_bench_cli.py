@@ -36,7 +36,7 @@ def test_more_than_one_gpu_exits_with_a_message(args, env):
 
 
 @pytest.mark.parametrize("flags", [["--mx", "--pow2"],
-                                   ["--dedup", "--fused"], ["--dedup", "--graph"], ["--mx", "--pow2", "--fp8-combine"],
+                                   ["--dedup", "--fused"], ["--dedup", "--f16"], ["--mx", "--pow2", "--fp8-combine"],
                                    ["--mn-scales", "--fp8-combine"], ["--mn-convert", "--mn-scales"],
                                    ["--mn-convert", "--dedup"], ["--graph", "--graph-steps", "3"],
                                    ["--graph", "--graph-steps", "0"]])
