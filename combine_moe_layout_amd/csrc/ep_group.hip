@@ -31,6 +31,8 @@
 //   3. group_meta_kernel: lane (t, j) writes column j of every row of token t.
 //   4. (optional) group_member_kernel: lane (t, g) writes is_token_in_group
 //      [t, g], 1 when g is one of the token's entries in the table.
+// Decode-sized batches take all four in one launch (group_layout_small_kernel
+// below).
 #include "ep_device.h"
 #include "ep_internal.h"
 #include "ep_scan.h"
