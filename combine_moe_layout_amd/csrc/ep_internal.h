@@ -88,8 +88,10 @@ constexpr bool kDispatchUsesHwCast = true;
 constexpr int kFusedMaxPairs = 2 * kChunkPairs;
 // Combines of at most this many pairs are decode-sized: one token per
 // workgroup, slots and weights through scalar loads, tokens split over
-// several workgroups when there are fewer tokens than CUs.
-constexpr int kDecodeCombinePairs = kChunkPairs;
+// several workgroups when there are fewer tokens than CUs.  (At 512 tokens,
+// top-8, the scalar-load form measured 11.5 against 11.9 us for the bf16
+// combine; at 8192 tokens the per-lane loads win.)
+constexpr int kDecodeCombinePairs = kFusedMaxPairs;
 constexpr int kFusedMaxTopk = 8;
 // Compute units of the MI355X (gfx950) this library is built for.
 constexpr int kChipCUs = 256;

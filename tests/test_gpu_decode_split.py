@@ -1,5 +1,5 @@
 """GPU parity of the decode-sized combines, where one token is spread over up to
-8 workgroups (batches of at most 2048 (token, k) pairs, one token per
+8 workgroups (batches of at most 4096 (token, k) pairs, one token per
 workgroup otherwise): bf16, fp16, FP8, MXFP8 and the unit-weight group
 combine, against the oracle.
 
@@ -25,7 +25,8 @@ pytestmark = pytest.mark.gpu
 CASES = [(1, 7168, 8), (2, 1024, 8), (5, 16512, 8), (31, 7168, 8), (32, 1664, 8), (33, 7168, 6),
          (64, 2048, 8), (100, 7168, 8), (128, 7168, 8), (129, 7168, 8), (16, 65536, 8),
          (3, 65536, 9), (256, 7168, 8), (7, 1152, 3),
-         (64, 4096, 1), (100, 2048, 2), (200, 7168, 4), (40, 640, 5)]
+         (64, 4096, 1), (100, 2048, 2), (200, 7168, 4), (40, 640, 5),
+         (384, 7168, 8), (512, 4096, 8)]   # whole-token form without a split, up to 4096 pairs
 
 NAN_BF16, NAN_F16 = 0x7FC0, 0x7E00
 
