@@ -156,10 +156,15 @@ __device__ __forceinline__ void chunk_totals(int32_t E, int32_t num_chunks, int6
         const int i = tid + b * kLayoutThreads;
         r[b] = src4[i < n4 ? i : n4 - 1];  // unconditional, so r stays in registers
       }
-      // unconditional as well: entries past the matrix land in the unused
-      // tail of the staging area and are never read
+      // Only whole quads of the matrix are stored here.  Quad n4 holds the
+      // last matrix % 4 entries, which the loop below fills from other
+      // lanes; a store of the clamped copy to that quad from another wave
+      // would race with it.
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) dst4[tid + b * kLayoutThreads] = r[b];
+      for (int b = 0; b < kBatch; ++b) {
+        const int i = tid + b * kLayoutThreads;
+        if (i < n4) dst4[i] = r[b];
+      }
     }
     for (int i = 4 * n4 + tid; i < matrix; i += kLayoutThreads) sh.counts[i] = chunk_count[i];
     __syncthreads();
