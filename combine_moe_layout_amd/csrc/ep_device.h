@@ -108,6 +108,8 @@ __device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, floa
   }
 }
 
+// Clamp to [-448, 448] (one v_med3_f32).  A NaN comes out as -448, so
+// callers that can meet NaN test for it themselves.
 __device__ __forceinline__ float clamp_fp8(float v) { return fminf(fmaxf(v, -kFp8Max), kFp8Max); }
 
 // E4M3 code -> fp32 (exact).  0x7F / 0xFF decode to NaN.

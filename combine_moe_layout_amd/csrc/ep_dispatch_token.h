@@ -75,6 +75,70 @@ __device__ __forceinline__ uint32_t mx_block_scale(float amax, float& inv) {
 // swizzles: 8 lanes per 128-channel block, 2 lanes per 32-channel MX block).
 // The block's scale word goes to word v / 8 of my_scales (MX: the block's
 // E8M0 byte to byte v / 2).
+// E4M3 codes of 16 values scaled by inv and clamped to +-448, four bytes per word.
+template <bool kHw>
+__device__ __forceinline__ void fp8_encode16(const float (&f)[16], float inv, u32x4& q) {
+  q.x = e4m3_encode4<kHw>(clamp_fp8(f[0] * inv), clamp_fp8(f[1] * inv), clamp_fp8(f[2] * inv),
+                          clamp_fp8(f[3] * inv));
+  q.y = e4m3_encode4<kHw>(clamp_fp8(f[4] * inv), clamp_fp8(f[5] * inv), clamp_fp8(f[6] * inv),
+                          clamp_fp8(f[7] * inv));
+  q.z = e4m3_encode4<kHw>(clamp_fp8(f[8] * inv), clamp_fp8(f[9] * inv),
+                          clamp_fp8(f[10] * inv), clamp_fp8(f[11] * inv));
+  q.w = e4m3_encode4<kHw>(clamp_fp8(f[12] * inv), clamp_fp8(f[13] * inv),
+                          clamp_fp8(f[14] * inv), clamp_fp8(f[15] * inv));
+}
+
+// Codes of a 128-channel block that holds a NaN or an infinity (fp32 scales):
+// the block maximum ignores NaN, as in the scale's definition, so a block with
+// an infinity gets scale = inf and inv = 0; finite values then encode as +-0
+// and every product that is NaN (a NaN input, or inf * 0) encodes as 0x7F.
+// Rare, so it is kept apart from the common path.
+template <bool kHw>
+__device__ __forceinline__ void fp8_nonfinite_block(const float (&f)[16], int32_t v, u32x4& q,
+                                                 uint32_t* my_scales) {
+  // Comparisons, not fmaxf: IEEE maxNum turns a signalling NaN (bf16 0x7F81,
+  // say) into a quiet NaN result instead of skipping it, while a comparison
+  // with any NaN is false, so NaN of either kind is skipped.
+  const auto larger = [](float a, float b) { return b > a ? b : a; };
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = larger(amax, fabsf(f[i]));
+  amax = larger(amax, __shfl_xor(amax, 1));
+  amax = larger(amax, __shfl_xor(amax, 2));
+  amax = larger(amax, __shfl_xor(amax, 4));
+  float scale, inv;
+  fp8_block_scale<false>(fmaxf(amax, kScaleFloor), scale, inv);
+  if ((v & 7) == 0) my_scales[v / 8] = __float_as_uint(scale);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float p[4];
+    uint32_t nan_bytes = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      p[b] = f[4 * i + b] * inv;
+      if (p[b] != p[b]) nan_bytes |= 0xFFu << (8 * b);
+    }
+    const uint32_t c = e4m3_encode4<kHw>(clamp_fp8(p[0]), clamp_fp8(p[1]), clamp_fp8(p[2]),
+                                         clamp_fp8(p[3]));
+    w[i] = (c & ~nan_bytes) | (0x7F7F7F7Fu & nan_bytes);
+  }
+  q = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// FP8 codes of one 16-channel slice (vector v of the code row: bf16 vectors
+// 2v and 2v+1 given in lo / hi), stored to every valid row; the lanes of one
+// scale block must call it together (their maximum is reduced with lane
+// swizzles: 8 lanes per 128-channel block, 2 lanes per 32-channel MX block).
+// The block's scale word goes to word v / 8 of my_scales (MX: the block's
+// E8M0 byte to byte v / 2).
+//
+// fp32 scales: the block maximum is taken with the NaN-propagating maximum
+// (v_maximum3_f32, as cheap as the ordinary one), so one comparison of the
+// finished maximum tells whether the block holds a NaN or an infinity; such
+// a block takes fp8_nonfinite_block.  In the common path every product lies
+// within +-448 * (1 + 2^-23) and the clamp only trims rounding.  (Non-finite
+// inputs are outside the power-of-two and MXFP8 formats' definitions.)
 template <bool kHw, int kMode = kScaleF32>
 __device__ __forceinline__ void fp8_vector_codes(const u32x4& lo, const u32x4& hi, int32_t v,
                                                  const int32_t* slots, int32_t k,
@@ -84,30 +148,40 @@ __device__ __forceinline__ void fp8_vector_codes(const u32x4& lo, const u32x4& h
                  bf16_lo(lo.z), bf16_hi(lo.z), bf16_lo(lo.w), bf16_hi(lo.w),
                  bf16_lo(hi.x), bf16_hi(hi.x), bf16_lo(hi.y), bf16_hi(hi.y),
                  bf16_lo(hi.z), bf16_hi(hi.z), bf16_lo(hi.w), bf16_hi(hi.w)};
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  float inv;
-  if constexpr (kMode == kScaleMx) {
-    const uint32_t byte = mx_block_scale(amax, inv);
-    if ((v & 1) == 0) reinterpret_cast<uint8_t*>(my_scales)[v / 2] = (uint8_t)byte;
-  } else {
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    amax = fmaxf(amax, __shfl_xor(amax, 4));
-    float scale;
-    fp8_block_scale<kMode == kScalePow2>(fmaxf(amax, kScaleFloor), scale, inv);
-    if ((v & 7) == 0) my_scales[v / 8] = __float_as_uint(scale);
-  }
   u32x4 q;
-  q.x = e4m3_encode4<kHw>(clamp_fp8(f[0] * inv), clamp_fp8(f[1] * inv), clamp_fp8(f[2] * inv),
-                          clamp_fp8(f[3] * inv));
-  q.y = e4m3_encode4<kHw>(clamp_fp8(f[4] * inv), clamp_fp8(f[5] * inv), clamp_fp8(f[6] * inv),
-                          clamp_fp8(f[7] * inv));
-  q.z = e4m3_encode4<kHw>(clamp_fp8(f[8] * inv), clamp_fp8(f[9] * inv),
-                          clamp_fp8(f[10] * inv), clamp_fp8(f[11] * inv));
-  q.w = e4m3_encode4<kHw>(clamp_fp8(f[12] * inv), clamp_fp8(f[13] * inv),
-                          clamp_fp8(f[14] * inv), clamp_fp8(f[15] * inv));
+  if constexpr (kMode == kScaleF32) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = __builtin_elementwise_maximum(amax, fabsf(f[i]));
+    amax = __builtin_elementwise_maximum(amax, __shfl_xor(amax, 1));
+    amax = __builtin_elementwise_maximum(amax, __shfl_xor(amax, 2));
+    amax = __builtin_elementwise_maximum(amax, __shfl_xor(amax, 4));
+    if (!(amax <= 3.40282347e38f)) {  // NaN or infinity somewhere in the block
+      fp8_nonfinite_block<kHw>(f, v, q, my_scales);
+    } else {
+      float scale, inv;
+      fp8_block_scale<false>(fmaxf(amax, kScaleFloor), scale, inv);
+      if ((v & 7) == 0) my_scales[v / 8] = __float_as_uint(scale);
+      fp8_encode16<kHw>(f, inv, q);
+    }
+  } else {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    float inv;
+    if constexpr (kMode == kScaleMx) {
+      const uint32_t byte = mx_block_scale(amax, inv);
+      if ((v & 1) == 0) reinterpret_cast<uint8_t*>(my_scales)[v / 2] = (uint8_t)byte;
+    } else {
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      amax = fmaxf(amax, __shfl_xor(amax, 4));
+      float scale;
+      fp8_block_scale<true>(fmaxf(amax, kScaleFloor), scale, inv);
+      if ((v & 7) == 0) my_scales[v / 8] = __float_as_uint(scale);
+    }
+    fp8_encode16<kHw>(f, inv, q);
+  }
   for (int32_t j = 0; j < k; ++j) {
     const int32_t s = slots[j];
     if (s >= 0) store_nt(recv + (int64_t)s * out_vec_per_row + v, q);

@@ -48,6 +48,10 @@
  *   R8  Quantised code: v = x * inv (one fp32 multiply), clamped to
  *       [-448, 448], rounded to the nearest E4M3 value, ties to even; the
  *       sign is kept, so a negative value that rounds to zero encodes 0x80.
+ *       Non-finite inputs (fp32-scale path): the block maximum skips NaN; a
+ *       v that is NaN encodes 0x7F whatever its sign; a block holding an
+ *       infinity has a = inf, so scale = inf, inv = +0, its finite values
+ *       encode +-0 and its infinities (inf * 0 = NaN) 0x7F.
  *   R9  Scales are laid out row-major [R, H/128], one scale row per receive row.
  *   R10 Combine: out[t] = bf16(sum_j w[t,j] * y[slot[t,j]]), skipping dropped
  *       or unrouted pairs; no renormalisation.  The oracle sums in fp64 (each

@@ -5,8 +5,8 @@ other's outputs.  The bar: layout, slots, bf16 dispatch, FP8 codes and scales
 and the identity-expert dequantisation are bit-exact; combine is within
 |gpu - ref| <= 8e-3 * max(|ref|, 1e-3) element-wise (the oracle sums in fp64,
 the kernel in fp32; both round once to bf16).  At the workloads' full sizes
-(the launch shapes the benchmark times) outputs are checked on sampled tokens
-the oracle computes one by one.
+(the launch shapes the benchmark times) every receive row and every output
+token is compared; the oracle's per-token calls run on several host threads.
 """
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -160,6 +160,14 @@ def _edge_layouts():
         ("one chunk: all to one expert, padded", np.full((200, 8), 7, np.int64), 16, 2, 100),
         # one layout chunk with top-k 9: the single-workgroup layout
         ("one chunk: k=9", g.integers(0, 64, (200, 9)), 64, 8, 0),
+        # two-launch path with a count matrix (chunks x E) that is not a
+        # multiple of 4 and whose last quad is staged by a different wave than
+        # the one that fills its tail entries
+        ("E=253, 3 chunks, matrix 759", g.integers(0, 253, (700, 8)), 253, 11, 0),
+        ("E=255, k=9, 3 chunks, matrix 765", g.integers(-1, 255, (600, 9)), 255, 5, 0),
+        ("E=1, 259 chunks, matrix 259", np.zeros((530000, 1), np.int64), 1, 1, 0),
+        ("E=7, 41 chunks, matrix 287", g.integers(0, 7, (10300, 8)), 7, 7, 0),
+        ("E=13 padded, 21 chunks, matrix 273", g.integers(-1, 13, (5300, 8)), 13, 13, 700),
     ]
     return cases
 
@@ -244,22 +252,32 @@ def test_dispatch_full_compare(case):
 
 
 @pytest.mark.parametrize("name", ["dsv3", "large", "skewed"])
-def test_dispatch_full_size_sampled(name):
+def test_dispatch_full_size_complete(name):
+    """Every receive row at the workload's full size (the benchmark's launch
+    shape): codes and scale bits (FP8) or row bits (bf16) against the oracle's
+    whole dispatch."""
     wl = W.make(name)
-    note("dispatch full size %s T=%d H=%d" % (name, wl.T, wl.H))
+    note("dispatch full size %s T=%d H=%d, every row" % (name, wl.T, wl.H))
     ol = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap)
     lay = gpu_layout(wl.topk_idx, wl.E, wl.G, wl.cap, with_src=False)
     q, s = _dispatch_gpu(wl, lay)
     g_slots = layout_to_host(lay)["slot_idx"]
     assert (g_slots == ol["slot_idx"]).all()
-    for t in sample_tokens(wl.T, 48):
-        rows = ol["slot_idx"][t]
-        if wl.fp8:
-            oq, os_ = oracle.quantize_token_fp8(wl.x_bits[t])
-            assert (q[rows] == oq).all(), "token %d codes" % t
-            assert (s[rows].view(np.uint32) == os_.view(np.uint32)).all(), "token %d scales" % t
-        else:
-            assert (q[rows] == wl.x_bits[t]).all(), "token %d rows" % t
+    R = ol["num_recv_rows"]
+    used = np.zeros(R, bool)
+    used[ol["slot_idx"][ol["slot_idx"] >= 0]] = True
+    if wl.fp8:
+        oq, os_ = oracle.dispatch_fp8(wl.x_bits, ol["slot_idx"], R)
+        bad = np.argwhere((q != oq).any(1) & used)
+        assert bad.size == 0, "%d rows' codes differ, first row %d" % (len(bad), bad[0][0])
+        bad = np.argwhere((s.view(np.uint32) != os_.view(np.uint32)).any(1) & used)
+        assert bad.size == 0, "%d rows' scales differ, first row %d" % (len(bad), bad[0][0])
+        note("%d rows of codes and scales identical" % used.sum())
+    else:
+        orecv = oracle.dispatch_bf16(wl.x_bits, ol["slot_idx"], R)
+        bad = np.argwhere((q != orecv).any(1) & used)
+        assert bad.size == 0, "%d rows differ, first row %d" % (len(bad), bad[0][0])
+        note("%d rows identical" % used.sum())
 
 
 def test_dequant_matches_oracle():
@@ -345,23 +363,35 @@ def test_combine_skips_dropped_and_unrouted_pairs():
     assert_close_bf16(got, oracle.combine(y, w, ol["slot_idx"]), "combine drops")
 
 
-def test_combine_full_size_sampled():
+def test_combine_full_size_complete():
+    """Every output token of the dsv3 combine (random expert outputs) against
+    the oracle's fp64 sum."""
     wl = W.make("dsv3")
-    note("combine full size dsv3 with random expert outputs")
+    note("combine full size dsv3 with random expert outputs, every token")
     y = W.random_expert_outputs(wl.R, wl.H, seed=6)
     ol = oracle.layout(wl.topk_idx, wl.E, wl.G, 0)
     lay = gpu_layout(wl.topk_idx, wl.E, wl.G, 0, with_src=False)
     got = _combine_gpu(y, wl.topk_weights, lay, wl.H)
-    toks = sample_tokens(wl.T, 48)
-    ref = oracle.combine_tokens(y, wl.topk_weights, ol["slot_idx"], toks)
-    assert_close_bf16(got[toks], ref, "combine dsv3 full size")
+    ref = _oracle_tokens(lambda toks: oracle.combine_tokens(y, wl.topk_weights, ol["slot_idx"], toks),
+                         wl.T, wl.H)
+    assert_close_bf16(got, ref, "combine dsv3 full size")
+
+
+def _oracle_tokens(fn, T: int, H: int, parts: int = 16) -> np.ndarray:
+    """fn(tokens) -> [len(tokens), H] bf16 bits, over all T tokens, split
+    into ranges run on threads (each oracle call runs single-threaded C)."""
+    bounds = np.linspace(0, T, parts + 1).astype(np.int64)
+    ranges = [np.arange(bounds[i], bounds[i + 1], dtype=np.int64) for i in range(parts)]
+    with ThreadPoolExecutor(parts) as ex:
+        outs = list(ex.map(lambda r: fn(r) if len(r) else np.zeros((0, H), np.uint16), ranges))
+    return np.concatenate(outs)
 
 
 # --------------------------------------------------------------------------- whole path
 @pytest.mark.parametrize("name", list(W.CONFIGS))
 def test_whole_path_identity_experts(name):
     """layout -> dispatch -> identity expert -> combine at the full size, on
-    the GPU; sampled tokens through the oracle's own chain."""
+    the GPU; every token through the oracle's own chain."""
     wl = W.make(name)
     note("whole path %s T=%d H=%d E=%d k=%d fp8=%s cap=%d" % (
         name, wl.T, wl.H, wl.E, wl.k, wl.fp8, wl.cap))
@@ -383,13 +413,13 @@ def test_whole_path_identity_experts(name):
     got = host_bits(out)
     del y
     ol = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap)
-    toks = sample_tokens(wl.T, 64) if wl.T > 256 else np.arange(wl.T)
     chain = oracle.chain_fp8_tokens if wl.fp8 else oracle.chain_bf16_tokens
-    ref = chain(wl.x_bits, wl.topk_weights, ol["slot_idx"], toks)
-    assert_close_bf16(got[toks], ref, "whole path %s" % name)
+    ref = _oracle_tokens(lambda toks: chain(wl.x_bits, wl.topk_weights, ol["slot_idx"], toks),
+                         wl.T, H)
+    assert_close_bf16(got, ref, "whole path %s, every token" % name)
     if not wl.fp8:
         # bf16 dispatch, identity experts, weights summing to 1: x comes back
-        same = (got[toks] == wl.x_bits[toks]) | (((got[toks] | wl.x_bits[toks]) & 0x7FFF) == 0)
+        same = (got == wl.x_bits) | (((got | wl.x_bits) & 0x7FFF) == 0)
         assert same.all()
 
 

@@ -105,6 +105,24 @@ def test_fp8_zero_and_signed_zero_blocks():
     assert (s == np.float32(np.float32(1e-4) / np.float32(448.0))).all()
 
 
+def test_fp8_nonfinite_block_golden():
+    """NaN and infinities on the fp32-scale path, worked by hand from the
+    definition: the block maximum skips NaN, an infinite maximum gives
+    scale = inf and inv = 0, and every NaN product encodes 0x7F."""
+    with open(os.path.join(GOLDEN, "fp8_nonfinite_block.json")) as f:
+        blocks = json.load(f)["blocks"]
+    xb = np.zeros(128 * len(blocks), np.uint16)
+    want = np.zeros(128 * len(blocks), np.uint8)
+    for b, blk in enumerate(blocks):
+        for i, (bits, code, _) in enumerate(blk["x"]):
+            xb[128 * b + i] = int(bits, 16)
+            want[128 * b + i] = int(code, 16)
+    q, s = oracle.quantize_token_fp8(xb)
+    bad = [(i, hex(a), hex(c)) for i, (a, c) in enumerate(zip(q, want)) if a != c]
+    assert not bad, bad[:5]
+    assert [hex(v) for v in s.view(np.uint32)] == [b["scale_bits"] for b in blocks]
+
+
 # --------------------------------------------------------------------------- bf16 dispatch
 def test_bf16_dispatch_is_the_gather():
     wl = workloads.make("skewed", T=64, H=512)

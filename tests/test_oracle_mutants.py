@@ -58,6 +58,9 @@ MUTANTS = [
     ("no floor under tiny blocks", "float a = amax > 1e-4f ? amax : 1e-4f;", "float a = amax;"),
     ("scale inverted", "float scale = a / 448.0f;", "float scale = 448.0f / a;"),
     ("amax of signed values", "float m = fabsf(bf16_to_float(x_row[c]));", "float m = bf16_to_float(x_row[c]);"),
+    ("E4M3 NaN keeps its sign", "if (isnan(v)) return 0x7F;", "if (isnan(v)) return signbit(v) ? 0xFF : 0x7F;"),
+    ("block maximum takes NaN", "if (m > amax) amax = m;\n        }\n        float a = amax > 1e-4f",
+     "if (!(m <= amax)) amax = m;\n        }\n        float a = amax > 1e-4f"),
     ("FP8 copies take the wrong scale row", "memcpy(recv_scales + (int64_t)s * nb, sc,",
      "memcpy(recv_scales + (int64_t)(s / 2) * nb, sc,"),
     ("combine uses the first weight only", "acc += (double)w[t * k + j] *", "acc += (double)w[t * k] *"),
@@ -133,6 +136,7 @@ def _battery():
         pins_dc.test_fp8_block_golden,
         pins_dc.test_fp8_dispatch_copies_and_rows,
         pins_dc.test_fp8_zero_and_signed_zero_blocks,
+        pins_dc.test_fp8_nonfinite_block_golden,
         pins_dc.test_bf16_dispatch_is_the_gather,
         pins_dc.test_bf16_dispatch_padded_skips_dropped,
         pins_dc.test_combine_golden,
