@@ -238,7 +238,7 @@ def ep_dispatch(x: torch.Tensor, layout: EpLayout, recv_dtype: int, recv_x: torc
     [R, H/32] E8M0 bytes (EP_MXFP8_E4M3), or their transposes [H/128, R] and
     [H/32, R] with EP_SCALES_MN_MAJOR.  EP_F16: x and recv_x fp16."""
     T, H = layout.num_tokens, x.shape[-1]
-    if tuple(x.shape) != (T, H) or recv_x.shape[0] != layout.num_recv_rows or recv_x.shape[-1] != H:
+    if tuple(x.shape) != (T, H) or tuple(recv_x.shape) != (layout.num_recv_rows, H):
         raise ValueError("dispatch buffers do not match the layout")
     _check_scales(recv_dtype, recv_scales, layout.num_recv_rows, H)
     xt, rt, st = _dispatch_types(recv_dtype)
@@ -255,7 +255,7 @@ def ep_layout_dispatch(topk_idx: torch.Tensor, layout: EpLayout, x: torch.Tensor
     T, H = layout.num_tokens, x.shape[-1]
     if tuple(topk_idx.shape) != (T, layout.num_topk):
         raise ValueError("topk_idx shape %s does not match the layout" % (tuple(topk_idx.shape),))
-    if tuple(x.shape) != (T, H) or recv_x.shape[0] != layout.num_recv_rows or recv_x.shape[-1] != H:
+    if tuple(x.shape) != (T, H) or tuple(recv_x.shape) != (layout.num_recv_rows, H):
         raise ValueError("dispatch buffers do not match the layout")
     _check_scales(recv_dtype, recv_scales, layout.num_recv_rows, H)
     xt, rt, st = _dispatch_types(recv_dtype)
@@ -271,7 +271,7 @@ def ep_combine(expert_out: torch.Tensor, topk_weights: torch.Tensor, layout: EpL
                out: torch.Tensor, stream=None) -> None:
     """expert_out bf16 [R, H], topk_weights fp32 [T, k] -> out bf16 [T, H]."""
     H = expert_out.shape[-1]
-    if (expert_out.shape[0] != layout.num_recv_rows
+    if (tuple(expert_out.shape) != (layout.num_recv_rows, H)
             or tuple(topk_weights.shape) != (layout.num_tokens, layout.num_topk)
             or tuple(out.shape) != (layout.num_tokens, H)):
         raise ValueError("combine buffers do not match the layout")
@@ -284,7 +284,7 @@ def ep_combine_f16(expert_out: torch.Tensor, topk_weights: torch.Tensor, layout:
                    out: torch.Tensor, stream=None) -> None:
     """expert_out fp16 [R, H], topk_weights fp32 [T, k] -> out fp16 [T, H]."""
     H = expert_out.shape[-1]
-    if (expert_out.shape[0] != layout.num_recv_rows
+    if (tuple(expert_out.shape) != (layout.num_recv_rows, H)
             or tuple(topk_weights.shape) != (layout.num_tokens, layout.num_topk)
             or tuple(out.shape) != (layout.num_tokens, H)):
         raise ValueError("combine buffers do not match the layout")
@@ -298,7 +298,7 @@ def ep_combine_fp8(expert_q: torch.Tensor, expert_scales: torch.Tensor, topk_wei
     """expert_q uint8 [R, H] E4M3 codes, expert_scales fp32 [R, H/128],
     topk_weights fp32 [T, k] -> out bf16 [T, H]."""
     H = expert_q.shape[-1]
-    if (expert_q.shape[0] != layout.num_recv_rows
+    if (tuple(expert_q.shape) != (layout.num_recv_rows, H)
             or tuple(expert_scales.shape) != (layout.num_recv_rows, H // 128)
             or tuple(topk_weights.shape) != (layout.num_tokens, layout.num_topk)
             or tuple(out.shape) != (layout.num_tokens, H)):
@@ -314,7 +314,7 @@ def ep_combine_mxfp8(expert_q: torch.Tensor, expert_scales: torch.Tensor, topk_w
     """expert_q uint8 [R, H] E4M3 codes, expert_scales uint8 [R, H/32] E8M0 bytes,
     topk_weights fp32 [T, k] -> out bf16 [T, H]."""
     H = expert_q.shape[-1]
-    if (expert_q.shape[0] != layout.num_recv_rows
+    if (tuple(expert_q.shape) != (layout.num_recv_rows, H)
             or tuple(expert_scales.shape) != (layout.num_recv_rows, H // 32)
             or tuple(topk_weights.shape) != (layout.num_tokens, layout.num_topk)
             or tuple(out.shape) != (layout.num_tokens, H)):
@@ -364,7 +364,7 @@ def ep_combine_groups(z: torch.Tensor, layout: EpGroupLayout, out: torch.Tensor,
     """z bf16 [T*kg, H] (one already-weighted row per (token, group)) -> out
     bf16 [T, H], the unit-weight sum of each token's group rows."""
     H = z.shape[-1]
-    if z.shape[0] != layout.num_recv_rows or tuple(out.shape) != (layout.num_tokens, H):
+    if tuple(z.shape) != (layout.num_recv_rows, H) or tuple(out.shape) != (layout.num_tokens, H):
         raise ValueError("group combine buffers do not match the layout")
     _check("ep_combine_groups", lib().ep_combine_groups(
         _ptr(z, "z", torch.bfloat16), ctypes.byref(layout.struct), H,

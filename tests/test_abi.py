@@ -97,6 +97,38 @@ def test_binding_rejects_host_tensors_before_any_launch(L):
         binding.ep_combine(recv, torch.zeros((16, 2)), lay, x)
 
 
+def test_binding_checks_row_buffer_shapes_exactly(L):
+    """The C ABI cannot see buffer sizes, so the binding compares every row
+    buffer's whole shape with (rows, hidden): a 1-D buffer whose length
+    happens to equal hidden, or a 3-D one, is refused before any pointer is
+    taken."""
+    import torch
+    T, k, E, H = 16, 2, 8, 32
+    lay = binding.EpLayout(T, k, E, 2, device=torch.device("cpu"))
+    R = lay.num_recv_rows
+    assert R == H  # so that a 1-D buffer of R elements has shape[-1] == H
+    x = torch.zeros((T, H), dtype=torch.bfloat16)
+    w = torch.zeros((T, k))
+    out = torch.zeros((T, H), dtype=torch.bfloat16)
+    flat = torch.zeros(R, dtype=torch.bfloat16)
+    cube = torch.zeros((R, 1, H), dtype=torch.bfloat16)
+    for bad in (flat, cube):
+        with pytest.raises(ValueError, match="do not match"):
+            binding.ep_dispatch(x, lay, binding.EP_BF16, bad)
+        with pytest.raises(ValueError, match="do not match"):
+            binding.ep_layout_dispatch(torch.zeros((T, k), dtype=torch.int64), lay, x,
+                                       binding.EP_BF16, bad)
+        with pytest.raises(ValueError, match="do not match"):
+            binding.ep_combine(bad, w, lay, out)
+        with pytest.raises(ValueError, match="do not match"):
+            binding.ep_combine_f16(bad.half(), w, lay, out.half())
+    q_flat = torch.zeros(R, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="do not match"):
+        binding.ep_combine_fp8(q_flat, torch.zeros((R, H // 128)), w, lay, out)
+    with pytest.raises(ValueError, match="do not match"):
+        binding.ep_combine_mxfp8(q_flat, torch.zeros((R, H // 32), dtype=torch.uint8), w, lay, out)
+
+
 def test_layout_init_validation(L):
     s = binding.ep_layout_t()
     ok = L.ep_layout_init(ctypes.byref(s), 8192, 8, 256, 8, 0)
