@@ -11,21 +11,33 @@ path and not timed.
 
 Prints one JSON line.  `value` is the step's ideal (algorithmic) HBM bytes
 divided by the step's wall time over K back-to-back steps with nothing else
-enqueued (the steady state).  The per-kernel times come from a separate pass
-of K steps with HIP events recorded around every call on the stream the
-kernels run on; the events cost a few us each, so that pass's step time is
-reported apart (`ms_per_step_with_events`).  The same line reports the
-per-kernel times of extra steps that each start with L2 and the MALL emptied
-(a 512 MiB read outside the events), and the roofline of the dominant kernel
-(combine) with its HBM traffic from the committed rocprofv3 counter summary.
+enqueued (the steady state, in which x is still in the last-level cache from
+the previous step, as it would be after the router read it).  The per-kernel
+times come from a separate pass of K steps with HIP events recorded around
+every call on the stream the kernels run on; the events cost a few us each,
+so that pass's step time is reported apart (`ms_per_step_with_events`).
+
+`after_flush` holds the HBM-only figures: every one of those steps starts
+after a 512 MiB read has emptied L2 and the MALL.  It gives per-kernel times
+(events around every call), the whole step's time with events only at its two
+ends, the dispatch kernel's roofline fraction, and the same whole step with
+ep_layout_dispatch and EP_READ_X_AHEAD (x read into the MALL while the
+latency-bound layout runs), for the workloads where that applies.
+
+`roofline` is the dominant kernel's (combine): algorithmic bytes per launch
+over the mean HIP-event time of its launches, beside the committed rocprofv3
+kernel-trace mean and HBM traffic when they were taken on the current kernel
+sources.  `cpu_baseline` is the oracle on this host's cores, single-threaded
+and with the tokens split across the cores.
 
 `--workload` times the other named workloads (tiny, skewed, lowlat, large) the
 same way; the default is the configuration the metric is quoted on.  Variant
-flags: --fused (one-call layout+dispatch), --pow2 / --mx (power-of-two or
-MXFP8 scales), --mn-scales (dispatch stores its scales transposed),
---mn-convert (row-major dispatch, then the scale-layout conversion kernel),
---fp8-combine (FP8 expert outputs), --f16 (fp16 rows), --dedup (per-group dedup layout, dispatch
-and combine), --graph (HIP graph).
+flags: --fused (one-call layout+dispatch), --read-x-ahead (the same with
+EP_READ_X_AHEAD), --pow2 / --mx (power-of-two or MXFP8 scales), --mn-scales
+(dispatch stores its scales transposed), --mn-convert (row-major dispatch, then
+the scale-layout conversion kernel), --fp8-combine (FP8 expert outputs), --f16
+(fp16 rows), --dedup (per-group dedup layout, dispatch and combine), --graph
+(HIP graph).
 """
 from __future__ import annotations
 
@@ -97,45 +109,90 @@ def sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel: str, workload: str, digest: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources; else None."""
-    path = os.path.join(PROFILES, "%s_%s_traffic.md" % (kernel, workload))
+def _committed_json(fname: str, tag: str, digest: str):
+    """The machine-readable `tag: {...}` line of a committed rocprofv3 summary
+    under profiles/, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, fname)
     if not os.path.exists(path):
         return None
-    m = re.search(r"traffic_json:\s*(\{.*\})", open(path).read())
+    m = re.search(tag + r":\s*(\{.*\})", open(path).read())
     if not m:
         return None
     rec = json.loads(m.group(1))
     return rec if rec.get("sources_digest") == digest else None
 
 
+def committed_traffic(workload: str, digest: str):
+    """HBM bytes per launch of each kernel (FETCH_SIZE + WRITE_SIZE, calibrated)
+    from profiles/<workload>_traffic.md."""
+    return _committed_json("%s_traffic.md" % workload, "traffic_json", digest)
+
+
+def committed_trace(workload: str, digest: str):
+    """Mean kernel durations (us) from profiles/<workload>_kernel_trace.md."""
+    return _committed_json("%s_kernel_trace.md" % workload, "trace_json", digest)
+
+
 def cpu_baseline(wl) -> dict:
-    """The oracle, as it is, single-threaded on this host, over the whole
-    workload: layout + FP8 dispatch + combine (the identity expert between
-    them is the oracle's own dequantisation, untimed, like on the GPU)."""
-    import oracle
+    """The oracle as it stands, on this host, over the whole workload: layout +
+    FP8 dispatch + combine (the identity expert between them, the oracle's own
+    dequantisation, is untimed, like on the GPU).  Timed single-threaded, then
+    with the tokens cut into one contiguous range per thread (as many threads
+    as the cores this process may run on, capped by the host's OMP_NUM_THREADS
+    share); the layout stays one sequential pass, its order being the
+    definition.  Each oracle call is single-threaded C that releases the GIL."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
     oracle.lib()
+    affinity = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS") or affinity)
+    threads = max(1, min(affinity, share))
+    T, H, R = wl.T, wl.H, wl.R
+
     t0 = time.perf_counter()
     lay = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap, want_recv_src=False)
-    q, s = oracle.dispatch_fp8(wl.x_bits, lay["slot_idx"], wl.R)
+    q, s = oracle.dispatch_fp8(wl.x_bits, lay["slot_idx"], R)
     t1 = time.perf_counter()
     y = oracle.dequant_fp8(q, s)
     del q, s
     t2 = time.perf_counter()
-    out = oracle.combine(y, wl.topk_weights, lay["slot_idx"])
+    out1 = oracle.combine(y, wl.topk_weights, lay["slot_idx"])
     t3 = time.perf_counter()
-    secs = (t1 - t0) + (t3 - t2)
+    single = (t1 - t0) + (t3 - t2)
+
+    bounds = np.linspace(0, T, threads + 1).astype(np.int64)
+    parts = [(int(bounds[i]), int(bounds[i + 1])) for i in range(threads) if bounds[i + 1] > bounds[i]]
+    x, w = wl.x_bits, wl.topk_weights
+    with ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        lay2 = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap, want_recv_src=False)
+        sl = lay2["slot_idx"]
+        q = np.zeros((R, H), np.uint8)
+        s = np.zeros((R, H // 128), np.float32)
+        list(ex.map(lambda r: oracle.dispatch_fp8_into(x[r[0]:r[1]], sl[r[0]:r[1]], q, s), parts))
+        t1 = time.perf_counter()
+        del q, s
+        t2 = time.perf_counter()
+        out = np.empty((T, H), np.uint16)
+        list(ex.map(lambda r: oracle.combine_into(y, w[r[0]:r[1]], sl[r[0]:r[1]], out[r[0]:r[1]]),
+                    parts))
+        t3 = time.perf_counter()
+    multi = (t1 - t0) + (t3 - t2)
+    assert (out == out1).all(), "the threaded oracle run must give the single-threaded result"
     used = int((lay["slot_idx"] >= 0).sum())
-    b = ideal_bytes(wl.T, wl.H, wl.E, wl.G, wl.k, used, True)
-    del y, out
-    return {"value": round(sum(b.values()) / secs / 1e9, 4), "unit": "GB/s", "cores": 1,
+    b = sum(ideal_bytes(T, H, wl.E, wl.G, wl.k, used, True).values())
+    del y, out, out1
+    return {"value": round(b / multi / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": "the whole workload (T=%d, H=%d, E=%d, top-%d, FP8 dispatch, bf16 "
-                      "combine), layout+dispatch+combine timed once, %.2f s" % (
-                          wl.T, wl.H, wl.E, wl.k, secs),
-            "seconds": round(secs, 3), "cpu": cpu_model()}
+                      "combine): layout (one sequential pass) + dispatch + combine, tokens split "
+                      "over %d threads, %.3f s; single-threaded %.3f s" % (
+                          T, H, wl.E, wl.k, threads, multi, single),
+            "seconds": round(multi, 4), "cpu": cpu_model(), "cores_available": affinity,
+            "single_thread": {"value": round(b / single / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "seconds": round(single, 4)}}
 
 
 def cpu_model() -> str:
@@ -173,7 +230,10 @@ def main() -> int:
                          "reads them with ep_combine_fp8 (ep_combine_mxfp8 with --mx)")
     ap.add_argument("--fused", action="store_true",
                     help="layout and dispatch through ep_layout_dispatch (one launch for batches "
-                         "of at most 2048 pairs); the layout/dispatch split is then not reported")
+                         "of at most 4096 pairs); the layout/dispatch split is then not reported")
+    ap.add_argument("--read-x-ahead", action="store_true",
+                    help="as --fused, with EP_READ_X_AHEAD: the layout launches read x into the "
+                         "last-level cache for dispatch")
     ap.add_argument("--mx", action="store_true",
                     help="MXFP8 dispatch (EP_MXFP8_E4M3: one E8M0 scale byte per 32 channels)")
     ap.add_argument("--mn-scales", action="store_true",
@@ -187,6 +247,8 @@ def main() -> int:
                     help="per-group dedup variant: ep_get_group_layout (with the receiving "
                          "side's metadata), dispatch to the groups, ep_combine_groups")
     args = ap.parse_args()
+    if args.read_x_ahead:
+        args.fused = True
     if args.dedup and (args.fused or args.fp8_combine or args.f16):
         print("--dedup times its own three calls; it combines with --pow2, --mx and --graph only",
               file=sys.stderr)
@@ -242,6 +304,8 @@ def main() -> int:
     # the timed dispatch's dtype; the untimed set-up below writes row-major
     # scales for the identity-expert stand-in
     step_dtype = dtype_enum | (B.EP_SCALES_MN_MAJOR if args.mn_scales else 0)
+    if args.read_x_ahead:
+        step_dtype |= B.EP_READ_X_AHEAD
     if args.f16:
         # fp16 activations of the same distribution (the bf16 values, converted)
         x = torch.from_numpy(wl.x_bits.view(np.int16)).to(dev).view(torch.bfloat16).to(torch.float16)
@@ -315,9 +379,10 @@ def main() -> int:
         nbytes["scales_mn"] = 2 * R * (H // 128) * 4
     step_bytes = sum(nbytes.values())
 
-    def step(ev=None, s=None):
+    def step(ev=None, s=None, read_ahead=False):
         # s: the stream to launch on (None = torch's current stream, which is
-        # the capture stream while a graph is being recorded)
+        # the capture stream while a graph is being recorded).  read_ahead:
+        # layout + dispatch through ep_layout_dispatch with EP_READ_X_AHEAD.
         if ev is not None:
             ev[0].record(s)
         if args.dedup:
@@ -331,8 +396,9 @@ def main() -> int:
             if ev is not None:
                 ev[3].record(s)
             return
-        if args.fused:
-            B.ep_layout_dispatch(topk_idx, lay, x, step_dtype, recv_q, recv_s, s)
+        if args.fused or read_ahead:
+            dt = step_dtype | (B.EP_READ_X_AHEAD if read_ahead else 0)
+            B.ep_layout_dispatch(topk_idx, lay, x, dt, recv_q, recv_s, s)
             if ev is not None:
                 ev[1].record(s)
         else:
@@ -425,24 +491,64 @@ def main() -> int:
     # nothing of the previous step is left in L2 or the MALL and the dirty
     # lines it left are written back before the step starts.  (Writing the
     # buffer instead would leave the MALL full of dirty lines whose write-back
-    # the next step's writes would pay for.)  Per-kernel event times only; the
+    # the next step's writes would pay for.)  Three passes: events around every
+    # call (per-kernel times); events only at the step's two ends (the step's
+    # own time, with no event inside it); and, where it applies, the step with
+    # layout + dispatch through ep_layout_dispatch with EP_READ_X_AHEAD.  The
     # timed loop above is the steady state.
     flushed = None
+    x_bytes = x.numel() * x.element_size()
+    read_ahead_applies = (not (args.dedup or args.fused or args.mn_convert)
+                          and T * k > 4096 and x_bytes <= (128 << 20))
     if graph is None and not args.no_flush:
         flush_buf = torch.zeros((512 << 20) // 8, dtype=torch.int64, device=dev)
         n_flush = min(args.steps, 50)
-        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_flush)]
-        for i in range(n_flush):
-            flush_buf.sum()
-            step(fev[i], stream)
-        torch.cuda.synchronize()
+
+        def flushed_pass(n_events, read_ahead=False):
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_flush)]
+            for i in range(n_flush):
+                flush_buf.sum()
+                if n_events == 4:
+                    step(evs[i], stream, read_ahead)
+                else:
+                    evs[i][0].record(stream)
+                    step(None, stream, read_ahead)
+                    evs[i][3].record(stream)
+            torch.cuda.synchronize()
+            return evs
+
+        fev = flushed_pass(4)
         first = "layout_dispatch" if args.fused else "layout"
         fper = {first: [ev[0].elapsed_time(ev[1]) for ev in fev]}
         if not args.fused:
             fper["dispatch"] = [ev[1].elapsed_time(ev[2]) for ev in fev]
         fper["combine"] = [ev[2].elapsed_time(ev[3]) for ev in fev]
-        flushed = {kname: round(float(np.mean(v)) * 1e3, 2) for kname, v in fper.items()}
+        flushed = {"kernel_us_mean": {kname: round(float(np.mean(v)) * 1e3, 2) for kname, v in fper.items()}}
+        whole = [ev[0].elapsed_time(ev[3]) * 1e3 for ev in flushed_pass(2)]
+        flushed["step_us"] = round(float(np.mean(whole)), 2)
+        flushed["step_us_p50"] = round(float(np.percentile(whole, 50)), 2)
+        if read_ahead_applies:
+            rev = flushed_pass(4, read_ahead=True)
+            whole_ra = [ev[0].elapsed_time(ev[3]) * 1e3 for ev in flushed_pass(2, read_ahead=True)]
+            flushed["read_x_ahead"] = {
+                "kernel_us_mean": {
+                    "layout_dispatch": round(float(np.mean([e[0].elapsed_time(e[1]) for e in rev])) * 1e3, 2),
+                    "combine": round(float(np.mean([e[2].elapsed_time(e[3]) for e in rev])) * 1e3, 2)},
+                "step_us": round(float(np.mean(whole_ra)), 2),
+                "step_us_p50": round(float(np.percentile(whole_ra, 50)), 2)}
         del flush_buf
+
+    # the steady state of the read-ahead form (x already cached when it runs)
+    steady_read_ahead = None
+    if graph is None and read_ahead_applies:
+        for _ in range(3):
+            step(None, stream, True)
+        torch.cuda.synchronize()
+        r0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(None, stream, True)
+        torch.cuda.synchronize()
+        steady_read_ahead = (time.perf_counter() - r0) * 1e6 / args.steps
 
     # plain copy of the same size as combine's traffic: the practical ceiling
     copy_bytes = 1 << 30
@@ -482,9 +588,12 @@ def main() -> int:
     else:
         dc_gbps = combine_gbps = dispatch_gbps = None
     digest = sources_digest()
-    # the committed counters cover the bf16-input combine kernel only
-    traffic = (None if (args.fp8_combine or args.dedup or args.f16) else
-               committed_traffic("combine", name, digest))
+    # the committed summaries: HBM traffic (two counter runs) and kernel-trace
+    # means of the default step of each workload, valid on the current sources
+    default_path = not (args.dedup or args.mx or args.f16 or args.pow2 or args.fp8_combine
+                        or args.mn_scales or args.mn_convert or args.fused)
+    traffic = committed_traffic(name, digest) if default_path else None
+    trace = committed_trace(name, digest) if default_path else None
 
     result = {
         "metric": "dispatch+combine effective HBM GB/s (% peak) at 8K tok×7168, top-8/256",
@@ -521,8 +630,8 @@ def main() -> int:
         "kernel_us_p50": {kk: round(v, 2) for kk, v in p50.items()},
         "kernel_us_p95": {kk: round(v, 2) for kk, v in p95.items()},
         "kernel_us_p99": {kk: round(v, 2) for kk, v in p99.items()},
-        "caches": "warm: steps back to back (x stays in the MALL between steps); "
-                  "*_after_flush: each step after a 512 MiB read empties L2 and the MALL",
+        "caches": "value and kernel_us_*: steps back to back (x stays in the MALL between "
+                  "steps); after_flush: each step after a 512 MiB read empties L2 and the MALL",
         "copy_kernel_gbps": round(copy_gbps, 1),
         "sources_digest": digest,
     }
@@ -530,29 +639,58 @@ def main() -> int:
         result["dispatch_plus_combine_gbps"] = round(dc_gbps, 1)
         result["dispatch_plus_combine_pct_peak"] = round(100 * dc_gbps / HBM_PEAK_GBPS, 2)
         result["dispatch_gbps"] = round(dispatch_gbps, 1)
-        result["roofline"] = {
+        roof = {
             "kernel": "combine_groups" if args.dedup else
             ("combine_mxfp8" if args.mx else "combine_fp8") if args.fp8_combine
             else "combine_f16" if args.f16 else "combine", "bound": "hbm",
             "achieved": round(combine_gbps, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(combine_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None if traffic is None else traffic["bytes_per_launch"],
-            "algorithmic_bytes": nbytes["combine"]}
+            "traffic": None if traffic is None else traffic["bytes_per_launch"]["combine"],
+            "algorithmic_bytes": nbytes["combine"],
+            "time_source": "mean of HIP events recorded just before and after each combine launch "
+                           "on its stream, over the %d steps of the per-kernel pass; each interval "
+                           "also holds the events' own cost (a few us)" % args.steps,
+            "launch_us": round(us["combine"], 2)}
+        if trace is not None:
+            # the committed rocprofv3 kernel trace (kernel start to end, no events)
+            t_c = trace["avg_us"]["combine"]
+            roof["profile_launch_us"] = t_c
+            roof["profile_frac"] = round(nbytes["combine"] / (t_c * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+            roof["profile"] = "profiles/%s_kernel_trace.md" % name
+        result["roofline"] = roof
     else:
         result["config"]["step"] += " (HIP graph replay, %d steps per graph)" % gs
         result["graph_steps"] = gs
     if flushed is not None:
         d_key = "layout_dispatch" if args.fused else "dispatch"
         d_bytes_f = nbytes["dispatch"] + (nbytes["layout"] if args.fused else 0) + nbytes.get("scales_mn", 0)
-        result["kernel_us_mean_after_flush"] = flushed
-        result["dispatch_plus_combine_gbps_after_flush"] = round(
-            (d_bytes_f + nbytes["combine"]) / ((flushed[d_key] + flushed["combine"]) * 1e-6) / 1e9, 1)
+        fk = flushed["kernel_us_mean"]
+        dc_f = (d_bytes_f + nbytes["combine"]) / ((fk[d_key] + fk["combine"]) * 1e-6) / 1e9
+        flushed["dispatch_plus_combine_gbps"] = round(dc_f, 1)
+        flushed["dispatch_plus_combine_pct_peak"] = round(100 * dc_f / HBM_PEAK_GBPS, 2)
+        flushed["dispatch_roofline_frac"] = round(
+            d_bytes_f / (fk[d_key] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+        # whole step, events at its ends only: all the step's bytes, and the
+        # dispatch + combine bytes alone (the layout's time stays in the denominator)
+        for key, form in ((None, flushed), ("read_x_ahead", flushed.get("read_x_ahead"))):
+            if form is None:
+                continue
+            st_us = form["step_us"]
+            form["step_gbps"] = round(step_bytes / (st_us * 1e-6) / 1e9, 1)
+            form["step_pct_peak"] = round(100 * step_bytes / (st_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2)
+            dc_b = step_bytes - nbytes["layout"]
+            form["dispatch_plus_combine_pct_peak_of_step"] = round(
+                100 * dc_b / (st_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2)
+        result["after_flush"] = flushed
+        # the earlier names of two of these figures
+        result["kernel_us_mean_after_flush"] = fk
+        result["dispatch_plus_combine_gbps_after_flush"] = round(dc_f, 1)
+    if steady_read_ahead is not None:
+        result["read_x_ahead_steady_step_us"] = round(steady_read_ahead, 2)
     if dedup is not None:
         result["dedup"] = dedup
     if convert is not None:
         result["scales_mn_conversion"] = convert
-    default_path = not (args.dedup or args.mx or args.f16 or args.pow2 or args.fp8_combine
-                        or args.mn_scales or args.mn_convert)
     if not args.no_cpu_baseline and name == "dsv3" and default_path:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

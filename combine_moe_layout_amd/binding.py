@@ -21,6 +21,7 @@ EP_FP8_E4M3_POW2 = 2
 EP_MXFP8_E4M3 = 3
 EP_F16 = 4
 EP_SCALES_MN_MAJOR = 0x100   # OR-ed into an FP8 dtype: scales stored transposed
+EP_READ_X_AHEAD = 0x200      # OR-ed into ep_layout_dispatch's dtype: x read into the MALL during the layout
 _FP8_DTYPES = (EP_FP8_E4M3, EP_FP8_E4M3_POW2, EP_MXFP8_E4M3)
 EP_FLAG_BAD_EXPERT = 1
 EP_FLAG_OVERFLOW = 2
@@ -214,7 +215,7 @@ def ep_get_layout(topk_idx: torch.Tensor, layout: EpLayout, stream=None) -> EpLa
 def _dispatch_types(recv_dtype: int):
     """(x dtype, recv_x dtype, recv_scales dtype) of a receive dtype (with or
     without EP_SCALES_MN_MAJOR)."""
-    recv_dtype &= ~EP_SCALES_MN_MAJOR
+    recv_dtype &= ~(EP_SCALES_MN_MAJOR | EP_READ_X_AHEAD)
     if recv_dtype == EP_F16:
         return torch.float16, torch.float16, None
     if recv_dtype == EP_MXFP8_E4M3:
@@ -226,7 +227,7 @@ def _dispatch_types(recv_dtype: int):
 
 def _check_scales(recv_dtype: int, recv_scales, R: int, H: int) -> None:
     """Every FP8 scale layout holds H/128 four-byte words per receive row."""
-    if (recv_dtype & ~EP_SCALES_MN_MAJOR) in _FP8_DTYPES and recv_scales is not None:
+    if (recv_dtype & ~(EP_SCALES_MN_MAJOR | EP_READ_X_AHEAD)) in _FP8_DTYPES and recv_scales is not None:
         if recv_scales.numel() * recv_scales.element_size() != R * (H // 128) * 4:
             raise ValueError("recv_scales does not hold %d rows of %d channels' scales" % (R, H))
 

@@ -35,30 +35,42 @@ int check_layout(const ep_layout_t* L) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_LAUNCH; }
 
-// Checks shared by ep_get_layout and ep_layout_dispatch.
-int check_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
-                     size_t workspace_bytes) {
+// The layout's own arguments (everything but the workspace).
+int check_layout_args(const int64_t* topk_idx, const ep_layout_t* layout) {
   int rc = check_layout(layout);
   if (rc != EP_OK) return rc;
   const ep_layout_t& L = *layout;
   if ((L.num_tokens > 0 && topk_idx == nullptr) || L.num_tokens_per_expert == nullptr ||
       L.expert_offsets == nullptr || L.num_tokens_per_group == nullptr ||
-      L.error_flags == nullptr || workspace == nullptr)
+      L.error_flags == nullptr)
     return EP_ERR_NULL;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return EP_ERR_ALIGN;
-  if (workspace_bytes <
-      ep::layout_workspace_bytes(L.num_tokens * (int64_t)L.num_topk, L.num_experts))
-    return EP_ERR_WORKSPACE;
   return EP_OK;
 }
 
-// Checks shared by ep_dispatch and ep_layout_dispatch (after the layout's).
+size_t layout_workspace_need(const ep_layout_t& L) {
+  return ep::layout_workspace_bytes(L.num_tokens * (int64_t)L.num_topk, L.num_experts);
+}
+
+// Checks shared by ep_get_layout and ep_layout_dispatch.
+int check_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
+                     size_t workspace_bytes) {
+  int rc = check_layout_args(topk_idx, layout);
+  if (rc != EP_OK) return rc;
+  if (workspace == nullptr) return EP_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return EP_ERR_ALIGN;
+  if (workspace_bytes < layout_workspace_need(*layout)) return EP_ERR_WORKSPACE;
+  return EP_OK;
+}
+
+// Checks shared by ep_dispatch and ep_layout_dispatch (after the layout's);
+// only the latter takes EP_READ_X_AHEAD.
 int check_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,
-                   void* recv_x, void* recv_scales) {
+                   void* recv_x, void* recv_scales, bool read_ahead_ok) {
   const int32_t base = ep::dtype_base(recv_dtype);
   const bool fp8 = ep::dtype_is_fp8(base);
   if (base != EP_BF16 && base != EP_F16 && !fp8) return EP_ERR_DTYPE;
   if (ep::dtype_scales_mn(recv_dtype) && !fp8) return EP_ERR_DTYPE;
+  if (ep::dtype_read_x_ahead(recv_dtype) && !read_ahead_ok) return EP_ERR_DTYPE;
   if (hidden < 8 || hidden > EP_MAX_HIDDEN || hidden % 8 != 0 || (fp8 && hidden % 128 != 0))
     return EP_ERR_SHAPE;
   if (layout->num_tokens == 0) return EP_OK;
@@ -112,7 +124,7 @@ int ep_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_
                 void* recv_x, void* recv_scales, void* stream) {
   int rc = check_layout(layout);
   if (rc != EP_OK) return rc;
-  rc = check_dispatch(x, layout, hidden, recv_dtype, recv_x, recv_scales);
+  rc = check_dispatch(x, layout, hidden, recv_dtype, recv_x, recv_scales, false);
   if (rc != EP_OK || layout->num_tokens == 0) return rc;
   return launch_status(ep::launch_dispatch(x, *layout, hidden, recv_dtype, recv_x, recv_scales,
                                            static_cast<hipStream_t>(stream)));
@@ -123,13 +135,18 @@ int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void*
                        void* recv_x, void* recv_scales, void* stream) {
   int rc = check_get_layout(topk_idx, layout, workspace, workspace_bytes);
   if (rc != EP_OK) return rc;
-  rc = check_dispatch(x, layout, hidden, recv_dtype, recv_x, recv_scales);
+  rc = check_dispatch(x, layout, hidden, recv_dtype, recv_x, recv_scales, true);
   if (rc != EP_OK) return rc;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool read_ahead = ep::dtype_read_x_ahead(recv_dtype);
+  recv_dtype &= ~EP_READ_X_AHEAD;
   if (ep::fused_layout_dispatch_fits(*layout))
     return launch_status(ep::launch_layout_dispatch_small(topk_idx, *layout, x, hidden, recv_dtype,
                                                           recv_x, recv_scales, s));
-  rc = launch_status(ep::launch_layout(topk_idx, *layout, workspace, s));
+  // With EP_READ_X_AHEAD the layout's launches also read x (2-byte elements)
+  // into the last-level cache.
+  const size_t x_bytes = read_ahead ? (size_t)layout->num_tokens * (size_t)hidden * 2 : 0;
+  rc = launch_status(ep::launch_layout_warm(topk_idx, *layout, workspace, x, x_bytes, s));
   if (rc != EP_OK || layout->num_tokens == 0) return rc;
   return launch_status(ep::launch_dispatch(x, *layout, hidden, recv_dtype, recv_x, recv_scales, s));
 }

@@ -34,20 +34,40 @@ hipError_t launch_layout(const int64_t* topk_idx, const ep_layout_t& L, void* wo
                          hipStream_t stream);
 
 // The layout over an id table that another kernel wrote, which also left
-// extra_flags bad-id flag entries at layout_extra_flags(L, workspace).
+// extra_flags bad-id flag entries at layout_extra_flags(L, workspace).  With
+// warm != null (and warm_bytes at most kWarmMaxBytes), the two layout
+// launches also read warm_bytes of `warm` into the last-level cache from
+// kWarmBlocks extra workgroups each (kWarmCountShare percent during the count
+// launch, the rest during the finish launch).
 hipError_t launch_layout_ids(const int64_t* ids, const ep_layout_t& L, void* workspace,
-                             int32_t extra_flags, hipStream_t stream);
+                             int32_t extra_flags, hipStream_t stream,
+                             const void* warm = nullptr, size_t warm_bytes = 0);
 int32_t* layout_extra_flags(const ep_layout_t& L, void* workspace);
 
+// The layout of a large batch whose dispatch source x (warm_bytes) follows:
+// x is read into the last-level cache while the latency-bound layout runs.
+#ifndef EP_WARM_COUNT_SHARE
+#define EP_WARM_COUNT_SHARE 40
+#endif
+constexpr int kWarmCountShare = EP_WARM_COUNT_SHARE;
+constexpr int kWarmBlocks = 256;
+// Half the MI355X MALL (256 MB): a larger source would evict itself before
+// dispatch reads it.
+constexpr size_t kWarmMaxBytes = (size_t)128 << 20;
+hipError_t launch_layout_warm(const int64_t* topk_idx, const ep_layout_t& L, void* workspace,
+                              const void* warm, size_t warm_bytes, hipStream_t stream);
 // Receive dtypes whose rows are E4M3 codes with a scale row (the others are a
 // bit copy of 2-byte elements).
 inline bool dtype_is_fp8(int32_t dtype) {
   return dtype == EP_FP8_E4M3 || dtype == EP_FP8_E4M3_POW2 || dtype == EP_MXFP8_E4M3;
 }
 
-// A dispatch dtype splits into its element type and the MN-major scale flag.
-inline int32_t dtype_base(int32_t dtype) { return dtype & ~EP_SCALES_MN_MAJOR; }
+// A dispatch dtype splits into its element type and the option flags.
+inline int32_t dtype_base(int32_t dtype) {
+  return dtype & ~(EP_SCALES_MN_MAJOR | EP_READ_X_AHEAD);
+}
 inline bool dtype_scales_mn(int32_t dtype) { return (dtype & EP_SCALES_MN_MAJOR) != 0; }
+inline bool dtype_read_x_ahead(int32_t dtype) { return (dtype & EP_READ_X_AHEAD) != 0; }
 
 // recv_scales: fp32 [R, hidden/128] or, for EP_MXFP8_E4M3, E8M0 bytes
 // [R, hidden/32]: hidden/128 4-byte words per row either way.  With

@@ -299,11 +299,55 @@ struct LayoutArgs {
   int32_t* expert_offsets;
   int32_t* num_tokens_per_group;
   int32_t* error_flags;
+  // Reading the dispatch source ahead (null when not asked for): workgroups
+  // past the layout's own read 16-byte vectors [0, warm_split) of `warm`
+  // during the count launch and [warm_split, warm_vecs) during the finish
+  // launch, warm_blocks workgroups per launch.
+  const u32x4* warm;
+  int64_t warm_vecs, warm_split;
+  int32_t warm_blocks;
+  int32_t never;  // 0 at run time; keeps the warm-up loads from being dropped
 };
+
+// Workgroup `worker` of `workers` reads its share of vectors [begin, end) of
+// src with ordinary loads and discards them.  Ordinary loads allocate in the
+// last-level cache (the MALL, 256 MB on MI355X), so a kernel that reads the
+// same rows next finds them there; the layout's few dozen latency-bound
+// workgroups leave HBM idle, and this fills that time.  Each wave instruction
+// covers 1 KiB of consecutive vectors; kWarmDepth loads per lane are in flight
+// at once.
+constexpr int kWarmDepth = 8;
+
+// Not inlined: inlined into the finish kernel it took that kernel from 44 to 84
+// VGPRs (5 waves per SIMD instead of 8); as a call it costs no registers there.
+__device__ __noinline__ void warm_slab(const u32x4* __restrict__ src, int64_t begin, int64_t end,
+                                       int32_t worker, int32_t workers, int32_t never,
+                                       int32_t* __restrict__ sink) {
+  const int64_t per = (end - begin + workers - 1) / workers;
+  const int64_t lo = begin + (int64_t)worker * per;
+  const int64_t hi = lo + per < end ? lo + per : end;
+  uint32_t acc = 0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += (int64_t)kLayoutThreads * kWarmDepth) {
+    u32x4 v[kWarmDepth];
+#pragma unroll
+    for (int u = 0; u < kWarmDepth; ++u) {
+      const int64_t j = i + (int64_t)u * kLayoutThreads;
+      v[u] = j < hi ? src[j] : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kWarmDepth; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (never != 0 && threadIdx.x == 0) sink[0] = (int32_t)acc;  // never taken
+}
 
 // Phase 1: ranks leave packed through slot_idx.
 __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(LayoutArgs a) {
   __shared__ int32_t hist[kLayoutWaves * EP_MAX_EXPERTS];
+  if ((int32_t)blockIdx.x >= a.num_chunks) {
+    warm_slab(a.warm, 0, a.warm_split, (int32_t)blockIdx.x - a.num_chunks, a.warm_blocks, a.never,
+              a.chunk_count);
+    return;
+  }
   int32_t eid[kLayoutItems], local[kLayoutItems];
   count_chunk(a.topk_idx, a.num_pairs, a.num_experts, a.expert_bits, blockIdx.x, hist,
               a.chunk_count, a.chunk_flags, nullptr, eid, local);
@@ -326,6 +370,12 @@ __device__ __forceinline__ int32_t load_flag_bits(const int32_t* __restrict__ ch
 // Phase 2 (also the whole layout when there are no pairs).
 __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(LayoutArgs a) {
   __shared__ LayoutShared sh;
+  const int32_t own = a.num_chunks > 0 ? a.num_chunks : 1;
+  if ((int32_t)blockIdx.x >= own) {
+    warm_slab(a.warm, a.warm_split, a.warm_vecs, (int32_t)blockIdx.x - own, a.warm_blocks,
+              a.never, a.chunk_count);
+    return;
+  }
   int32_t eid[kLayoutItems], local[kLayoutItems];
   // workgroup 0 reports the flags; their loads are issued first and used last
   const int32_t flag_bits = blockIdx.x == 0 ? load_flag_bits(a.chunk_flags, 0, a.num_flags) : 0;
@@ -363,13 +413,19 @@ hipError_t launch_layout(const int64_t* topk_idx, const ep_layout_t& L, void* wo
   return launch_layout_ids(topk_idx, L, workspace, 0, stream);
 }
 
+hipError_t launch_layout_warm(const int64_t* topk_idx, const ep_layout_t& L, void* workspace,
+                              const void* warm, size_t warm_bytes, hipStream_t stream) {
+  return launch_layout_ids(topk_idx, L, workspace, 0, stream, warm, warm_bytes);
+}
+
 int32_t* layout_extra_flags(const ep_layout_t& L, void* workspace) {
   const int64_t chunks = layout_num_chunks(L.num_tokens * (int64_t)L.num_topk);
   return static_cast<int32_t*>(workspace) + chunks * L.num_experts + chunks;
 }
 
 hipError_t launch_layout_ids(const int64_t* topk_idx, const ep_layout_t& L, void* workspace,
-                             int32_t extra_flags, hipStream_t stream) {
+                             int32_t extra_flags, hipStream_t stream, const void* warm,
+                             size_t warm_bytes) {
   LayoutArgs a;
   a.topk_idx = topk_idx;
   a.num_pairs = L.num_tokens * (int64_t)L.num_topk;
@@ -390,6 +446,12 @@ hipError_t launch_layout_ids(const int64_t* topk_idx, const ep_layout_t& L, void
   a.expert_offsets = L.expert_offsets;
   a.num_tokens_per_group = L.num_tokens_per_group;
   a.error_flags = L.error_flags;
+  const bool warming = warm != nullptr && warm_bytes >= 16 && warm_bytes <= kWarmMaxBytes;
+  a.warm = static_cast<const u32x4*>(warm);
+  a.warm_vecs = warming ? (int64_t)(warm_bytes / 16) : 0;
+  a.warm_split = a.warm_vecs * kWarmCountShare / 100;
+  a.warm_blocks = warming ? kWarmBlocks : 0;
+  a.never = 0;
 
   // Batches the fused decode kernel takes: its layout-only form, one workgroup
   // per token.
@@ -400,9 +462,9 @@ hipError_t launch_layout_ids(const int64_t* topk_idx, const ep_layout_t& L, void
     return hipGetLastError();
   }
   if (chunks > 0)
-    hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)chunks), dim3(kLayoutThreads), 0,
-                       stream, a);
-  hipLaunchKernelGGL(layout_finish_kernel, dim3((unsigned)(chunks > 0 ? chunks : 1)),
+    hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)(chunks + a.warm_blocks)),
+                       dim3(kLayoutThreads), 0, stream, a);
+  hipLaunchKernelGGL(layout_finish_kernel, dim3((unsigned)((chunks > 0 ? chunks : 1) + a.warm_blocks)),
                      dim3(kLayoutThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -70,11 +70,14 @@ enum ep_dtype {
     EP_F16 = 4            /* fp16 rows: x is fp16 and the rows are a bit copy of it */
 };
 
-/* Flag OR-ed into an FP8 receive dtype (EP_FP8_E4M3, EP_FP8_E4M3_POW2 or
- * EP_MXFP8_E4M3) of ep_dispatch / ep_layout_dispatch: the scales are stored
- * transposed (MN-major), see ep_dispatch. */
+/* Flags OR-ed into the receive dtype.
+ * EP_SCALES_MN_MAJOR: with an FP8 dtype (EP_FP8_E4M3, EP_FP8_E4M3_POW2 or
+ *   EP_MXFP8_E4M3) of ep_dispatch / ep_layout_dispatch, the scales are stored
+ *   transposed (MN-major), see ep_dispatch.
+ * EP_READ_X_AHEAD: ep_layout_dispatch only, any dtype; see that call. */
 enum ep_dtype_flag {
-    EP_SCALES_MN_MAJOR = 0x100
+    EP_SCALES_MN_MAJOR = 0x100,
+    EP_READ_X_AHEAD = 0x200
 };
 
 /* Bits of layout->error_flags, written by ep_get_layout. */
@@ -133,7 +136,10 @@ int ep_layout_init(ep_layout_t* layout, int64_t num_tokens, int32_t num_topk,
 int64_t ep_num_recv_rows(int64_t num_tokens, int32_t num_topk, int32_t num_experts,
                          int32_t capacity);
 
-/* Bytes of device workspace ep_get_layout needs for these sizes.  Host only. */
+/* Bytes of device workspace ep_get_layout needs for these sizes: per-chunk
+ * expert counts and flags, sized from the batch's tokens, top-k and experts as
+ * the pages size their buffers ([yololab] "ElasticBuffer": buffer capacity
+ * follows max tokens, top-k, hidden and EP degree).  Host only. */
 size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_experts);
 
 /*
@@ -179,7 +185,7 @@ int ep_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* work
  *                that section "FP8與低精度通訊" of [yololab] lists among the
  *                checks, for GEMMs that read a tile's row scales together).
  *                R is layout->num_recv_rows.  The flag with a non-FP8 dtype,
- *                or any other extra bit, is EP_ERR_DTYPE.
+ *                EP_READ_X_AHEAD, or any other extra bit, is EP_ERR_DTYPE.
  * recv_scales (fp32 or E8M0 rows) must be 4-byte aligned.
  * Rows that no slot names are left untouched.  hidden % 8 == 0.
  * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN, EP_ERR_DTYPE or EP_ERR_LAUNCH.
@@ -213,6 +219,15 @@ int ep_scales_to_mn_major(const void* scales, int64_t rows, int32_t hidden, int3
  * "高吞吐與低延遲工作負載"); larger batches run the two calls' kernels in turn.
  * Arguments, layouts and status codes are those of ep_get_layout and
  * ep_dispatch; the workspace is required in both cases.
+ * recv_dtype | EP_READ_X_AHEAD (larger batches whose x is at most 128 MiB;
+ * ignored otherwise): the two layout launches also read x with cached loads
+ * from extra workgroups, so that x sits in the last-level cache (the 256 MB
+ * MALL) when dispatch reads it.  The layout alone leaves HBM idle, and x
+ * read from HBM during dispatch competes with its row writes.  Results are
+ * unchanged.  It pays when x is not already cached (measured on MI355X at
+ * 8192 tokens x 7168: layout + dispatch 138 -> 127 us after the caches were
+ * emptied) and costs a few us when it is (111 -> 117 us when the router has
+ * just read x).  ep_dispatch and ep_get_layout reject the flag (EP_ERR_DTYPE).
  */
 int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
                        size_t workspace_bytes, const void* x, int32_t hidden, int32_t recv_dtype,

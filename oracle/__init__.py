@@ -205,6 +205,20 @@ def dispatch_fp8(x_bits: np.ndarray, slot_idx: np.ndarray, R: int):
     return q, s
 
 
+def dispatch_fp8_into(x_bits: np.ndarray, slot_idx: np.ndarray, q: np.ndarray,
+                      s: np.ndarray) -> None:
+    """dispatch_fp8 of the tokens in x_bits (a contiguous range of rows) with
+    their slot rows, written into the caller's receive arrays q [R,H] and
+    s [R,H/128].  Different token ranges write disjoint receive rows, so
+    ranges may run on separate threads (the C call releases the GIL)."""
+    assert x_bits.flags.c_contiguous and slot_idx.flags.c_contiguous
+    assert x_bits.dtype == np.uint16 and slot_idx.dtype == np.int32
+    assert q.flags.c_contiguous and s.flags.c_contiguous and q.dtype == np.uint8 and s.dtype == np.float32
+    T, H = x_bits.shape
+    assert slot_idx.shape[0] == T and q.shape[1] == H and s.shape == (q.shape[0], H // 128)
+    lib().ep_oracle_dispatch_fp8(_p(x_bits), T, slot_idx.shape[1], H, _p(slot_idx), _p(q), _p(s))
+
+
 def dequant_fp8(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
     q = _c(q, np.uint8)
     scales = _c(scales, np.float32)
@@ -224,6 +238,18 @@ def combine(y_bits: np.ndarray, w: np.ndarray, slot_idx: np.ndarray) -> np.ndarr
     out = np.empty((T, H), np.uint16)
     lib().ep_oracle_combine(_p(y_bits), _p(w), _p(slot_idx), T, k, H, _p(out))
     return out
+
+
+def combine_into(y_bits: np.ndarray, w: np.ndarray, slot_idx: np.ndarray, out: np.ndarray) -> None:
+    """combine of the tokens whose weight and slot rows are given (a
+    contiguous range), written into out (the same range of output rows); the
+    C call releases the GIL, so ranges may run on separate threads."""
+    for a, dt in ((y_bits, np.uint16), (w, np.float32), (slot_idx, np.int32), (out, np.uint16)):
+        assert a.flags.c_contiguous and a.dtype == dt
+    T, k = slot_idx.shape
+    H = y_bits.shape[1]
+    assert w.shape == (T, k) and out.shape == (T, H)
+    lib().ep_oracle_combine(_p(y_bits), _p(w), _p(slot_idx), T, k, H, _p(out))
 
 
 def combine_tokens(y_bits: np.ndarray, w: np.ndarray, slot_idx: np.ndarray, tokens) -> np.ndarray:

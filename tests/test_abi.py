@@ -217,6 +217,14 @@ def test_entry_points_reject_bad_arguments(L):
     assert L.ep_dispatch(fake, by(s), 256, mn | 3, fake, fake + 1, None) == -3
     assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake, 256, mn | 0, fake, None, None) == -6
     assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake, 256, mn | 1, fake, None, None) == -1
+    # the read-ahead flag: ep_layout_dispatch takes it with any dtype, ep_dispatch never
+    ra = binding.EP_READ_X_AHEAD
+    assert L.ep_dispatch(fake, by(s), 256, ra | 0, fake, None, None) == -6
+    assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake + 4, 256, ra | 0, fake, None, None) == -3
+    assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake + 4, 256, ra | mn | 1, fake, fake, None) == -3
+    assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake, 256, ra | mn | 0, fake, None, None) == -6
+    assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake, 256, ra | 5, fake, None, None) == -6
+    assert L.ep_layout_dispatch(fake, by(s), fake, ws_need, fake, 256, 0x400 | 1, fake, fake, None) == -6
     assert L.ep_combine_mxfp8(None, fake, fake, by(s), 256, fake, None) == -1
     assert L.ep_combine_mxfp8(fake, fake, fake, by(s), 200, fake, None) == -2   # hidden % 128
     assert L.ep_combine_mxfp8(fake + 8, fake, fake, by(s), 256, fake, None) == -3

@@ -512,3 +512,36 @@ def test_layout_dispatch_large_batch_takes_the_two_launch_path():
     assert (layout_to_host(lay)["slot_idx"] == ol["slot_idx"]).all()
     oq, os_ = oracle.dispatch_fp8(wl.x_bits, ol["slot_idx"], wl.R)
     assert (q.cpu().numpy() == oq).all() and (s.cpu().numpy().view(np.uint32) == os_.view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("name,T,H,fp8", [("dsv3", None, None, True), ("skewed", 1024, None, False),
+                                          ("dsv3", 300, 2048, True), ("lowlat", None, None, True),
+                                          ("large", None, None, True)])
+def test_layout_dispatch_read_x_ahead(name, T, H, fp8):
+    """EP_READ_X_AHEAD changes where x is read from, never the results: layout
+    and every receive row against the oracle.  (dsv3 and skewed take the
+    read-ahead; the decode batch and large's 512 MiB x ignore the flag.)"""
+    wl = W.make(name, T=T, H=H)
+    note("ep_layout_dispatch | EP_READ_X_AHEAD: %s T=%d H=%d fp8=%s" % (name, wl.T, wl.H, fp8))
+    lay = B.EpLayout(wl.T, wl.k, wl.E, wl.G, wl.cap)
+    R = lay.num_recv_rows
+    x = dev_bf16(wl.x_bits)
+    ti = torch.from_numpy(wl.topk_idx).cuda()
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap)
+    used = np.zeros(R, bool)
+    used[ol["slot_idx"][ol["slot_idx"] >= 0]] = True
+    if fp8:
+        q = torch.empty((R, wl.H), dtype=torch.uint8, device="cuda")
+        s = torch.empty((R, wl.H // 128), dtype=torch.float32, device="cuda")
+        B.ep_layout_dispatch(ti, lay, x, B.EP_FP8_E4M3 | B.EP_READ_X_AHEAD, q, s)
+        assert_layout_equal(layout_to_host(lay), dict(ol, recv_src=None), name)
+        oq, os_ = oracle.dispatch_fp8(wl.x_bits, ol["slot_idx"], R)
+        qh, sh = q.cpu().numpy(), s.cpu().numpy()
+        assert ((qh != oq).any(1) & used).sum() == 0
+        assert ((sh.view(np.uint32) != os_.view(np.uint32)).any(1) & used).sum() == 0
+    else:
+        q = torch.empty((R, wl.H), dtype=torch.bfloat16, device="cuda")
+        B.ep_layout_dispatch(ti, lay, x, B.EP_BF16 | B.EP_READ_X_AHEAD, q)
+        assert_layout_equal(layout_to_host(lay), dict(ol, recv_src=None), name)
+        orecv = oracle.dispatch_bf16(wl.x_bits, ol["slot_idx"], R)
+        assert ((host_bits(q) != orecv).any(1) & used).sum() == 0
