@@ -28,6 +28,7 @@ EP_FLAG_OVERFLOW = 2
 EP_MAX_EXPERTS = 1024
 EP_MAX_TOPK = 64
 EP_MAX_HIDDEN = 65536
+EP_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 class EpError(RuntimeError):
@@ -61,6 +62,7 @@ SIGNATURES = {
     "ep_num_recv_rows": (_i64, [_i64, _i32, _i32, _i32]),
     "ep_layout_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "ep_get_layout": (ctypes.c_int, [_vp, _LP, _vp, _sz, _vp]),
+    "ep_get_layout_noalloc": (ctypes.c_int, [_vp, _LP, _vp]),
     "ep_dispatch": (ctypes.c_int, [_vp, _LP, _i32, _i32, _vp, _vp, _vp]),
     "ep_layout_dispatch": (ctypes.c_int, [_vp, _LP, _vp, _sz, _vp, _i32, _i32, _vp, _vp, _vp]),
     "ep_scales_to_mn_major": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp]),
@@ -209,6 +211,17 @@ def ep_get_layout(topk_idx: torch.Tensor, layout: EpLayout, stream=None) -> EpLa
         _ptr(topk_idx, "topk_idx", torch.int64) if topk_idx.numel() else None,
         ctypes.byref(layout.struct), layout.workspace.data_ptr(), layout.workspace.numel(),
         _stream(stream)))
+    return layout
+
+
+def ep_get_layout_noalloc(topk_idx: torch.Tensor, layout: EpLayout, stream=None) -> EpLayout:
+    """ep_get_layout with the library's own fixed per-GPU workspace instead of
+    layout.workspace (for callers that cannot allocate at call time)."""
+    if tuple(topk_idx.shape) != (layout.num_tokens, layout.num_topk):
+        raise ValueError("topk_idx shape %s does not match the layout" % (tuple(topk_idx.shape),))
+    _check("ep_get_layout_noalloc", lib().ep_get_layout_noalloc(
+        _ptr(topk_idx, "topk_idx", torch.int64) if topk_idx.numel() else None,
+        ctypes.byref(layout.struct), _stream(stream)))
     return layout
 
 

@@ -3,6 +3,8 @@
 // caller's stream.  Nothing here allocates or synchronises.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "ep_internal.h"
 
 namespace {
@@ -62,6 +64,33 @@ int check_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* w
   return EP_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Layout workspace for ep_get_layout_noalloc: a fixed array in device memory,
+// one copy on every GPU the library runs on, held until the process ends.
+// Host code never uses the array's name as an address (on the host it is a
+// stand-in, not a device pointer): the first call on each device resolves
+// that device's copy with hipGetSymbolAddress and keeps the pointer.
+constexpr size_t kNoAllocScratchBytes = EP_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, or nullptr if it cannot be resolved.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // Checks shared by ep_dispatch and ep_layout_dispatch (after the layout's);
 // only the latter takes EP_READ_X_AHEAD.
 int check_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,
@@ -118,6 +147,16 @@ int ep_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* work
   if (rc != EP_OK) return rc;
   return launch_status(
       ep::launch_layout(topk_idx, *layout, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int ep_get_layout_noalloc(const int64_t* topk_idx, const ep_layout_t* layout, void* stream) {
+  int rc = check_layout_args(topk_idx, layout);
+  if (rc != EP_OK) return rc;
+  if (layout_workspace_need(*layout) > kNoAllocScratchBytes) return EP_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return EP_ERR_LAUNCH;
+  return launch_status(
+      ep::launch_layout(topk_idx, *layout, ws, static_cast<hipStream_t>(stream)));
 }
 
 int ep_dispatch(const void* x, const ep_layout_t* layout, int32_t hidden, int32_t recv_dtype,

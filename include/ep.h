@@ -29,7 +29,8 @@
  *   - Ownership: the caller allocates and frees all device memory (inputs,
  *     outputs, layout arrays, workspace).  The library allocates nothing and
  *     keeps no mutable global state; calls on different buffers may run
- *     concurrently.
+ *     concurrently.  The one exception is ep_get_layout_noalloc, whose
+ *     workspace is a fixed array the library holds on each GPU.
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  *     stream).  Calls only enqueue work and never synchronise; outputs and
  *     error flags are valid once the stream has been synchronised.
@@ -155,6 +156,25 @@ size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t n
  */
 int ep_get_layout(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/*
+ * ep_get_layout for callers that cannot allocate device memory at call time
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same results, with the workspace taken from a fixed array
+ * of EP_NOALLOC_SCRATCH_BYTES bytes that the library keeps in device memory,
+ * one copy per GPU, held until the process ends.  It runs on the current
+ * device (the one `stream` belongs to).  It allocates nothing: the first call
+ * on a device only looks up that device's copy of the array.  Sizes whose
+ * workspace (ep_layout_workspace_bytes) exceeds the array are rejected with
+ * EP_ERR_WORKSPACE before anything is enqueued.  Every call on a GPU uses
+ * that GPU's one array, which keeps the last call's contents (nothing in it
+ * needs to start at zero): calls that overlap on one GPU -- on two streams,
+ * or from two threads -- race and must be ordered by the caller.
+ * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_WORKSPACE or EP_ERR_LAUNCH
+ * (also when the device's array cannot be looked up).
+ */
+#define EP_NOALLOC_SCRATCH_BYTES (4u << 20)
+int ep_get_layout_noalloc(const int64_t* topk_idx, const ep_layout_t* layout, void* stream);
 
 /*
  * Dispatch ([yololab] stage table, dispatch row; [backyes] 五.2: one row
