@@ -212,12 +212,31 @@ static void launch_k(dim3 grid, dim3 block, hipStream_t stream, const void* y, c
                        hidden, m, static_cast<u32x4*>(out));
 }
 
+// Prefill-sized batches whose rows take a power-of-two number of lanes up to
+// 512 fill 1024-lane workgroups with 1024 / lanes tokens: fewer, larger
+// workgroups for the same lanes.  Measured on MI355X (bf16 rows, random
+// routing, one combine per event pair): hidden 4096, top-6, 65,536 tokens
+// 647-649 -> 624-631 us (654 -> 623 us inside the layout/dispatch/combine
+// step); hidden 4096, top-8, 16,384 tokens 206-208 -> 204 us; hidden 2048,
+// 131,072 tokens 851 -> 831 us; hidden 1024, 262,144 tokens 832-844 -> 829-831
+// us.  Partly filled workgroups (2 tokens of 256 lanes, 2 or 4 of 128)
+// measured slower than one token.  The FP8 combine
+// keeps one token per workgroup: its scalar slot and weight loads need a
+// uniform token.
+static void pack_prefill_tokens(const ep_layout_t& L, CombineMap& m) {
+  if (m.tokens_per_block == 1 && m.slices == 1 &&
+      L.num_tokens * (int64_t)L.num_topk > (int64_t)kDecodeCombinePairs &&
+      m.lanes_per_token <= 512 && 1024 % m.lanes_per_token == 0)
+    m.tokens_per_block = 1024 / m.lanes_per_token;
+}
+
 template <bool kUnit, bool kF16 = false>
 static hipError_t launch_combine_weights(const void* y, const float* w, const ep_layout_t& L,
                                          int32_t hidden, void* out, hipStream_t stream) {
   const int64_t T = L.num_tokens;
   if (T == 0) return hipSuccess;
-  const CombineMap m = combine_map(hidden / 8);
+  CombineMap m = combine_map(hidden / 8);
+  pack_prefill_tokens(L, m);
   const dim3 grid((unsigned)((T + m.tokens_per_block - 1) / m.tokens_per_block));
   const dim3 block(m.lanes_per_token * m.tokens_per_block);
   switch (L.num_topk) {

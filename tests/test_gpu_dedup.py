@@ -216,7 +216,9 @@ def test_dispatch_to_groups_full_size_sampled():
 @pytest.mark.parametrize("name,T,H,G", [("tiny", None, None, 4), ("dsv3", 256, None, None),
                                          ("lowlat", None, None, None), ("large", 512, None, None),
                                          ("dsv3", 40, 24, None), ("dsv3", 9, 16512, None),
-                                         ("large", 300, 4096, 64), ("skewed", 100, 7168, 1)])
+                                         ("large", 300, 4096, 64), ("skewed", 100, 7168, 1),
+                                         # prefill-sized, packed 1024-lane workgroups, ragged tail
+                                         ("large", 1001, 4096, None), ("dsv3", 1027, 2048, 8)])
 def test_combine_groups_random_rows(name, T, H, G):
     wl = W.make(name, T=T, H=H)
     G = G or wl.G

@@ -186,7 +186,9 @@ def test_dispatch_f16_is_a_bit_copy(name, T, H):
 @pytest.mark.parametrize("name,T,H,scale", [("tiny", None, None, 1.0), ("dsv3", 256, None, 1.0),
                                              ("large", 300, None, 100.0), ("lowlat", None, None, 1.0),
                                              ("dsv3", 40, 24, 1.0), ("dsv3", 9, 16512, 1.0),
-                                             ("skewed", 64, 7168, 2.0 ** -14)])
+                                             ("skewed", 64, 7168, 2.0 ** -14),
+                                             # prefill-sized, packed 1024-lane workgroups, ragged tail
+                                             ("large", 1001, None, 1.0), ("dsv3", 1029, 1024, 1.0)])
 def test_combine_f16_random_rows(name, T, H, scale):
     wl = W.make(name, T=T, H=H)
     lay = gpu_layout(wl.topk_idx, wl.E, wl.G, wl.cap)

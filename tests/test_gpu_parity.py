@@ -307,6 +307,12 @@ COMBINE_CASES = [
     ("dsv3", 33, 24),      # H % 16 != 0: 8-channel lanes
     ("dsv3", 21, 16400),   # row loops
     ("dsv3", 64, 128),     # several tokens per workgroup
+    # prefill-sized batches packed into 1024-lane workgroups, ragged last workgroup
+    ("large", 1001, None),  # 512 lanes per token: 2 tokens per workgroup
+    ("dsv3", 1027, 2048),  # 256 lanes: 4 per workgroup
+    ("dsv3", 1029, 1024),  # 128 lanes: 8 per workgroup
+    ("dsv3", 1100, 512),   # 64 lanes: 16 per workgroup
+    ("dsv3", 1030, 3072),  # 384 lanes: does not divide 1024, one token per workgroup
 ]
 
 
