@@ -55,8 +55,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["ep_combine.hip", "ep_dispatch.hip", "ep_dispatch_token.h", "ep_layout.hip",
-                  "ep_device.h", "ep_internal.h", "ep_aux.hip"]
+CSRC = os.path.join(ROOT, "combine_moe_layout_amd", "csrc")
 
 
 def ideal_bytes(T: int, H: int, E: int, G: int, k: int, R_used: int, fp8: bool,
@@ -102,10 +101,12 @@ def ideal_bytes_dedup(T: int, H: int, G: int, k: int, kg: int, used: int, fp8: b
 
 
 def sources_digest() -> str:
+    """Digest of every source of libep.so (kernels, launchers and the C ABI):
+    a committed profile counts only while this matches."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "combine_moe_layout_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -497,9 +498,7 @@ def main() -> int:
     # layout + dispatch through ep_layout_dispatch with EP_READ_X_AHEAD.  The
     # timed loop above is the steady state.
     flushed = None
-    x_bytes = x.numel() * x.element_size()
-    read_ahead_applies = (not (args.dedup or args.fused or args.mn_convert)
-                          and T * k > 4096 and x_bytes <= (128 << 20))
+    read_ahead_applies = not (args.dedup or args.fused or args.mn_convert) and T * k > 4096
     if graph is None and not args.no_flush:
         flush_buf = torch.zeros((512 << 20) // 8, dtype=torch.int64, device=dev)
         n_flush = min(args.steps, 50)

@@ -35,8 +35,8 @@ hipError_t launch_layout(const int64_t* topk_idx, const ep_layout_t& L, void* wo
 
 // The layout over an id table that another kernel wrote, which also left
 // extra_flags bad-id flag entries at layout_extra_flags(L, workspace).  With
-// warm != null (and warm_bytes at most kWarmMaxBytes), the two layout
-// launches also read warm_bytes of `warm` into the last-level cache from
+// warm != null, the two layout launches also read the first
+// min(warm_bytes, kWarmMaxBytes) of `warm` into the last-level cache from
 // kWarmBlocks extra workgroups each (kWarmCountShare percent during the count
 // launch, the rest during the finish launch).
 hipError_t launch_layout_ids(const int64_t* ids, const ep_layout_t& L, void* workspace,
@@ -51,8 +51,9 @@ int32_t* layout_extra_flags(const ep_layout_t& L, void* workspace);
 #endif
 constexpr int kWarmCountShare = EP_WARM_COUNT_SHARE;
 constexpr int kWarmBlocks = 256;
-// Half the MI355X MALL (256 MB): a larger source would evict itself before
-// dispatch reads it.
+// At most half the MI355X MALL (256 MB) is read ahead: more would evict
+// itself before dispatch reads it.  Of a larger source only the first part
+// is read ahead; dispatch reads tokens in order, so it meets that part first.
 constexpr size_t kWarmMaxBytes = (size_t)128 << 20;
 hipError_t launch_layout_warm(const int64_t* topk_idx, const ep_layout_t& L, void* workspace,
                               const void* warm, size_t warm_bytes, hipStream_t stream);

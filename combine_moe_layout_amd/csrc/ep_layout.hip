@@ -446,9 +446,11 @@ hipError_t launch_layout_ids(const int64_t* topk_idx, const ep_layout_t& L, void
   a.expert_offsets = L.expert_offsets;
   a.num_tokens_per_group = L.num_tokens_per_group;
   a.error_flags = L.error_flags;
-  const bool warming = warm != nullptr && warm_bytes >= 16 && warm_bytes <= kWarmMaxBytes;
+  // a larger source: its first kWarmMaxBytes, which dispatch reads first
+  const size_t warm_span = warm_bytes < kWarmMaxBytes ? warm_bytes : kWarmMaxBytes;
+  const bool warming = warm != nullptr && warm_span >= 16;
   a.warm = static_cast<const u32x4*>(warm);
-  a.warm_vecs = warming ? (int64_t)(warm_bytes / 16) : 0;
+  a.warm_vecs = warming ? (int64_t)(warm_span / 16) : 0;
   a.warm_split = a.warm_vecs * kWarmCountShare / 100;
   a.warm_blocks = warming ? kWarmBlocks : 0;
   a.never = 0;

@@ -239,15 +239,17 @@ int ep_scales_to_mn_major(const void* scales, int64_t rows, int32_t hidden, int3
  * "高吞吐與低延遲工作負載"); larger batches run the two calls' kernels in turn.
  * Arguments, layouts and status codes are those of ep_get_layout and
  * ep_dispatch; the workspace is required in both cases.
- * recv_dtype | EP_READ_X_AHEAD (larger batches whose x is at most 128 MiB;
- * ignored otherwise): the two layout launches also read x with cached loads
- * from extra workgroups, so that x sits in the last-level cache (the 256 MB
- * MALL) when dispatch reads it.  The layout alone leaves HBM idle, and x
- * read from HBM during dispatch competes with its row writes.  Results are
- * unchanged.  It pays when x is not already cached (measured on MI355X at
- * 8192 tokens x 7168: layout + dispatch 138 -> 127 us after the caches were
- * emptied) and costs a few us when it is (111 -> 117 us when the router has
- * just read x).  ep_dispatch and ep_get_layout reject the flag (EP_ERR_DTYPE).
+ * recv_dtype | EP_READ_X_AHEAD (batches larger than the one-launch size;
+ * ignored by decode-sized ones): the two layout launches also read x -- its
+ * first 128 MiB when it is larger -- with cached loads from extra workgroups,
+ * so that it sits in the last-level cache (the 256 MB MALL) when dispatch
+ * reads it.  The layout alone leaves HBM idle, and x read from HBM during
+ * dispatch competes with its row writes.  Results are unchanged.  It pays
+ * when x is not already cached (measured on MI355X at 8192 tokens x 7168:
+ * layout + dispatch 138 -> 127 us after the caches were emptied; 65,536
+ * tokens x 4096, whose x never fits: step 1050 -> 1045 us) and costs a few
+ * us when it is (111 -> 117 us when the router has just read x).
+ * ep_dispatch and ep_get_layout reject the flag (EP_ERR_DTYPE).
  */
 int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
                        size_t workspace_bytes, const void* x, int32_t hidden, int32_t recv_dtype,

@@ -525,8 +525,8 @@ def test_layout_dispatch_large_batch_takes_the_two_launch_path():
                                           ("large", None, None, True)])
 def test_layout_dispatch_read_x_ahead(name, T, H, fp8):
     """EP_READ_X_AHEAD changes where x is read from, never the results: layout
-    and every receive row against the oracle.  (dsv3 and skewed take the
-    read-ahead; the decode batch and large's 512 MiB x ignore the flag.)"""
+    and every receive row against the oracle.  (dsv3 and skewed read all of x
+    ahead, large its first 128 MiB; the decode batch ignores the flag.)"""
     wl = W.make(name, T=T, H=H)
     note("ep_layout_dispatch | EP_READ_X_AHEAD: %s T=%d H=%d fp8=%s" % (name, wl.T, wl.H, fp8))
     lay = B.EpLayout(wl.T, wl.k, wl.E, wl.G, wl.cap)
