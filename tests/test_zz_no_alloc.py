@@ -83,3 +83,40 @@ def test_noalloc_refuses_sizes_beyond_its_array():
     lay.num_tokens_per_expert = lay.expert_offsets = lay.num_tokens_per_group = fake
     lay.slot_idx = lay.error_flags = fake
     assert B.lib().ep_get_layout_noalloc(fake, ctypes.byref(lay), None) == -4
+
+
+def test_noalloc_layout_under_graph_capture():
+    """Recorded in a HIP graph (the allocation-free entry point's first use
+    case) and replayed several times, with eager calls on other inputs
+    between the replays: every replay equals ep_get_layout on the recorded
+    input.  The array's address is looked up by the eager calls before the
+    capture; the recording only holds kernel launches."""
+    wl = W.make("dsv3")
+    T, k = wl.T, wl.k
+    ti = torch.from_numpy(wl.topk_idx).cuda()
+    ref = B.EpLayout(T, k, wl.E, wl.G, 0)
+    B.ep_get_layout(ti, ref)
+    want = _arrays(ref)
+    lay = B.EpLayout(T, k, wl.E, wl.G, 0)
+    B.ep_get_layout_noalloc(ti, lay)  # eager first call on this device
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            B.ep_get_layout_noalloc(ti, lay)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(9)
+    for rep in range(4):
+        lay.slot_idx.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _arrays(lay)
+        for key in want:
+            assert (got[key] == want[key]).all(), (rep, key)
+        # eager calls on another input overwrite the shared array between replays
+        other = g.integers(-1, 64, (3000, 6)).astype(np.int64)
+        _both(other, 64, 8, 0)
+    note("noalloc under graph capture: 4 replays equal to ep_get_layout")
