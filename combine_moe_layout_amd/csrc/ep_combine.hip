@@ -374,13 +374,47 @@ __global__ __launch_bounds__(1024) void combine_fp8_kernel(
   }
 }
 
+// FP8 rows of prefill-sized batches wider than four waves are split into
+// slices of whole waves, one workgroup each: slices of 4, 3 or 2 waves when
+// one of these divides the row's waves (the widest that does), else 2-wave
+// slices with a last slice of one wave.  Measured on MI355X (top-8, random
+// routing, 8192 tokens unless noted; one token per workgroup -> split, both
+// on one box): hidden 7168 (14 waves, 7 x 2) 116-121 -> 101-102 us, MXFP8
+// 115-121 -> 103-104 us, top-6 90-92 -> 80-82 us, 600 tokens 13.6 -> 12.0
+// us; 6656 (13 waves, 2 x 6 + 1) 109-114 -> 93-94 us; 8192 (4 x 4) 125-130
+// -> 111-112 us; 8704 (17 waves) 141-156 -> 119-121 us; 16384 at 4096 tokens
+// (8 x 4) 119-125 -> 111-112 us; 6144 (3 x 4) 90-93 -> 87-88 us; 5120
+// (5 x 2) 81-84 -> 73-74 us; 4608 (3 x 3) 74-77 -> 67-68 us; ragged 7296
+// (912 vectors, 5 x 3) 124 -> 106 us; 2560 (2 + 2 + 1) 40.4-41.2 -> 39.3-39.5
+// us; 3200 (7 waves) 51-53 us either way; 4096 at 65,536 tokens, top-6
+// (2 x 4) 337-346 us either way.  Every split gave output identical to the
+// unsplit launch.  Slices of 4 waves over a 5-wave row (one full, one a
+// quarter full) measured slower (46.8 us), as did a 256-lane target that
+// leaves a partly filled last slice at 7168 (104 us).  The bf16 combine reads
+// twice the bytes per vector and measured slower split (182 -> 187-194 us at
+// hidden 7168), so it keeps whole rows.
+static void split_prefill_rows(int32_t vecs, int64_t T, CombineMap& m, dim3& grid, dim3& block) {
+  const int32_t waves = (vecs + 63) / 64;
+  if (waves <= 4) return;
+  const int32_t w = waves % 4 == 0 ? 4 : (waves % 3 == 0 ? 3 : 2);
+  const int64_t S = (waves + w - 1) / w;
+  if (T * S * 64 * w > (int64_t)INT32_MAX) return;  // work items must fit the 32-bit grid size
+  m.lanes_per_token = 64 * w;
+  m.slices = (int32_t)S;
+  grid = dim3((unsigned)(T * S));
+  block = dim3((unsigned)(64 * w));
+}
+
 template <int K, bool kMx>
 static void launch_fp8_k(dim3 grid, dim3 block, hipStream_t stream, const uint8_t* q,
                          const void* scales, const float* w, const ep_layout_t& L,
                          int32_t hidden, CombineMap m, void* out) {
-  if (m.tokens_per_block == 1 &&
-      L.num_tokens * (int64_t)L.num_topk <= (int64_t)kDecodeCombinePairs)
-    split_tokens(hidden / 8, L.num_tokens, m, grid, block);
+  if (m.tokens_per_block == 1) {
+    if (L.num_tokens * (int64_t)L.num_topk <= (int64_t)kDecodeCombinePairs)
+      split_tokens(hidden / 8, L.num_tokens, m, grid, block);
+    else
+      split_prefill_rows(hidden / 8, L.num_tokens, m, grid, block);
+  }
   if (m.tokens_per_block == 1)
     hipLaunchKernelGGL((combine_fp8_kernel<K, true, kMx>), grid, block, 0, stream, q, scales, w,
                        L.slot_idx, L.num_tokens, L.num_topk, hidden, m, static_cast<u32x4*>(out));

@@ -51,6 +51,26 @@ def test_combine_mxfp8_random_outputs(name, T, H):
                       oracle.combine_mxfp8(q, sc, wl.topk_weights, ol["slot_idx"]), "combine_mxfp8 %s" % name)
 
 
+@pytest.mark.parametrize("name,T,H", [("dsv3", 600, 7168), ("dsv3", 520, 4608), ("dsv3", 520, 7296),
+                                       ("dsv3", 520, 3200), ("dsv3", 513, 16512), ("large", 700, None)])
+def test_combine_mxfp8_prefill_widths(name, T, H):
+    """Prefill-sized batches (more than 4096 pairs) at widths whose rows are
+    split over several workgroups per token in different ways (whole, ragged
+    and partly filled slices).  Codes with the sign bit clear and softmax
+    weights, so that no sum cancels below the tolerance's reach."""
+    wl = W.make(name, T=T, H=H)
+    assert wl.T * wl.k > 4096 and (wl.topk_weights >= 0).all()
+    note("combine_mxfp8 prefill %s T=%d H=%d k=%d" % (name, wl.T, wl.H, wl.k))
+    q, sc = _random_mx_rows(wl.R, wl.H, seed=13)
+    q &= 0x7F
+    q[q == 0x7F] = 0x38
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap)
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, wl.cap, with_src=False)
+    assert_close_bf16(_combine_mx_gpu(q, sc, wl.topk_weights, lay, wl.H),
+                      oracle.combine_mxfp8(q, sc, wl.topk_weights, ol["slot_idx"]),
+                      "combine_mxfp8 prefill %s H=%d" % (name, wl.H))
+
+
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 9])
 def test_combine_mxfp8_other_topk(k):
     """The compile-time top-k sizes and the generic path (k = 3, 5, 9), with

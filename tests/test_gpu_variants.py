@@ -117,6 +117,43 @@ def test_combine_fp8_random_outputs(name, T, H):
                       "combine_fp8 %s" % name)
 
 
+# Prefill-sized batches (more than 4096 (token, k) pairs) at widths whose rows
+# are split over several workgroups per token in different ways: 14 waves
+# (7 x 128 lanes), 10 (5 x 128), 9 (3 x 192), 15 ragged (912 vectors), 7 (a
+# partly filled second slice), 32 (8 x 256), 33 (11 x 192), top-6 rows of 8
+# waves, and the generic top-k path.
+PREFILL_FP8_CASES = [("dsv3", 600, 7168), ("dsv3", 520, 5120), ("dsv3", 520, 4608),
+                     ("dsv3", 520, 7296), ("dsv3", 520, 3200), ("dsv3", 520, 16384),
+                     ("dsv3", 513, 16512), ("large", 700, None), ("k3", 1500, 7168)]
+
+
+def _prefill_workload(name, T, H):
+    if name == "k3":
+        return W.custom(T=T, H=H, E=32, k=3, G=4, seed=5)
+    return W.make(name, T=T, H=H)
+
+
+@pytest.mark.parametrize("name,T,H", PREFILL_FP8_CASES)
+def test_combine_fp8_prefill_widths(name, T, H):
+    """Codes with the sign bit clear and softmax weights: no sum cancels, so
+    the tolerance relative to the result bounds the fp32 accumulation (random
+    signs with scales up to 2^4 make a few of these millions of sums cancel
+    to ~1e-3 from terms near 1e4, where any fp32 sum differs from the fp64
+    one by more than 8e-3 of the result).  Any element read from the wrong
+    row, block or offset is off by far more."""
+    wl = _prefill_workload(name, T, H)
+    assert wl.T * wl.k > 4096 and (wl.topk_weights >= 0).all()
+    note("combine_fp8 prefill %s T=%d H=%d k=%d" % (name, wl.T, wl.H, wl.k))
+    q, sc = _random_fp8_rows(wl.R, wl.H, seed=11)
+    q &= 0x7F
+    q[q == 0x7F] = 0x38
+    ol = oracle.layout(wl.topk_idx, wl.E, wl.G, wl.cap)
+    lay = gpu_layout(wl.topk_idx, wl.E, wl.G, wl.cap, with_src=False)
+    assert_close_bf16(_combine_fp8_gpu(q, sc, wl.topk_weights, lay, wl.H),
+                      oracle.combine_fp8(q, sc, wl.topk_weights, ol["slot_idx"]),
+                      "combine_fp8 prefill %s H=%d" % (name, wl.H))
+
+
 @pytest.mark.parametrize("k", [3, 9])
 def test_combine_fp8_other_topk(k):
     wl = W.custom(T=120, H=512, E=32, k=k, G=4, seed=k)
