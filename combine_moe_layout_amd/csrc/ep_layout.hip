@@ -19,10 +19,10 @@
 //      deterministic.  The chunk's per-expert totals go to the workspace.
 //   phase 2 (finish): each workgroup sums the chunk totals of earlier chunks
 //      (its base inside each expert) and of all chunks (the expert totals),
-//      staging the whole count matrix in LDS with every load in flight at once
-//      when it fits, scans the totals into expert offsets and writes the
-//      receive rows of its chunk.  Workgroup 0 also writes the counts,
-//      offsets, group totals and error flags.
+//      a few lanes of one wave per expert, scans the totals into expert
+//      offsets with one DPP sum per wave and writes the receive rows of its
+//      chunk.  Workgroup 0 also writes the counts, offsets, group totals and
+//      error flags, before its receive rows.
 // Two launches run the phases; the ranks travel from one to the other through
 // slot_idx, packed as (rank in chunk) << kExpertBits | expert.  An input of
 // one chunk (up to kChunkPairs pairs: decode batches) runs both phases in a
@@ -33,19 +33,18 @@
 
 namespace ep {
 
-// Per-chunk counts up to this many ints are staged whole in LDS (all loads in
-// flight at once); larger matrices are summed from memory.
-constexpr int kStageInts = 16384;
-static_assert(kStageInts % (4 * kLayoutThreads) == 0, "staging is done in whole 16-byte batches");
-static_assert(kStageInts >= kLayoutWaves * EP_MAX_EXPERTS,
-              "phase-1 histograms alias the staging area");
+static_assert(EP_MAX_EXPERTS <= kLayoutThreads, "phase 2 gives every expert a lane");
 
-struct LayoutShared {
-  int32_t counts[kStageInts];  // phase 2; phase 1 uses the front as kLayoutWaves histograms
+// Phase 2's LDS: per-expert totals, bases inside the expert (chunks before
+// this one), offsets and the exclusive prefix of the totals; per-wave sums
+// and flags.
+struct ScanShared {
   int32_t tot[EP_MAX_EXPERTS];
   int32_t pre[EP_MAX_EXPERTS];
   int32_t off[EP_MAX_EXPERTS];
+  int32_t pfx[EP_MAX_EXPERTS + 1];  // exclusive prefix of tot, then the grand total
   int32_t wave[kLayoutWaves];
+  int32_t wflag[kLayoutWaves];
 };
 
 size_t layout_workspace_bytes(int64_t pairs, int32_t num_experts, int64_t extra_flags) {
@@ -63,10 +62,12 @@ __device__ __forceinline__ int64_t pair_of(int64_t c, int i) {
 // Phase 1 for chunk c: eid[i] = expert of item i (-1 if none), local[i] = its
 // rank among the chunk's pairs of that expert.  Writes the chunk's totals and
 // its bad-id flag (and, if tot_out is not null, the totals to that LDS array
-// too); returns the flag.  Ends with the histograms no longer needed.
+// too); returns the flag.  wave_flags is kLayoutWaves ints of LDS.  On return
+// other waves may still read the histograms and wave_flags: a caller that
+// reuses that LDS passes a barrier first.
 __device__ __forceinline__ int count_chunk(const int64_t* __restrict__ topk_idx,
                                            int64_t num_pairs, int32_t E, int32_t expert_bits,
-                                           int64_t c, int32_t* hist,
+                                           int64_t c, int32_t* hist, int32_t* wave_flags,
                                            int32_t* __restrict__ chunk_count,
                                            int32_t* __restrict__ chunk_flags, int32_t* tot_out,
                                            int32_t (&eid)[kLayoutItems],
@@ -88,6 +89,9 @@ __device__ __forceinline__ int count_chunk(const int64_t* __restrict__ topk_idx,
     bad |= !ok && v != -1;
     eid[i] = ok ? (int32_t)v : -1;
   }
+  // the wave's bad-id flag, read by every thread after the barrier below
+  const bool wave_bad = __ballot(bad) != 0;
+  if (lane == 0) wave_flags[wave] = wave_bad ? 1 : 0;
 
   const uint64_t below_me = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
@@ -120,170 +124,172 @@ __device__ __forceinline__ int count_chunk(const int64_t* __restrict__ topk_idx,
     chunk_count[c * E + e] = run;
     if (tot_out != nullptr) tot_out[e] = run;
   }
-  const int any_bad = __syncthreads_or(bad ? 1 : 0);
+  int any_bad = 0;
+#pragma unroll
+  for (int w = 0; w < kLayoutWaves; ++w) any_bad |= wave_flags[w];
   if (threadIdx.x == 0) chunk_flags[c] = any_bad ? EP_FLAG_BAD_EXPERT : 0;
+  __syncthreads();  // the rows now hold each wave's exclusive prefix
 #pragma unroll
   for (int i = 0; i < kLayoutItems; ++i)
     if (eid[i] >= 0) local[i] += my_hist[eid[i]];
-  __syncthreads();
   return any_bad ? EP_FLAG_BAD_EXPERT : 0;
 }
 
-// Expert totals over all chunks (sh.tot) and over the chunks before chunk c
-// (sh.pre), from the per-chunk totals in memory.
-__device__ __forceinline__ void chunk_totals(int32_t E, int32_t num_chunks, int64_t c,
-                                             const int32_t* __restrict__ chunk_count,
-                                             LayoutShared& sh) {
+// Inclusive sum over the 64 lanes of a wave with DPP moves (no LDS): four
+// shifts inside each row of 16 lanes, then row 0's and row 2's last lanes
+// into rows 1 and 3, then lane 31 into rows 2 and 3.  Every lane of the wave
+// must be active.
+__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t x) {
+  const int row_lane = threadIdx.x & 15;
+  const int row = (threadIdx.x & 63) >> 4;
+  int32_t t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  if (row_lane >= 1) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  if (row_lane >= 2) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  if (row_lane >= 4) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  if (row_lane >= 8) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  if (row & 1) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  if (row >= 2) x += t;
+  return x;
+}
+
+// Expert totals over all chunks (sh.tot), over the chunks before chunk c
+// (sh.pre), their exclusive prefix (sh.pfx, with the grand total at [E]) and
+// the expert offsets (sh.off).  Expert e owns lpe consecutive lanes of one
+// wave (lpe a power of two, lpe * E <= kLayoutThreads); each sums every
+// lpe-th chunk's count of e straight from memory.  One inclusive sum over the
+// wave's lanes then gives each expert's total (the difference across its
+// lanes) and the totals of the wave's earlier experts; the waves' sums and
+// flag bits meet in LDS across one barrier.  kSingleChunk: the totals are
+// already in sh.tot (visible to every thread) and no chunk comes before.
+// Returns the workgroup's flag bits (EP_FLAG_BAD_EXPERT if any thread's
+// flag_bits is set, EP_FLAG_OVERFLOW if a padded expert overflows) and sets
+// total to the number of routed pairs.
+template <bool kSingleChunk>
+__device__ __forceinline__ int32_t expert_scan(int32_t E, int32_t capacity, int32_t num_chunks,
+                                               int64_t c, const int32_t* __restrict__ chunk_count,
+                                               ScanShared& sh, int32_t flag_bits, int32_t& total) {
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kLayoutThreads) {
-    sh.tot[e] = 0;
-    sh.pre[e] = 0;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  int lpe = kWave;
+  while (lpe > 1 && lpe * E > kLayoutThreads) lpe >>= 1;
+  const int e = tid / lpe;
+  const int sub = tid % lpe;
+  const bool serves = e < E;
+  int32_t tot = 0, pre = 0;
+  if constexpr (kSingleChunk) {
+    if (serves && sub == 0) tot = sh.tot[e];
+  } else if (serves) {
+#pragma unroll 8
+    for (int cc = sub; cc < num_chunks; cc += lpe) {
+      const int32_t v = chunk_count[(int64_t)cc * E + e];
+      tot += v;
+      pre += cc < c ? v : 0;
+    }
   }
-  const int64_t matrix = (int64_t)num_chunks * E;
-  const int lanes_per_expert = E >= kLayoutThreads ? 1 : kLayoutThreads / E;
-  const int span = E >= kLayoutThreads ? E : E * lanes_per_expert;
-  if (matrix <= kStageInts) {
-    // 16-byte loads, a fixed number per thread, all issued before the first
-    // is waited for (the workspace is 256-byte aligned)
-    constexpr int kBatch = kStageInts / 4 / kLayoutThreads;
-    const int n4 = (int)(matrix / 4);
-    const int4* src4 = reinterpret_cast<const int4*>(chunk_count);
-    int4* dst4 = reinterpret_cast<int4*>(sh.counts);
-    if (n4 > 0) {
-      int4 r[kBatch];
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        const int i = tid + b * kLayoutThreads;
-        r[b] = src4[i < n4 ? i : n4 - 1];  // unconditional, so r stays in registers
-      }
-      // Only whole quads of the matrix are stored here.  Quad n4 holds the
-      // last matrix % 4 entries, which the loop below fills from other
-      // lanes; a store of the clamped copy to that quad from another wave
-      // would race with it.
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        const int i = tid + b * kLayoutThreads;
-        if (i < n4) dst4[i] = r[b];
-      }
-    }
-    for (int i = 4 * n4 + tid; i < matrix; i += kLayoutThreads) sh.counts[i] = chunk_count[i];
-    __syncthreads();
-    for (int idx = tid; idx < span; idx += kLayoutThreads) {
-      const int e = idx % E;
-      const int sub = idx / E;
-      int32_t tot = 0, pre = 0;
-      for (int cc = sub; cc < num_chunks; cc += lanes_per_expert) {
-        const int32_t v = sh.counts[cc * E + e];
-        tot += v;
-        pre += cc < c ? v : 0;
-      }
-      atomicAdd(&sh.tot[e], tot);
-      atomicAdd(&sh.pre[e], pre);
-    }
-  } else {
-    __syncthreads();
-    for (int idx = tid; idx < span; idx += kLayoutThreads) {
-      const int e = idx % E;
-      const int sub = idx / E;
-      int32_t tot = 0, pre = 0;
-#pragma unroll 16
-      for (int cc = sub; cc < num_chunks; cc += lanes_per_expert) {
-        const int32_t v = chunk_count[(int64_t)cc * E + e];
-        tot += v;
-        pre += cc < c ? v : 0;
-      }
-      atomicAdd(&sh.tot[e], tot);
-      atomicAdd(&sh.pre[e], pre);
-    }
+  const int32_t inc_tot = wave_inclusive_sum(tot);
+  const int32_t inc_pre = wave_inclusive_sum(pre);
+  const int first = lane - sub;  // this expert's first lane in the wave
+  const int last = first + lpe - 1;
+  const int32_t tot_below = __shfl(inc_tot, first > 0 ? first - 1 : 0);
+  const int32_t pre_below = __shfl(inc_pre, first > 0 ? first - 1 : 0);
+  const int32_t tot_end = __shfl(inc_tot, last);
+  const int32_t pre_end = __shfl(inc_pre, last);
+  const int32_t excl = first > 0 ? tot_below : 0;  // the wave's experts before e
+  const int32_t e_tot = tot_end - excl;
+  const int32_t e_pre = pre_end - (first > 0 ? pre_below : 0);
+  const bool over = serves && sub == 0 && capacity > 0 && e_tot > capacity;
+  const bool wave_bad = __ballot(flag_bits != 0) != 0;
+  const bool wave_over = __ballot(over) != 0;
+  const int32_t wave_sum = __builtin_amdgcn_readlane(inc_tot, kWave - 1);
+  if (lane == 0) {
+    sh.wave[wave] = wave_sum;
+    sh.wflag[wave] = (wave_bad ? EP_FLAG_BAD_EXPERT : 0) | (wave_over ? EP_FLAG_OVERFLOW : 0);
   }
   __syncthreads();
+  int32_t before = 0, flags = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kLayoutWaves; ++w) {
+    before += w < wave ? sh.wave[w] : 0;
+    total += sh.wave[w];
+    flags |= sh.wflag[w];
+  }
+  if (serves && sub == 0) {
+    const int32_t run = before + excl;
+    sh.tot[e] = e_tot;
+    sh.pre[e] = e_pre;
+    sh.pfx[e] = run;
+    sh.off[e] = capacity > 0 ? e * capacity : run;
+  }
+  if (tid == 0) sh.pfx[E] = total;
+  __syncthreads();
+  return flags;
 }
 
 // Phase 2 for chunk c, given every chunk's totals in memory.  kSingleChunk:
-// there is only this chunk, and sh.tot and sh.pre are already set by the
-// caller.  For c == 0, flag_bits is the OR of this thread's share of the flag
+// there is only this chunk, and sh.tot is already set by the caller.  For c == 0, flag_bits is the OR of this thread's share of the flag
 // entries (one per chunk, then any written by a kernel that prepared the ids),
 // which the caller loads at its start so that their latency is hidden.
+// Workgroup 0 writes the counts, offsets, group totals and flags as soon as
+// the scan is done, before the receive rows, so that no store waits on
+// another: the group totals are differences of the exclusive prefix, and the
+// flags travel through one word per wave across the scan's own barrier.
 template <bool kSingleChunk>
 __device__ __forceinline__ void finish_chunk(
     int64_t num_pairs, int32_t E, int32_t num_groups, int32_t capacity, int32_t num_chunks,
-    int64_t c, const int32_t* __restrict__ chunk_count, LayoutShared& sh,
+    int64_t c, const int32_t* __restrict__ chunk_count, ScanShared& sh,
     const int32_t (&eid)[kLayoutItems], const int32_t (&local)[kLayoutItems],
     int32_t* __restrict__ slot_idx, int32_t* __restrict__ recv_src,
     int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ num_tokens_per_group, int32_t* __restrict__ error_flags,
     int32_t flag_bits) {
   const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = tid / kWave;
 
-  // 1. expert totals over all chunks, and over the chunks before this one
-  if constexpr (!kSingleChunk) chunk_totals(E, num_chunks, c, chunk_count, sh);
+  // 1-2. expert totals, bases inside each expert, offsets, flags
+  int32_t total;
+  const int32_t flags =
+      expert_scan<kSingleChunk>(E, capacity, num_chunks, c, chunk_count, sh, flag_bits, total);
 
-  // 2. exclusive scan of the totals (contiguous mode) -> expert offsets
-  const int per = (E + kLayoutThreads - 1) / kLayoutThreads;
-  const int first = tid * per;
-  int32_t mine = 0;
-  for (int i = 0; i < per; ++i)
-    if (first + i < E) mine += sh.tot[first + i];
-  int32_t incl = mine;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int32_t n = __shfl_up(incl, d);
-    if (lane >= d) incl += n;
+  // 3. metadata, once
+  if (c == 0) {
+    for (int e = tid; e < E; e += kLayoutThreads) {
+      num_tokens_per_expert[e] = sh.tot[e];
+      expert_offsets[e] = sh.off[e];
+    }
+    if (tid == 0) {
+      expert_offsets[E] = capacity > 0 ? E * capacity : total;
+      error_flags[0] = flags;
+    }
+    const int per_group = E / num_groups;
+    for (int g = tid; g < num_groups; g += kLayoutThreads)
+      num_tokens_per_group[g] = sh.pfx[(g + 1) * per_group] - sh.pfx[g * per_group];
   }
-  if (lane == kWave - 1) sh.wave[wave] = incl;
-  __syncthreads();
-  int32_t before = 0, total = 0;
+
+  // 4. receive rows of this chunk's pairs: every row first, then the stores
+  int32_t slot[kLayoutItems];
 #pragma unroll
-  for (int w = 0; w < kLayoutWaves; ++w) {
-    before += w < wave ? sh.wave[w] : 0;
-    total += sh.wave[w];
-  }
-  int32_t run = before + incl - mine;
-  for (int i = 0; i < per; ++i) {
-    if (first + i < E) {
-      sh.off[first + i] = capacity > 0 ? (first + i) * capacity : run;
-      run += sh.tot[first + i];
+  for (int i = 0; i < kLayoutItems; ++i) {
+    slot[i] = -1;
+    const int e = eid[i];
+    if (e >= 0) {
+      const int32_t r = sh.pre[e] + local[i];  // rank inside expert e
+      if (capacity == 0 || r < capacity) slot[i] = sh.off[e] + r;
     }
   }
-  __syncthreads();
-
-  // 3. receive rows of this chunk's pairs
 #pragma unroll
   for (int i = 0; i < kLayoutItems; ++i) {
     const int64_t p = pair_of(c, i);
     if (p < num_pairs) {
-      int32_t s = -1;
-      const int e = eid[i];
-      if (e >= 0) {
-        const int32_t r = sh.pre[e] + local[i];  // rank inside expert e
-        if (capacity == 0 || r < capacity) s = sh.off[e] + r;
-      }
-      slot_idx[p] = s;
-      if (recv_src != nullptr && s >= 0) recv_src[s] = (int32_t)p;
+      slot_idx[p] = slot[i];
+      if (recv_src != nullptr && slot[i] >= 0) recv_src[slot[i]] = (int32_t)p;
     }
-  }
-
-  // 4. metadata, once
-  if (c == 0) {
-    bool over = false;
-    for (int e = tid; e < E; e += kLayoutThreads) {
-      num_tokens_per_expert[e] = sh.tot[e];
-      expert_offsets[e] = sh.off[e];
-      over |= capacity > 0 && sh.tot[e] > capacity;
-    }
-    if (tid == 0) expert_offsets[E] = capacity > 0 ? E * capacity : total;
-    const int per_group = E / num_groups;
-    for (int g = tid; g < num_groups; g += kLayoutThreads) {
-      int32_t s = 0;
-      for (int e = g * per_group; e < (g + 1) * per_group; ++e) s += sh.tot[e];
-      num_tokens_per_group[g] = s;
-    }
-    const int any_bad = __syncthreads_or(flag_bits);
-    const int any_over = __syncthreads_or(over ? 1 : 0);
-    if (tid == 0)
-      error_flags[0] = (any_bad ? EP_FLAG_BAD_EXPERT : 0) | (any_over ? EP_FLAG_OVERFLOW : 0);
   }
 }
 
@@ -343,13 +349,14 @@ __device__ __noinline__ void warm_slab(const u32x4* __restrict__ src, int64_t be
 // Phase 1: ranks leave packed through slot_idx.
 __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(LayoutArgs a) {
   __shared__ int32_t hist[kLayoutWaves * EP_MAX_EXPERTS];
+  __shared__ int32_t wave_flags[kLayoutWaves];
   if ((int32_t)blockIdx.x >= a.num_chunks) {
     warm_slab(a.warm, 0, a.warm_split, (int32_t)blockIdx.x - a.num_chunks, a.warm_blocks);
     return;
   }
   int32_t eid[kLayoutItems], local[kLayoutItems];
   count_chunk(a.topk_idx, a.num_pairs, a.num_experts, a.expert_bits, blockIdx.x, hist,
-              a.chunk_count, a.chunk_flags, nullptr, eid, local);
+              wave_flags, a.chunk_count, a.chunk_flags, nullptr, eid, local);
 #pragma unroll
   for (int i = 0; i < kLayoutItems; ++i) {
     const int64_t p = pair_of(blockIdx.x, i);
@@ -368,7 +375,7 @@ __device__ __forceinline__ int32_t load_flag_bits(const int32_t* __restrict__ ch
 
 // Phase 2 (also the whole layout when there are no pairs).
 __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(LayoutArgs a) {
-  __shared__ LayoutShared sh;
+  __shared__ ScanShared sh;
   const int32_t own = a.num_chunks > 0 ? a.num_chunks : 1;
   if ((int32_t)blockIdx.x >= own) {
     warm_slab(a.warm, a.warm_split, a.warm_vecs, (int32_t)blockIdx.x - own, a.warm_blocks);
@@ -393,14 +400,15 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(LayoutArg
 // Inputs of at most one chunk (decode-sized batches): both phases in one
 // workgroup and one launch; the totals stay in LDS.
 __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(LayoutArgs a) {
-  __shared__ LayoutShared sh;
+  __shared__ int32_t hist[kLayoutWaves * EP_MAX_EXPERTS];
+  __shared__ int32_t wave_flags[kLayoutWaves];
+  __shared__ ScanShared sh;
   int32_t eid[kLayoutItems], local[kLayoutItems];
   // entries after the chunk's own (written by a kernel that prepared the ids)
   const int32_t extra_bits = load_flag_bits(a.chunk_flags, 1, a.num_flags);
-  const int bad = count_chunk(a.topk_idx, a.num_pairs, a.num_experts, a.expert_bits, 0,
-                              sh.counts, a.chunk_count, a.chunk_flags, sh.tot, eid, local);
-  for (int e = threadIdx.x; e < a.num_experts; e += kLayoutThreads) sh.pre[e] = 0;
-  __syncthreads();
+  const int bad = count_chunk(a.topk_idx, a.num_pairs, a.num_experts, a.expert_bits, 0, hist,
+                              wave_flags, a.chunk_count, a.chunk_flags, sh.tot, eid, local);
+  __syncthreads();  // the totals in sh.tot, for every thread
   finish_chunk<true>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, 1, 0, a.chunk_count,
                      sh, eid, local, a.slot_idx, a.recv_src, a.num_tokens_per_expert,
                      a.expert_offsets, a.num_tokens_per_group, a.error_flags, bad | extra_bits);
