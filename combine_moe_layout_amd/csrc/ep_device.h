@@ -23,6 +23,29 @@ typedef uint32_t u32x4_vec __attribute__((ext_vector_type(4)));
 // cache lines (64 lanes x 16 or 8 contiguous bytes: 1 KiB or 512 B): a
 // non-temporal access does not keep the line, so a second instruction reading
 // the other half of a line would fetch it again.
+// Inclusive sum over the 64 lanes of a wave with DPP moves (no LDS): four
+// shifts inside each row of 16 lanes, then row 0's and row 2's last lanes
+// into rows 1 and 3, then lane 31 into rows 2 and 3.  Every lane of the wave
+// must be active.
+__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t x) {
+  const int row_lane = threadIdx.x & 15;
+  const int row = (threadIdx.x & 63) >> 4;
+  int32_t t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  if (row_lane >= 1) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  if (row_lane >= 2) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  if (row_lane >= 4) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  if (row_lane >= 8) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  if (row & 1) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  if (row >= 2) x += t;
+  return x;
+}
+
 __device__ __forceinline__ u32x4 load_nt(const u32x4* p) {
   const u32x4_vec v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_vec*>(p));
   return u32x4{v.x, v.y, v.z, v.w};

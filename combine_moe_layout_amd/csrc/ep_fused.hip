@@ -60,6 +60,7 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
   __shared__ int32_t s_pre[EP_MAX_EXPERTS];
   __shared__ int32_t s_off[EP_MAX_EXPERTS];
   __shared__ int32_t s_wave[1024 / kWave];
+  __shared__ int32_t s_flags;  // the metadata workgroup's error flags
   __shared__ uint32_t s_scale[kMaxScalesPerBlock];
   const int tid = threadIdx.x;
   const int E = a.num_experts, k = a.k;
@@ -107,6 +108,7 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
     s_hist[e] = 0;
     s_pre[e] = 0;
   }
+  if (tid == 0) s_flags = 0;
   __syncthreads();
   bool bad = false;
 #pragma unroll
@@ -126,27 +128,30 @@ __global__ __launch_bounds__(1024) void layout_dispatch_small_kernel(FusedArgs a
   __syncthreads();
 
   if (!token_block) {
-    // metadata: counts, offsets, group totals, flags
-    const int32_t total = block_exclusive_scan(s_hist, s_off, E, s_wave);
+    // metadata: counts, offsets, group totals (differences of the exclusive
+    // prefix), flags (one LDS OR per wave, ordered by the scan's barriers)
     bool over = false;
+    for (int e = tid; e < E; e += blockDim.x) over |= a.capacity > 0 && s_hist[e] > a.capacity;
+    bad |= (extra_bits & EP_FLAG_BAD_EXPERT) != 0;
+    over |= (extra_bits & EP_FLAG_OVERFLOW) != 0;
+    const bool wave_bad = __ballot(bad) != 0;
+    const bool wave_over = __ballot(over) != 0;
+    if (tid % kWave == 0 && (wave_bad || wave_over))
+      atomicOr(&s_flags, (wave_bad ? EP_FLAG_BAD_EXPERT : 0) | (wave_over ? EP_FLAG_OVERFLOW : 0));
+    const int32_t total = block_exclusive_scan(s_hist, s_off, E, s_wave);
     for (int e = tid; e < E; e += blockDim.x) {
       a.num_tokens_per_expert[e] = s_hist[e];
       a.expert_offsets[e] = a.capacity > 0 ? e * a.capacity : s_off[e];
-      over |= a.capacity > 0 && s_hist[e] > a.capacity;
     }
-    if (tid == 0) a.expert_offsets[E] = a.capacity > 0 ? E * a.capacity : total;
+    if (tid == 0) {
+      a.expert_offsets[E] = a.capacity > 0 ? E * a.capacity : total;
+      a.error_flags[0] = s_flags;
+    }
     const int per_group = E / a.num_groups;
     for (int g = tid; g < a.num_groups; g += blockDim.x) {
-      int32_t s = 0;
-      for (int e = g * per_group; e < (g + 1) * per_group; ++e) s += s_hist[e];
-      a.num_tokens_per_group[g] = s;
+      const int32_t end = g + 1 == a.num_groups ? total : s_off[(g + 1) * per_group];
+      a.num_tokens_per_group[g] = end - s_off[g * per_group];
     }
-    bad |= (extra_bits & EP_FLAG_BAD_EXPERT) != 0;
-    over |= (extra_bits & EP_FLAG_OVERFLOW) != 0;
-    const int any_bad = __syncthreads_or(bad ? 1 : 0);
-    const int any_over = __syncthreads_or(over ? 1 : 0);
-    if (tid == 0)
-      a.error_flags[0] = (any_bad ? EP_FLAG_BAD_EXPERT : 0) | (any_over ? EP_FLAG_OVERFLOW : 0);
     return;
   }
 

@@ -178,6 +178,7 @@ __global__ __launch_bounds__(kGroupSmallLanes) void group_layout_small_kernel(Gr
   __shared__ int32_t s_pre[EP_MAX_EXPERTS];
   __shared__ int32_t s_off[EP_MAX_EXPERTS];
   __shared__ int32_t s_wave[kGroupSmallLanes / kWave];
+  __shared__ int32_t s_bad;  // the metadata workgroup's bad-id flag
   __shared__ int32_t s_ent[kFusedMaxTopk];   // this token's entries: groups ascending, then -1
   __shared__ int32_t s_row[kFusedMaxTopk];   // their receive rows
   const int tid = threadIdx.x;
@@ -197,6 +198,7 @@ __global__ __launch_bounds__(kGroupSmallLanes) void group_layout_small_kernel(Gr
     s_hist[g] = 0;
     s_pre[g] = 0;
   }
+  if (tid == 0) s_bad = 0;
   bool bad = false;
 #pragma unroll
   for (int i = 0; i < kGroupSmallTrips; ++i) {
@@ -228,6 +230,10 @@ __global__ __launch_bounds__(kGroupSmallLanes) void group_layout_small_kernel(Gr
       }
     }
   }
+  // the bad-id flag: one LDS write per wave (the ballot with every lane
+  // active), ordered by the scan's barriers
+  const bool wave_bad = __ballot(bad) != 0;
+  if (!token_block && tid % kWave == 0 && wave_bad) s_bad = 1;
   __syncthreads();
   const int32_t total = block_exclusive_scan(s_hist, s_off, G, s_wave);
 
@@ -237,9 +243,10 @@ __global__ __launch_bounds__(kGroupSmallLanes) void group_layout_small_kernel(Gr
       a.expert_offsets[g] = s_off[g];
       a.num_tokens_per_group[g] = s_hist[g];  // the group layout's groups are its experts
     }
-    if (tid == 0) a.expert_offsets[G] = total;
-    const int any_bad = __syncthreads_or(bad ? 1 : 0);
-    if (tid == 0) a.error_flags[0] = any_bad ? EP_FLAG_BAD_EXPERT : 0;
+    if (tid == 0) {
+      a.expert_offsets[G] = total;
+      a.error_flags[0] = s_bad ? EP_FLAG_BAD_EXPERT : 0;
+    }
     return;
   }
 

@@ -135,29 +135,6 @@ __device__ __forceinline__ int count_chunk(const int64_t* __restrict__ topk_idx,
   return any_bad ? EP_FLAG_BAD_EXPERT : 0;
 }
 
-// Inclusive sum over the 64 lanes of a wave with DPP moves (no LDS): four
-// shifts inside each row of 16 lanes, then row 0's and row 2's last lanes
-// into rows 1 and 3, then lane 31 into rows 2 and 3.  Every lane of the wave
-// must be active.
-__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t x) {
-  const int row_lane = threadIdx.x & 15;
-  const int row = (threadIdx.x & 63) >> 4;
-  int32_t t;
-  t = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  if (row_lane >= 1) x += t;
-  t = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  if (row_lane >= 2) x += t;
-  t = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  if (row_lane >= 4) x += t;
-  t = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  if (row_lane >= 8) x += t;
-  t = __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  if (row & 1) x += t;
-  t = __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  if (row >= 2) x += t;
-  return x;
-}
-
 // Expert totals over all chunks (sh.tot), over the chunks before chunk c
 // (sh.pre), their exclusive prefix (sh.pfx, with the grand total at [E]) and
 // the expert offsets (sh.off).  Expert e owns lpe consecutive lanes of one

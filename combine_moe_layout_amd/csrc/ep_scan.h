@@ -6,7 +6,8 @@
 namespace ep {
 
 // Exclusive scan of n <= EP_MAX_EXPERTS values in LDS (in place into out),
-// returning the total; every thread of the block calls it.
+// returning the total; every thread of the block calls it (the block is whole
+// waves).  Its two barriers also order any LDS writes made before the call.
 __device__ __forceinline__ int32_t block_exclusive_scan(const int32_t* in, int32_t* out, int n,
                                                       int32_t* s_wave) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -16,12 +17,7 @@ __device__ __forceinline__ int32_t block_exclusive_scan(const int32_t* in, int32
   int32_t mine = 0;
   for (int i = 0; i < per; ++i)
     if (first + i < n) mine += in[first + i];
-  int32_t incl = mine;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int32_t v = __shfl_up(incl, d);
-    if (lane >= d) incl += v;
-  }
+  const int32_t incl = wave_inclusive_sum(mine);
   if (lane == kWave - 1) s_wave[wave] = incl;
   __syncthreads();
   int32_t before = 0, total = 0;
