@@ -19,9 +19,9 @@
 //      deterministic.  The chunk's per-expert totals go to the workspace.
 //   phase 2 (finish): each workgroup sums the chunk totals of earlier chunks
 //      (its base inside each expert) and of all chunks (the expert totals),
-//      a few lanes of one wave per expert, scans the totals into expert
-//      offsets with one DPP sum per wave and writes the receive rows of its
-//      chunk.  Workgroup 0 also writes the counts, offsets, group totals and
+//      up to kScanParts lanes per expert with each wave's loads on whole rows
+//      of the counts, scans the totals into expert offsets with one DPP sum
+//      per wave and writes the receive rows of its chunk.  Workgroup 0 also writes the counts, offsets, group totals and
 //      error flags, before its receive rows.
 // Two launches run the phases; the ranks travel from one to the other through
 // slot_idx, packed as (rank in chunk) << kExpertBits | expert.  An input of
@@ -35,9 +35,15 @@ namespace ep {
 
 static_assert(EP_MAX_EXPERTS <= kLayoutThreads, "phase 2 gives every expert a lane");
 
+// Phase 2 splits the chunks among up to kScanParts lanes per expert, and each
+// such lane has up to kScanLoads of its counts in flight at once (64 parts of
+// 16 chunks: two million pairs).
+constexpr int kScanParts = 64;
+constexpr int kScanLoads = 16;
+
 // Phase 2's LDS: per-expert totals, bases inside the expert (chunks before
 // this one), offsets and the exclusive prefix of the totals; per-wave sums
-// and flags.
+// and flags; the parts' partial sums, [part][expert].
 struct ScanShared {
   int32_t tot[EP_MAX_EXPERTS];
   int32_t pre[EP_MAX_EXPERTS];
@@ -45,6 +51,8 @@ struct ScanShared {
   int32_t pfx[EP_MAX_EXPERTS + 1];  // exclusive prefix of tot, then the grand total
   int32_t wave[kLayoutWaves];
   int32_t wflag[kLayoutWaves];
+  int32_t part_tot[kLayoutThreads];
+  int32_t part_pre[kLayoutThreads];
 };
 
 size_t layout_workspace_bytes(int64_t pairs, int32_t num_experts, int64_t extra_flags) {
@@ -60,9 +68,9 @@ __device__ __forceinline__ int64_t pair_of(int64_t c, int i) {
 }
 
 // Phase 1 for chunk c: eid[i] = expert of item i (-1 if none), local[i] = its
-// rank among the chunk's pairs of that expert.  Writes the chunk's totals and
-// its bad-id flag (and, if tot_out is not null, the totals to that LDS array
-// too); returns the flag.  wave_flags is kLayoutWaves ints of LDS.  On return
+// rank among the chunk's pairs of that expert.  Writes the chunk's totals (to
+// chunk_count[c * E + e]) and its bad-id flag (and, if tot_out is not null,
+// the totals to that LDS array too); returns the flag.  wave_flags is kLayoutWaves ints of LDS.  On return
 // other waves may still read the histograms and wave_flags: a caller that
 // reuses that LDS passes a barrier first.
 __device__ __forceinline__ int count_chunk(const int64_t* __restrict__ topk_idx,
@@ -137,11 +145,11 @@ __device__ __forceinline__ int count_chunk(const int64_t* __restrict__ topk_idx,
 
 // Expert totals over all chunks (sh.tot), over the chunks before chunk c
 // (sh.pre), their exclusive prefix (sh.pfx, with the grand total at [E]) and
-// the expert offsets (sh.off).  Expert e owns lpe consecutive lanes of one
-// wave (lpe a power of two, lpe * E <= kLayoutThreads); each sums every
-// lpe-th chunk's count of e straight from memory.  One inclusive sum over the
-// wave's lanes then gives each expert's total (the difference across its
-// lanes) and the totals of the wave's earlier experts; the waves' sums and
+// the expert offsets (sh.off).  Lane (part, e) with e fastest sums every
+// parts-th chunk's count of expert e straight from memory (so a wave's loads
+// cover whole rows of the chunk-major counts) into LDS; lane e then adds its
+// expert's parts, and one inclusive DPP sum per wave over those totals gives
+// each expert the totals of the wave's earlier experts.  The waves' sums and
 // flag bits meet in LDS across one barrier.  kSingleChunk: the totals are
 // already in sh.tot (visible to every thread) and no chunk comes before.
 // Returns the workgroup's flag bits (EP_FLAG_BAD_EXPERT if any thread's
@@ -154,37 +162,52 @@ __device__ __forceinline__ int32_t expert_scan(int32_t E, int32_t capacity, int3
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
-  int lpe = kWave;
-  while (lpe > 1 && lpe * E > kLayoutThreads) lpe >>= 1;
-  const int e = tid / lpe;
-  const int sub = tid % lpe;
-  const bool serves = e < E;
+  const bool serves = tid < E;  // lane e = tid of the scan
   int32_t tot = 0, pre = 0;
   if constexpr (kSingleChunk) {
-    if (serves && sub == 0) tot = sh.tot[e];
-  } else if (serves) {
-#pragma unroll 8
-    for (int cc = sub; cc < num_chunks; cc += lpe) {
-      const int32_t v = chunk_count[(int64_t)cc * E + e];
-      tot += v;
-      pre += cc < c ? v : 0;
+    if (serves) tot = sh.tot[tid];
+  } else {
+    int parts = kLayoutThreads / E;
+    if (parts > kScanParts) parts = kScanParts;
+    const int part = tid / E;
+    const int e = tid - part * E;
+    if (part < parts) {
+      // the first kScanLoads of the part's chunks with every load in flight
+      // at once (a fixed trip count), then any further ones
+      int32_t v[kScanLoads];
+#pragma unroll
+      for (int i = 0; i < kScanLoads; ++i) {
+        const int cc = part + i * parts;
+        v[i] = cc < num_chunks ? chunk_count[(int64_t)cc * E + e] : 0;
+      }
+      int32_t pt = 0, pp = 0;
+#pragma unroll
+      for (int i = 0; i < kScanLoads; ++i) {
+        pt += v[i];
+        pp += part + i * parts < c ? v[i] : 0;
+      }
+      for (int cc = part + kScanLoads * parts; cc < num_chunks; cc += parts) {
+        const int32_t w = chunk_count[(int64_t)cc * E + e];
+        pt += w;
+        pp += cc < c ? w : 0;
+      }
+      sh.part_tot[part * E + e] = pt;
+      sh.part_pre[part * E + e] = pp;
+    }
+    __syncthreads();
+    if (serves) {
+      for (int q = 0; q < parts; ++q) {
+        tot += sh.part_tot[q * E + tid];
+        pre += sh.part_pre[q * E + tid];
+      }
     }
   }
-  const int32_t inc_tot = wave_inclusive_sum(tot);
-  const int32_t inc_pre = wave_inclusive_sum(pre);
-  const int first = lane - sub;  // this expert's first lane in the wave
-  const int last = first + lpe - 1;
-  const int32_t tot_below = __shfl(inc_tot, first > 0 ? first - 1 : 0);
-  const int32_t pre_below = __shfl(inc_pre, first > 0 ? first - 1 : 0);
-  const int32_t tot_end = __shfl(inc_tot, last);
-  const int32_t pre_end = __shfl(inc_pre, last);
-  const int32_t excl = first > 0 ? tot_below : 0;  // the wave's experts before e
-  const int32_t e_tot = tot_end - excl;
-  const int32_t e_pre = pre_end - (first > 0 ? pre_below : 0);
-  const bool over = serves && sub == 0 && capacity > 0 && e_tot > capacity;
+  const int32_t incl = wave_inclusive_sum(tot);
+  const int32_t excl = incl - tot;  // the wave's experts before this one
+  const bool over = serves && capacity > 0 && tot > capacity;
   const bool wave_bad = __ballot(flag_bits != 0) != 0;
   const bool wave_over = __ballot(over) != 0;
-  const int32_t wave_sum = __builtin_amdgcn_readlane(inc_tot, kWave - 1);
+  const int32_t wave_sum = __builtin_amdgcn_readlane(incl, kWave - 1);
   if (lane == 0) {
     sh.wave[wave] = wave_sum;
     sh.wflag[wave] = (wave_bad ? EP_FLAG_BAD_EXPERT : 0) | (wave_over ? EP_FLAG_OVERFLOW : 0);
@@ -198,12 +221,12 @@ __device__ __forceinline__ int32_t expert_scan(int32_t E, int32_t capacity, int3
     total += sh.wave[w];
     flags |= sh.wflag[w];
   }
-  if (serves && sub == 0) {
+  if (serves) {
     const int32_t run = before + excl;
-    sh.tot[e] = e_tot;
-    sh.pre[e] = e_pre;
-    sh.pfx[e] = run;
-    sh.off[e] = capacity > 0 ? e * capacity : run;
+    sh.tot[tid] = tot;
+    sh.pre[tid] = pre;
+    sh.pfx[tid] = run;
+    sh.off[tid] = capacity > 0 ? tid * capacity : run;
   }
   if (tid == 0) sh.pfx[E] = total;
   __syncthreads();
