@@ -246,9 +246,10 @@ int ep_scales_to_mn_major(const void* scales, int64_t rows, int32_t hidden, int3
  * reads it.  The layout alone leaves HBM idle, and x read from HBM during
  * dispatch competes with its row writes.  Results are unchanged.  It pays
  * when x is not already cached (measured on MI355X at 8192 tokens x 7168:
- * layout + dispatch 138 -> 127 us after the caches were emptied; 65,536
- * tokens x 4096, whose x never fits: step 1050 -> 1045 us) and costs a few
- * us when it is (111 -> 117 us when the router has just read x).
+ * the layout + dispatch kernels 130 -> 123 us and the step 309 -> 302 us
+ * after the caches were emptied; 65,536 tokens x 4096, whose x never fits:
+ * step 1044 -> 1041 us) and costs about 12 us when it is (step 279 -> 291
+ * us when the router has just read x).
  * ep_dispatch and ep_get_layout reject the flag (EP_ERR_DTYPE).
  */
 int ep_layout_dispatch(const int64_t* topk_idx, const ep_layout_t* layout, void* workspace,
