@@ -161,8 +161,8 @@ def _edge_layouts():
         # one layout chunk with top-k 9: the single-workgroup layout
         ("one chunk: k=9", g.integers(0, 64, (200, 9)), 64, 8, 0),
         # two-launch path with a count matrix (chunks x E) that is not a
-        # multiple of 4 and whose last quad is staged by a different wave than
-        # the one that fills its tail entries
+        # multiple of 4, odd expert counts (parts of lanes per expert that do
+        # not fill the workgroup) and many chunks per part
         ("E=253, 3 chunks, matrix 759", g.integers(0, 253, (700, 8)), 253, 11, 0),
         ("E=255, k=9, 3 chunks, matrix 765", g.integers(-1, 255, (600, 9)), 255, 5, 0),
         ("E=1, 259 chunks, matrix 259", np.zeros((530000, 1), np.int64), 1, 1, 0),
