@@ -197,13 +197,22 @@ def cpu_baseline(wl) -> dict:
 
 
 def cpu_model() -> str:
+    """/proc/cpuinfo's model name of the first CPU, with its family, model and
+    stepping numbers (a virtual machine may show only the vendor's brand)."""
+    fields = {}
     try:
         for ln in open("/proc/cpuinfo"):
-            if ln.startswith("model name"):
-                return ln.split(":", 1)[1].strip()
+            if not ln.strip():
+                break
+            key, _, val = ln.partition(":")
+            fields.setdefault(key.strip(), val.strip())
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = [(k, fields[k]) for k in ("cpu family", "model", "stepping") if k in fields]
+    if ids:
+        name += " (%s)" % ", ".join("%s %s" % kv for kv in ids)
+    return name
 
 
 def main() -> int:
