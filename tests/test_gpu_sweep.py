@@ -76,6 +76,20 @@ def test_random_configuration(seed):
         else:
             assert (sh[used].view(np.uint32) == os_[used].view(np.uint32)).all(), "scales"
         y_bits = oracle.dequant_mxfp8(oq, os_) if mx else oracle.dequant_fp8(oq, os_)
+        # the combine of FP8 expert outputs, both sides on the oracle's
+        # dispatched codes and scales (a token's rows are copies of it and the
+        # weights are positive, so no sum cancels)
+        out8 = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        w = torch.from_numpy(wl.topk_weights).cuda()
+        q8, s8 = torch.from_numpy(oq).cuda(), torch.from_numpy(os_).cuda()
+        if mx:
+            B.ep_combine_mxfp8(q8, s8, w, lay, out8)
+            ref8 = oracle.combine_mxfp8(oq, os_, wl.topk_weights, ol["slot_idx"])
+        else:
+            B.ep_combine_fp8(q8, s8, w, lay, out8)
+            ref8 = oracle.combine_fp8(oq, os_, wl.topk_weights, ol["slot_idx"])
+        torch.cuda.synchronize()
+        assert_close_bf16(host_bits(out8), ref8, "sweep %d FP8 combine" % seed)
 
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     B.ep_combine(dev_bf16(y_bits), torch.from_numpy(wl.topk_weights).cuda(), lay, out)
