@@ -14,9 +14,12 @@
 // FP8 expert outputs (ep_combine_fp8).
 //
 // How: HBM-bound (k row reads and one row write per token, each read once).
-// One workgroup per token (rows shorter than a wave share a workgroup), one
-// lane per 16-byte vector (8 channels) of the row, so every wave instruction
-// covers 1 KiB of one row and the rows can be read with the non-temporal hint.
+// One workgroup per token by default, one lane per 16-byte vector (8
+// channels) of the row, so every wave instruction covers 1 KiB of one row and
+// the rows can be read with the non-temporal hint.  Short rows share a
+// workgroup (rows shorter than a wave; at prefill size, rows of 128 to 512
+// lanes), and a token's row is split over several workgroups in decode-sized
+// batches and, for FP8 rows wider than four waves, at prefill size.
 // The k rows of a lane are loaded before any arithmetic (the top-k is a
 // template parameter for the common sizes, so all k loads are in flight
 // together), then accumulated with fp32 fma.  A pair without a receive row is
@@ -220,9 +223,9 @@ static void launch_k(dim3 grid, dim3 block, hipStream_t stream, const void* y, c
 // step); hidden 4096, top-8, 16,384 tokens 206-208 -> 204 us; hidden 2048,
 // 131,072 tokens 851 -> 831 us; hidden 1024, 262,144 tokens 832-844 -> 829-831
 // us.  Partly filled workgroups (2 tokens of 256 lanes, 2 or 4 of 128)
-// measured slower than one token.  The FP8 combine
-// keeps one token per workgroup: its scalar slot and weight loads need a
-// uniform token.
+// measured slower than one token.  The FP8 combine keeps a uniform token per
+// workgroup (its scalar slot and weight loads need one) and splits wide rows
+// over several workgroups instead (split_prefill_rows).
 static void pack_prefill_tokens(const ep_layout_t& L, CombineMap& m) {
   if (m.tokens_per_block == 1 && m.slices == 1 &&
       L.num_tokens * (int64_t)L.num_topk > (int64_t)kDecodeCombinePairs &&
@@ -276,10 +279,11 @@ hipError_t launch_combine_f16(const void* y, const float* w, const ep_layout_t& 
 // and accumulates w * scale * value in fp32; the 8 bf16 results leave as one
 // 16-byte non-temporal store (a wave writes 1 KiB of the output row).  Eight
 // channels per lane measured about 9% faster than sixteen, whose two 16-byte
-// output stores per lane each cover only half of every cache line.  When one
-// workgroup holds one token, the token index is uniform and its slots and
-// weights come in through scalar loads before the row loads: about 10% faster
-// than per-lane loads for this kernel (112 vs 124 us at 8192 x 7168, top-8).
+// output stores per lane each cover only half of every cache line.  When a
+// workgroup holds one token (or one slice of one token's row), the token index
+// is uniform and its slots and weights come in through scalar loads before the
+// row loads: about 10% faster than per-lane loads for this kernel (112 vs 124
+// us at 8192 x 7168, top-8, one workgroup per token).
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 

@@ -21,8 +21,9 @@
 //      (its base inside each expert) and of all chunks (the expert totals),
 //      up to kScanParts lanes per expert with each wave's loads on whole rows
 //      of the counts, scans the totals into expert offsets with one DPP sum
-//      per wave and writes the receive rows of its chunk.  Workgroup 0 also writes the counts, offsets, group totals and
-//      error flags, before its receive rows.
+//      per wave and writes the receive rows of its chunk.  Workgroup 0 also
+//      writes the counts, offsets, group totals and error flags, before its
+//      receive rows.
 // Two launches run the phases; the ranks travel from one to the other through
 // slot_idx, packed as (rank in chunk) << kExpertBits | expert.  An input of
 // one chunk (up to kChunkPairs pairs: decode batches) runs both phases in a
@@ -70,9 +71,10 @@ __device__ __forceinline__ int64_t pair_of(int64_t c, int i) {
 // Phase 1 for chunk c: eid[i] = expert of item i (-1 if none), local[i] = its
 // rank among the chunk's pairs of that expert.  Writes the chunk's totals (to
 // chunk_count[c * E + e]) and its bad-id flag (and, if tot_out is not null,
-// the totals to that LDS array too); returns the flag.  wave_flags is kLayoutWaves ints of LDS.  On return
-// other waves may still read the histograms and wave_flags: a caller that
-// reuses that LDS passes a barrier first.
+// the totals to that LDS array too); returns the flag.  wave_flags is
+// kLayoutWaves ints of LDS.  On return other waves may still read the
+// histograms and wave_flags: a caller that reuses that LDS passes a barrier
+// first.
 __device__ __forceinline__ int count_chunk(const int64_t* __restrict__ topk_idx,
                                            int64_t num_pairs, int32_t E, int32_t expert_bits,
                                            int64_t c, int32_t* hist, int32_t* wave_flags,
@@ -234,9 +236,10 @@ __device__ __forceinline__ int32_t expert_scan(int32_t E, int32_t capacity, int3
 }
 
 // Phase 2 for chunk c, given every chunk's totals in memory.  kSingleChunk:
-// there is only this chunk, and sh.tot is already set by the caller.  For c == 0, flag_bits is the OR of this thread's share of the flag
-// entries (one per chunk, then any written by a kernel that prepared the ids),
-// which the caller loads at its start so that their latency is hidden.
+// there is only this chunk, and sh.tot is already set by the caller.  For
+// c == 0, flag_bits is the OR of this thread's share of the flag entries (one
+// per chunk, then any written by a kernel that prepared the ids), which the
+// caller loads at its start so that their latency is hidden.
 // Workgroup 0 writes the counts, offsets, group totals and flags as soon as
 // the scan is done, before the receive rows, so that no store waits on
 // another: the group totals are differences of the exclusive prefix, and the
@@ -471,8 +474,8 @@ hipError_t launch_layout_ids(const int64_t* topk_idx, const ep_layout_t& L, void
   if (chunks > 0)
     hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)(chunks + a.warm_blocks)),
                        dim3(kLayoutThreads), 0, stream, a);
-  hipLaunchKernelGGL(layout_finish_kernel, dim3((unsigned)((chunks > 0 ? chunks : 1) + a.warm_blocks)),
-                     dim3(kLayoutThreads), 0, stream, a);
+  const unsigned finish_blocks = (unsigned)((chunks > 0 ? chunks : 1) + a.warm_blocks);
+  hipLaunchKernelGGL(layout_finish_kernel, dim3(finish_blocks), dim3(kLayoutThreads), 0, stream, a);
   return hipGetLastError();
 }
 
