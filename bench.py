@@ -27,8 +27,10 @@ latency-bound layout runs), for the workloads where that applies.
 `roofline` is the dominant kernel's (combine): algorithmic bytes per launch
 over the mean HIP-event time of its launches, beside the committed rocprofv3
 kernel-trace mean and HBM traffic when they were taken on the current kernel
-sources.  `cpu_baseline` is the oracle on this host's cores, single-threaded
-and with the tokens split across the cores.
+sources; `kernel_us_profile` then gives that trace's time of every kernel of
+the step (no event cost) and dispatch + combine over those times.
+`cpu_baseline` is the oracle on this host's cores, single-threaded and with
+the tokens split across the cores.
 
 `--workload` times the other named workloads (tiny, skewed, lowlat, large) the
 same way; the default is the configuration the metric is quoted on.  Variant
@@ -665,6 +667,17 @@ def main() -> int:
             roof["profile_launch_us"] = t_c
             roof["profile_frac"] = round(nbytes["combine"] / (t_c * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
             roof["profile"] = "profiles/%s_kernel_trace.md" % name
+            # every kernel of the step as the committed trace timed it, and
+            # dispatch + combine over those times
+            avg = trace["avg_us"]
+            layout_us = sum(v for kk, v in avg.items() if kk.startswith("layout"))
+            result["kernel_us_profile"] = {"layout": round(layout_us, 2),
+                                           "dispatch": avg.get("dispatch"), "combine": t_c,
+                                           "source": roof["profile"]}
+            if "dispatch" in avg:
+                dc_p = (nbytes["dispatch"] + nbytes["combine"]) / ((avg["dispatch"] + t_c) * 1e-6) / 1e9
+                result["kernel_us_profile"]["dispatch_plus_combine_pct_peak"] = round(
+                    100 * dc_p / HBM_PEAK_GBPS, 2)
         result["roofline"] = roof
     else:
         result["config"]["step"] += " (HIP graph replay, %d steps per graph)" % gs
