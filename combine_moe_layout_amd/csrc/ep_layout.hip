@@ -24,8 +24,10 @@
 //      per wave and writes the receive rows of its chunk.  Workgroup 0 also
 //      writes the counts, offsets, group totals and error flags, before its
 //      receive rows.
-// Two launches run the phases; the ranks travel from one to the other through
-// slot_idx, packed as (rank in chunk) << kExpertBits | expert.  An input of
+// Two launches run the phases (three for inputs with many chunks, whose bases
+// one launch in between computes once, layout_bases_kernel); the ranks travel
+// from phase 1 to phase 2 through slot_idx, packed as (rank in chunk) <<
+// kExpertBits | expert.  An input of
 // one chunk (up to kChunkPairs pairs: decode batches) runs both phases in a
 // single workgroup and launch.  (A single cooperative launch with a grid
 // barrier was measured slower on MI355X than the two ordinary launches.)
@@ -37,10 +39,23 @@ namespace ep {
 static_assert(EP_MAX_EXPERTS <= kLayoutThreads, "phase 2 gives every expert a lane");
 
 // Phase 2 splits the chunks among up to kScanParts lanes per expert, and each
-// such lane has up to kScanLoads of its counts in flight at once (64 parts of
-// 16 chunks: two million pairs).
+// such lane reads its counts kScanLoads at a time, all of a batch in flight at
+// once (one batch covers 16 chunks per part: 64 of them at 256 experts).
 constexpr int kScanParts = 64;
 constexpr int kScanLoads = 16;
+
+// Where phase 2 finds each expert's totals: already in LDS (an input of one
+// chunk), summed from the per-chunk counts by every workgroup, or read from
+// the bases one extra launch computed once (inputs whose count matrix every
+// workgroup would otherwise re-read at great length).
+enum ScanSource { kTotalsInLds = 0, kSumCounts = 1, kReadBases = 2 };
+
+// The extra launch is taken when chunks * chunks * E, the per-chunk counts
+// all the finish workgroups would read, exceeds this.
+#ifndef EP_LAYOUT_BASES_MIN
+#define EP_LAYOUT_BASES_MIN (8 << 20)
+#endif
+constexpr int64_t kBasesMinWork = EP_LAYOUT_BASES_MIN;
 
 // Phase 2's LDS: per-expert totals, bases inside the expert (chunks before
 // this one), offsets and the exclusive prefix of the totals; per-wave sums
@@ -58,7 +73,9 @@ struct ScanShared {
 
 size_t layout_workspace_bytes(int64_t pairs, int32_t num_experts, int64_t extra_flags) {
   int64_t chunks = layout_num_chunks(pairs);
-  size_t bytes = (size_t)(chunks * num_experts + chunks + extra_flags) * sizeof(int32_t);
+  // per-chunk counts, per-chunk flags, extra flags, expert totals
+  size_t bytes = (size_t)(chunks * num_experts + chunks + extra_flags + num_experts) *
+                 sizeof(int32_t);
   return ((bytes + 255) / 256) * 256 + 256;
 }
 
@@ -152,47 +169,57 @@ __device__ __forceinline__ int count_chunk(const int64_t* __restrict__ topk_idx,
 // cover whole rows of the chunk-major counts) into LDS; lane e then adds its
 // expert's parts, and one inclusive DPP sum per wave over those totals gives
 // each expert the totals of the wave's earlier experts.  The waves' sums and
-// flag bits meet in LDS across one barrier.  kSingleChunk: the totals are
-// already in sh.tot (visible to every thread) and no chunk comes before.
+// flag bits meet in LDS across one barrier.  kSrc == kTotalsInLds: the totals
+// are already in sh.tot (visible to every thread) and no chunk comes before;
+// kReadBases: chunk_count holds each chunk's base inside every expert (its
+// column prefix) and totals every expert's total.
 // Returns the workgroup's flag bits (EP_FLAG_BAD_EXPERT if any thread's
 // flag_bits is set, EP_FLAG_OVERFLOW if a padded expert overflows) and sets
 // total to the number of routed pairs.
-template <bool kSingleChunk>
+template <int kSrc>
 __device__ __forceinline__ int32_t expert_scan(int32_t E, int32_t capacity, int32_t num_chunks,
                                                int64_t c, const int32_t* __restrict__ chunk_count,
-                                               ScanShared& sh, int32_t flag_bits, int32_t& total) {
+                                               const int32_t* __restrict__ totals, ScanShared& sh,
+                                               int32_t flag_bits, int32_t& total) {
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   const bool serves = tid < E;  // lane e = tid of the scan
   int32_t tot = 0, pre = 0;
-  if constexpr (kSingleChunk) {
+  if constexpr (kSrc == kTotalsInLds) {
     if (serves) tot = sh.tot[tid];
+  } else if constexpr (kSrc == kReadBases) {
+    if (serves) {
+      tot = totals[tid];
+      pre = chunk_count[c * E + tid];
+    }
   } else {
     int parts = kLayoutThreads / E;
     if (parts > kScanParts) parts = kScanParts;
     const int part = tid / E;
     const int e = tid - part * E;
     if (part < parts) {
-      // the first kScanLoads of the part's chunks with every load in flight
-      // at once (a fixed trip count), then any further ones
-      int32_t v[kScanLoads];
-#pragma unroll
-      for (int i = 0; i < kScanLoads; ++i) {
-        const int cc = part + i * parts;
-        v[i] = cc < num_chunks ? chunk_count[(int64_t)cc * E + e] : 0;
-      }
+      // the part's chunks in batches of kScanLoads, every load of a batch in
+      // flight at once (a fixed trip count; a plain loop would wait for each).
+      // The first batch is straight-line code: most inputs need no other, and
+      // a loop around it measured slower for them.
       int32_t pt = 0, pp = 0;
+      auto batch = [&](int first) {
+        int32_t v[kScanLoads];
 #pragma unroll
-      for (int i = 0; i < kScanLoads; ++i) {
-        pt += v[i];
-        pp += part + i * parts < c ? v[i] : 0;
-      }
-      for (int cc = part + kScanLoads * parts; cc < num_chunks; cc += parts) {
-        const int32_t w = chunk_count[(int64_t)cc * E + e];
-        pt += w;
-        pp += cc < c ? w : 0;
-      }
+        for (int i = 0; i < kScanLoads; ++i) {
+          const int cc = first + i * parts;
+          v[i] = cc < num_chunks ? chunk_count[(int64_t)cc * E + e] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < kScanLoads; ++i) {
+          pt += v[i];
+          pp += first + i * parts < c ? v[i] : 0;
+        }
+      };
+      batch(part);
+      for (int first = part + kScanLoads * parts; first < num_chunks; first += kScanLoads * parts)
+        batch(first);
       sh.part_tot[part * E + e] = pt;
       sh.part_pre[part * E + e] = pp;
     }
@@ -235,8 +262,9 @@ __device__ __forceinline__ int32_t expert_scan(int32_t E, int32_t capacity, int3
   return flags;
 }
 
-// Phase 2 for chunk c, given every chunk's totals in memory.  kSingleChunk:
-// there is only this chunk, and sh.tot is already set by the caller.  For
+// Phase 2 for chunk c, given every chunk's totals in memory (or, for kSrc ==
+// kReadBases, every chunk's bases and the experts' totals; for kTotalsInLds
+// there is only this chunk, and sh.tot is already set by the caller).  For
 // c == 0, flag_bits is the OR of this thread's share of the flag entries (one
 // per chunk, then any written by a kernel that prepared the ids), which the
 // caller loads at its start so that their latency is hidden.
@@ -244,10 +272,11 @@ __device__ __forceinline__ int32_t expert_scan(int32_t E, int32_t capacity, int3
 // the scan is done, before the receive rows, so that no store waits on
 // another: the group totals are differences of the exclusive prefix, and the
 // flags travel through one word per wave across the scan's own barrier.
-template <bool kSingleChunk>
+template <int kSrc>
 __device__ __forceinline__ void finish_chunk(
     int64_t num_pairs, int32_t E, int32_t num_groups, int32_t capacity, int32_t num_chunks,
-    int64_t c, const int32_t* __restrict__ chunk_count, ScanShared& sh,
+    int64_t c, const int32_t* __restrict__ chunk_count, const int32_t* __restrict__ totals,
+    ScanShared& sh,
     const int32_t (&eid)[kLayoutItems], const int32_t (&local)[kLayoutItems],
     int32_t* __restrict__ slot_idx, int32_t* __restrict__ recv_src,
     int32_t* __restrict__ num_tokens_per_expert, int32_t* __restrict__ expert_offsets,
@@ -257,8 +286,8 @@ __device__ __forceinline__ void finish_chunk(
 
   // 1-2. expert totals, bases inside each expert, offsets, flags
   int32_t total;
-  const int32_t flags =
-      expert_scan<kSingleChunk>(E, capacity, num_chunks, c, chunk_count, sh, flag_bits, total);
+  const int32_t flags = expert_scan<kSrc>(E, capacity, num_chunks, c, chunk_count, totals, sh,
+                                          flag_bits, total);
 
   // 3. metadata, once
   if (c == 0) {
@@ -302,6 +331,7 @@ struct LayoutArgs {
   int32_t num_experts, expert_bits, num_groups, capacity, num_chunks, num_flags;
   int32_t* chunk_count;
   int32_t* chunk_flags;
+  int32_t* totals;  // every expert's total, when the bases launch runs
   int32_t* slot_idx;
   int32_t* recv_src;
   int32_t* num_tokens_per_expert;
@@ -377,6 +407,7 @@ __device__ __forceinline__ int32_t load_flag_bits(const int32_t* __restrict__ ch
 }
 
 // Phase 2 (also the whole layout when there are no pairs).
+template <int kSrc>
 __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(LayoutArgs a) {
   __shared__ ScanShared sh;
   const int32_t own = a.num_chunks > 0 ? a.num_chunks : 1;
@@ -394,10 +425,63 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_finish_kernel(LayoutArg
     eid[i] = v >= 0 ? (v & ((1 << kExpertBits) - 1)) : -1;
     local[i] = v >= 0 ? (v >> kExpertBits) : 0;
   }
-  finish_chunk<false>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, a.num_chunks,
-                      blockIdx.x, a.chunk_count, sh, eid, local, a.slot_idx, a.recv_src,
-                      a.num_tokens_per_expert, a.expert_offsets, a.num_tokens_per_group,
-                      a.error_flags, flag_bits);
+  finish_chunk<kSrc>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, a.num_chunks,
+                     blockIdx.x, a.chunk_count, a.totals, sh, eid, local, a.slot_idx,
+                     a.recv_src, a.num_tokens_per_expert, a.expert_offsets,
+                     a.num_tokens_per_group, a.error_flags, flag_bits);
+}
+
+// Between the two phases, for inputs with many chunks: each expert's total and
+// each chunk's base inside it (the exclusive prefix of the expert's counts
+// over the chunks), computed once instead of by every finish workgroup.  One
+// workgroup per kWave experts, one lane per expert; wave w takes a contiguous
+// block of chunks, sums it (each load instruction reads a run of a row of the
+// chunk-major counts), the block sums meet in LDS, and the wave then writes
+// its chunks' bases over their counts (no other wave reads those rows).
+__global__ __launch_bounds__(kLayoutThreads) void layout_bases_kernel(LayoutArgs a) {
+  __shared__ int32_t s_sum[kLayoutWaves][kWave];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int32_t E = a.num_experts;
+  const int32_t C = a.num_chunks;
+  const int e = (int)blockIdx.x * kWave + lane;
+  const bool serves = e < E;
+  const int32_t per = (C + kLayoutWaves - 1) / kLayoutWaves;
+  const int32_t lo = wave * per;
+  const int32_t hi = lo + per < C ? lo + per : C;
+  int32_t* col = a.chunk_count + e;
+  int32_t sum = 0;
+  if (serves) {
+    for (int32_t first = lo; first < hi; first += kScanLoads) {
+      int32_t v[kScanLoads];
+#pragma unroll
+      for (int i = 0; i < kScanLoads; ++i)
+        v[i] = first + i < hi ? col[(int64_t)(first + i) * E] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanLoads; ++i) sum += v[i];
+    }
+  }
+  s_sum[wave][lane] = sum;
+  __syncthreads();
+  int32_t run = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kLayoutWaves; ++w) {
+    run += w < wave ? s_sum[w][lane] : 0;
+    total += s_sum[w][lane];
+  }
+  if (!serves) return;
+  if (wave == 0) a.totals[e] = total;
+  for (int32_t first = lo; first < hi; first += kScanLoads) {
+    int32_t v[kScanLoads];
+#pragma unroll
+    for (int i = 0; i < kScanLoads; ++i)
+      v[i] = first + i < hi ? col[(int64_t)(first + i) * E] : 0;
+#pragma unroll
+    for (int i = 0; i < kScanLoads; ++i) {
+      if (first + i < hi) col[(int64_t)(first + i) * E] = run;
+      run += v[i];
+    }
+  }
 }
 
 // Inputs of at most one chunk (decode-sized batches): both phases in one
@@ -412,7 +496,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(LayoutArg
   const int bad = count_chunk(a.topk_idx, a.num_pairs, a.num_experts, a.expert_bits, 0, hist,
                               wave_flags, a.chunk_count, a.chunk_flags, sh.tot, eid, local);
   __syncthreads();  // the totals in sh.tot, for every thread
-  finish_chunk<true>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, 1, 0, a.chunk_count,
+  finish_chunk<kTotalsInLds>(a.num_pairs, a.num_experts, a.num_groups, a.capacity, 1, 0,
+                             a.chunk_count, a.totals,
                      sh, eid, local, a.slot_idx, a.recv_src, a.num_tokens_per_expert,
                      a.expert_offsets, a.num_tokens_per_group, a.error_flags, bad | extra_bits);
 }
@@ -449,6 +534,7 @@ hipError_t launch_layout_ids(const int64_t* topk_idx, const ep_layout_t& L, void
   a.num_flags = (int32_t)chunks + extra_flags;
   a.chunk_count = static_cast<int32_t*>(workspace);
   a.chunk_flags = a.chunk_count + chunks * L.num_experts;
+  a.totals = a.chunk_flags + a.num_flags;
   a.slot_idx = L.slot_idx;
   a.recv_src = L.recv_src;
   a.num_tokens_per_expert = L.num_tokens_per_expert;
@@ -475,7 +561,15 @@ hipError_t launch_layout_ids(const int64_t* topk_idx, const ep_layout_t& L, void
     hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)(chunks + a.warm_blocks)),
                        dim3(kLayoutThreads), 0, stream, a);
   const unsigned finish_blocks = (unsigned)((chunks > 0 ? chunks : 1) + a.warm_blocks);
-  hipLaunchKernelGGL(layout_finish_kernel, dim3(finish_blocks), dim3(kLayoutThreads), 0, stream, a);
+  if (chunks * chunks * L.num_experts > kBasesMinWork) {
+    hipLaunchKernelGGL(layout_bases_kernel, dim3((unsigned)((L.num_experts + kWave - 1) / kWave)),
+                       dim3(kLayoutThreads), 0, stream, a);
+    hipLaunchKernelGGL(layout_finish_kernel<kReadBases>, dim3(finish_blocks), dim3(kLayoutThreads),
+                       0, stream, a);
+  } else {
+    hipLaunchKernelGGL(layout_finish_kernel<kSumCounts>, dim3(finish_blocks), dim3(kLayoutThreads),
+                       0, stream, a);
+  }
   return hipGetLastError();
 }
 

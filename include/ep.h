@@ -138,7 +138,8 @@ int64_t ep_num_recv_rows(int64_t num_tokens, int32_t num_topk, int32_t num_exper
                          int32_t capacity);
 
 /* Bytes of device workspace ep_get_layout needs for these sizes: per-chunk
- * expert counts and flags, sized from the batch's tokens, top-k and experts as
+ * expert counts and flags and the experts' totals, sized from the batch's
+ * tokens, top-k and experts as
  * the pages size their buffers ([yololab] "ElasticBuffer": buffer capacity
  * follows max tokens, top-k, hidden and EP degree).  Host only. */
 size_t ep_layout_workspace_bytes(int64_t num_tokens, int32_t num_topk, int32_t num_experts);

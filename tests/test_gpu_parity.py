@@ -152,6 +152,12 @@ def _edge_layouts():
         # more chunks than workgroups resident at once: the two-launch path
         ("1.1M pairs, 547 chunks", g.integers(0, 64, (140000, 8)), 64, 8, 0),
         ("1.1M pairs padded", g.integers(-1, 64, (140000, 8)), 64, 8, 20000),
+        # one lane per expert in the finish scan, many batches of chunks each
+        ("E=1024, 300 chunks", g.integers(0, 1024, (76800, 8)), 1024, 8, 0),
+        # the extra launch that computes every chunk's bases once (chunks^2 * E
+        # large), with experts that leave its last workgroup partly idle
+        ("E=100, 300 chunks, bases launch", g.integers(-1, 100, (76800, 8)), 100, 10, 0),
+        ("E=100, 300 chunks padded, bases launch", g.integers(0, 100, (76800, 8)), 100, 10, 5000),
         # one layout chunk, top-k <= 8: one workgroup per token
         ("one chunk: masked and bad ids", g.integers(-3, 40, (200, 6)), 32, 4, 0),
         ("one chunk: padded overflow cap=3", g.integers(-1, 16, (300, 4)), 16, 4, 3),
