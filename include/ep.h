@@ -247,9 +247,9 @@ int ep_scales_to_mn_major(const void* scales, int64_t rows, int32_t hidden, int3
  * reads it.  The layout alone leaves HBM idle, and x read from HBM during
  * dispatch competes with its row writes.  Results are unchanged.  It pays
  * when x is not already cached (measured on MI355X at 8192 tokens x 7168:
- * the layout + dispatch kernels 130 -> 123 us and the step 309 -> 302 us
+ * the layout + dispatch kernels 130 -> 123 us and the step 310 -> 303 us
  * after the caches were emptied; 65,536 tokens x 4096, whose x never fits:
- * step 1044 -> 1037 us) and costs about 12 us when it is (step 280 -> 291
+ * step 1042 -> 1039 us) and costs about 12 us when it is (step 280 -> 292
  * us when the router has just read x).
  * ep_dispatch and ep_get_layout reject the flag (EP_ERR_DTYPE).
  */
